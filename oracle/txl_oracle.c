@@ -1,0 +1,355 @@
+/*
+ * txl_oracle.c -- CPU oracle for the Transformer-XL relative-attention path.
+ *
+ * TEST INFRASTRUCTURE ONLY. This file is the plain, slow, obviously correct
+ * reference that the HIP library is checked against. It shares no code, header,
+ * table or constant with the HIP path, and the product never links or calls it:
+ * only the tests, the smoke check and the CPU-baseline leg of the benchmark do.
+ *
+ * Everything is double precision, row-major, with explicit loops. There is no
+ * blocking, fusion or shift trick: every score is computed from its own query,
+ * key and distance. OpenMP only splits independent outer loops across threads;
+ * every sum keeps its sequential order.
+ *
+ * Sources (web pages on Transformer-XL):
+ *  [XL]   "Transformer-XL, explained." (vibeengines.com/paper/transformer-xl):
+ *         the seven numbered method steps and the legend of the score equation.
+ *  [SIM]  segment-recurrence simulator (mysimulator.uk): the memory equations
+ *         h~ = [SG(mem); h], K,V = h~ W, Q = h W, mem = last M rows of h~, and
+ *         Attention = softmax(Q K^T / sqrt(d)) V.
+ *  [GLO]  Ultralytics glossary "Transformer-XL" (German and Vietnamese): the
+ *         segment loop with an empty first memory and the key counts 4, 8.
+ *  [IMPL] "Implementing Transformer-XL" (mbrenndoerfer.com): the NumPy layer
+ *         with W_q, W_k_E, W_k_R, W_v, W_o, u, v, post-LN residual blocks, the
+ *         LayerNorm with population std + 1e-6, and the ReLU FFN.
+ *
+ * Conventions fixed here where the pages leave them open:
+ *  - weights are stored out-major, W[d_out][d_in], and y = x W^T;
+ *  - head h owns columns [h*dh, (h+1)*dh) of every D-wide tensor, dh = D/H;
+ *  - the distance of query i (segment row) to key j (row of [mem; h]) with m
+ *    memory rows is delta = m + i - j; key j is visible iff j <= m + i;
+ *  - score = ((q_i + u).k_j + (q_i + v).r_delta) / sqrt(dh), r = R W_kR^T;
+ *  - R[delta][k] = sin(delta * 10000^(-2k/D)), R[delta][D/2 + k] = cos(...);
+ *  - softmax has no epsilon in the denominator;
+ *  - the memory holds the layer's INPUT rows, oldest first.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG 1
+#define ORC_ERR_NOMEM 2
+
+/* Number of threads the OpenMP loops below use (1 without OpenMP). */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Relative-encoding table ([XL] step 4 and the legend entry for R_{i-j}:
+ * a sinusoidal encoding of the distance with no trained parameters). The
+ * pages do not print the formula; the [sin | cos] half-split with base 10000
+ * is the reading taken. D must be even. */
+int orc_sinusoid_table(int R_len, int D, double *R)
+{
+    if (R_len < 0 || D < 2 || (D % 2) != 0 || !R) return ORC_ERR_ARG;
+    int half = D / 2;
+    for (int d = 0; d < R_len; ++d) {
+        for (int k = 0; k < half; ++k) {
+            double freq = pow(10000.0, -2.0 * (double)k / (double)D);
+            R[(size_t)d * D + k] = sin((double)d * freq);
+            R[(size_t)d * D + half + k] = cos((double)d * freq);
+        }
+    }
+    return ORC_OK;
+}
+
+/* y[n][o] = sum_i x[n][i] * Wt[o][i]  ([SIM] K,V = h~ W, Q = h W; [IMPL] the
+ * projections hidden @ W). */
+int orc_linear(long N, int Din, int Dout, const double *x, const double *Wt, double *y)
+{
+    if (N < 0 || Din < 1 || Dout < 1 || !x || !Wt || !y) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (long n = 0; n < N; ++n) {
+        for (int o = 0; o < Dout; ++o) {
+            double acc = 0.0;
+            for (int i = 0; i < Din; ++i) acc += x[n * Din + i] * Wt[(size_t)o * Din + i];
+            y[n * Dout + o] = acc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* LayerNorm of [IMPL]: gamma * (x - mean) / (std + 1e-6) + beta, std the
+ * population standard deviation over the last axis. */
+int orc_layer_norm(long N, int D, const double *x, const double *g, const double *b, double *y)
+{
+    if (N < 0 || D < 1 || !x || !g || !b || !y) return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (long n = 0; n < N; ++n) {
+        const double *row = x + n * D;
+        double mean = 0.0;
+        for (int c = 0; c < D; ++c) mean += row[c];
+        mean /= D;
+        double var = 0.0;
+        for (int c = 0; c < D; ++c) var += (row[c] - mean) * (row[c] - mean);
+        var /= D;
+        double sd = sqrt(var) + 1e-6;
+        for (int c = 0; c < D; ++c) y[n * D + c] = g[c] * (row[c] - mean) / sd + b[c];
+    }
+    return ORC_OK;
+}
+
+/*
+ * Relative multi-head attention of one segment over [mem; h] followed by the
+ * output projection ([XL] steps 3-4 and the score legend; [SIM]; [IMPL]
+ * relative_attention).
+ *
+ *   h    [B][W][D]   current segment (queries and the last W keys)
+ *   mem  [B][m][D]   cached rows, oldest first (ignored when m == 0)
+ *   out  [B][W][D]   (P . V) W_o^T
+ *   P, AC, BD  optional [B][H][W][m+W]: probabilities (0 where masked), and the
+ *              unscaled content and distance terms (NaN where masked).
+ */
+int orc_rel_attn(int B, int W, int D, int H, int m,
+                 const double *h, const double *mem,
+                 const double *Wq, const double *WkE, const double *WkR,
+                 const double *Wv, const double *Wo,
+                 const double *u, const double *v,
+                 const double *R, int R_len,
+                 double *out, double *P, double *AC, double *BD)
+{
+    if (B < 1 || W < 1 || D < 1 || H < 1 || D % H != 0 || m < 0) return ORC_ERR_ARG;
+    if (!h || (m > 0 && !mem) || !Wq || !WkE || !WkR || !Wv || !Wo || !u || !v || !R || !out)
+        return ORC_ERR_ARG;
+    const int K = m + W;
+    if (R_len < K) return ORC_ERR_ARG;
+    const int dh = D / H;
+    const double inv_sqrt_dh = 1.0 / sqrt((double)dh);
+
+    /* [SIM] h~ = [SG(mem); h]: memory first, then the segment. */
+    double *ctx = malloc(sizeof(double) * (size_t)B * K * D);
+    double *Q = malloc(sizeof(double) * (size_t)B * W * D);
+    double *KE = malloc(sizeof(double) * (size_t)B * K * D);
+    double *V = malloc(sizeof(double) * (size_t)B * K * D);
+    double *RK = malloc(sizeof(double) * (size_t)K * D);
+    double *O = malloc(sizeof(double) * (size_t)B * W * D);
+    if (!ctx || !Q || !KE || !V || !RK || !O) {
+        free(ctx); free(Q); free(KE); free(V); free(RK); free(O);
+        return ORC_ERR_NOMEM;
+    }
+    for (int b = 0; b < B; ++b) {
+        for (int j = 0; j < m; ++j)
+            memcpy(ctx + ((size_t)b * K + j) * D, mem + ((size_t)b * m + j) * D, sizeof(double) * D);
+        for (int i = 0; i < W; ++i)
+            memcpy(ctx + ((size_t)b * K + m + i) * D, h + ((size_t)b * W + i) * D, sizeof(double) * D);
+    }
+
+    /* Queries from the segment only; content keys and values from [mem; h]
+     * ([XL] step 3); distance keys r = R W_kR^T for every distance 0..K-1
+     * ([XL] step 4: separate key projections for content and distance). */
+    orc_linear((long)B * W, D, D, h, Wq, Q);
+    orc_linear((long)B * K, D, D, ctx, WkE, KE);
+    orc_linear((long)B * K, D, D, ctx, Wv, V);
+    orc_linear((long)K, D, D, R, WkR, RK);
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int hd = 0; hd < H; ++hd) {
+            double *s = malloc(sizeof(double) * K);
+            const int c0 = hd * dh;
+            for (int i = 0; i < W; ++i) {
+                const double *q = Q + ((size_t)b * W + i) * D;
+                double smax = -INFINITY;
+                for (int j = 0; j < K; ++j) {
+                    size_t pidx = (((size_t)b * H + hd) * W + i) * K + j;
+                    if (j > m + i) {           /* causal mask over [mem; h] */
+                        s[j] = -INFINITY;
+                        if (AC) AC[pidx] = NAN;
+                        if (BD) BD[pidx] = NAN;
+                        continue;
+                    }
+                    const int delta = m + i - j;   /* query-key distance */
+                    const double *k = KE + ((size_t)b * K + j) * D;
+                    const double *r = RK + (size_t)delta * D;
+                    double ac = 0.0, bd = 0.0;
+                    for (int c = c0; c < c0 + dh; ++c) ac += (q[c] + u[c]) * k[c];
+                    for (int c = c0; c < c0 + dh; ++c) bd += (q[c] + v[c]) * r[c];
+                    if (AC) AC[pidx] = ac;
+                    if (BD) BD[pidx] = bd;
+                    s[j] = (ac + bd) * inv_sqrt_dh;
+                    if (s[j] > smax) smax = s[j];
+                }
+                double denom = 0.0;
+                for (int j = 0; j <= m + i && j < K; ++j) {
+                    s[j] = exp(s[j] - smax);
+                    denom += s[j];
+                }
+                for (int j = 0; j < K; ++j) {
+                    double p = (j <= m + i) ? s[j] / denom : 0.0;
+                    s[j] = p;
+                    if (P) P[(((size_t)b * H + hd) * W + i) * K + j] = p;
+                }
+                double *o = O + ((size_t)b * W + i) * D;
+                for (int c = c0; c < c0 + dh; ++c) {
+                    double acc = 0.0;
+                    for (int j = 0; j < K; ++j) acc += s[j] * V[((size_t)b * K + j) * D + c];
+                    o[c] = acc;
+                }
+            }
+            free(s);
+        }
+    }
+    /* Heads concatenated in order, then the output projection ([IMPL]). */
+    orc_linear((long)B * W, D, D, O, Wo, out);
+
+    free(ctx); free(Q); free(KE); free(V); free(RK); free(O);
+    return ORC_OK;
+}
+
+/* Post-LN block of [IMPL] forward: h1 = LN1(h + attn), y = LN2(h1 + FFN(h1)),
+ * FFN(x) = ReLU(x W1^T + b1) W2^T + b2. */
+int orc_layer_fwd(int B, int W, int D, int H, int F, int m,
+                  const double *h, const double *mem,
+                  const double *Wq, const double *WkE, const double *WkR,
+                  const double *Wv, const double *Wo,
+                  const double *u, const double *v,
+                  const double *ln1_g, const double *ln1_b,
+                  const double *W1, const double *b1, const double *W2, const double *b2,
+                  const double *ln2_g, const double *ln2_b,
+                  const double *R, int R_len, double *y)
+{
+    if (F < 1 || !ln1_g || !ln1_b || !W1 || !b1 || !W2 || !b2 || !ln2_g || !ln2_b || !y)
+        return ORC_ERR_ARG;
+    const long N = (long)B * W;
+    double *att = malloc(sizeof(double) * N * D);
+    double *h1 = malloc(sizeof(double) * N * D);
+    double *f1 = malloc(sizeof(double) * N * F);
+    double *f2 = malloc(sizeof(double) * N * D);
+    if (!att || !h1 || !f1 || !f2) { free(att); free(h1); free(f1); free(f2); return ORC_ERR_NOMEM; }
+    int st = orc_rel_attn(B, W, D, H, m, h, mem, Wq, WkE, WkR, Wv, Wo, u, v, R, R_len,
+                          att, NULL, NULL, NULL);
+    if (st != ORC_OK) { free(att); free(h1); free(f1); free(f2); return st; }
+    for (long n = 0; n < N * D; ++n) att[n] += h[n];
+    orc_layer_norm(N, D, att, ln1_g, ln1_b, h1);
+    orc_linear(N, D, F, h1, W1, f1);
+    for (long n = 0; n < N; ++n)
+        for (int c = 0; c < F; ++c) {
+            double z = f1[n * F + c] + b1[c];
+            f1[n * F + c] = z > 0.0 ? z : 0.0;
+        }
+    orc_linear(N, F, D, f1, W2, f2);
+    for (long n = 0; n < N; ++n)
+        for (int c = 0; c < D; ++c) f2[n * D + c] += b2[c] + h1[n * D + c];
+    orc_layer_norm(N, D, f2, ln2_g, ln2_b, y);
+    free(att); free(h1); free(f1); free(f2);
+    return ORC_OK;
+}
+
+/* Memory update of [SIM]: mem <- last M rows of h~ = [mem; h] (logical order,
+ * oldest first). new_mem must hold [B][M][D]; returns the new row count. */
+int orc_mem_update(int B, int M, int D, int m, const double *mem, int W, const double *h,
+                   double *new_mem, int *new_m)
+{
+    if (B < 1 || M < 1 || D < 1 || m < 0 || m > M || W < 1 || !h || !new_mem || !new_m)
+        return ORC_ERR_ARG;
+    const int K = m + W;
+    const int keep = K < M ? K : M;
+    for (int b = 0; b < B; ++b) {
+        for (int t = 0; t < keep; ++t) {
+            int src = K - keep + t;   /* row of [mem; h] */
+            const double *row = src < m ? mem + ((size_t)b * m + src) * D
+                                        : h + ((size_t)b * W + (src - m)) * D;
+            memcpy(new_mem + ((size_t)b * M + t) * D, row, sizeof(double) * D);
+        }
+    }
+    *new_m = keep;
+    return ORC_OK;
+}
+
+/*
+ * Segment-by-segment driver over a stream x [B][S*W][D] ([XL] steps 1-3 and 6:
+ * segments in order, every layer caches its input rows, layer n reads the
+ * cache of layer n-1's states). Layer parameters are stacked along a leading
+ * axis of size L. full_layer = 0 runs the attention + output projection only
+ * (single-layer attention workloads); full_layer = 1 runs the post-LN block.
+ * The memory of every layer starts empty. y [B][S*W][D] receives the last
+ * layer's output per segment; mems_out (optional, [L][B][M][D]) and
+ * mem_len_out (optional, [L]) receive the final memories.
+ */
+int orc_stack_fwd(int B, int W, int D, int H, int F, int L, int S, int M, int full_layer,
+                  const double *x,
+                  const double *Wq, const double *WkE, const double *WkR,
+                  const double *Wv, const double *Wo,
+                  const double *u, const double *v,
+                  const double *ln1_g, const double *ln1_b,
+                  const double *W1, const double *b1, const double *W2, const double *b2,
+                  const double *ln2_g, const double *ln2_b,
+                  const double *R, int R_len, double *y, double *mems_out, int *mem_len_out)
+{
+    if (B < 1 || W < 1 || D < 1 || H < 1 || L < 1 || S < 1 || M < 1 || !x || !y) return ORC_ERR_ARG;
+    if (full_layer && F < 1) return ORC_ERR_ARG;
+    const size_t DD = (size_t)D * D;
+    const size_t seg = (size_t)W * D;
+    double *mems = calloc((size_t)L * B * M * D, sizeof(double));
+    double *tmp_mem = calloc((size_t)B * M * D, sizeof(double));
+    int *mlen = calloc((size_t)L, sizeof(int));
+    double *hin = malloc(sizeof(double) * (size_t)B * seg);
+    double *hout = malloc(sizeof(double) * (size_t)B * seg);
+    if (!mems || !tmp_mem || !mlen || !hin || !hout) {
+        free(mems); free(tmp_mem); free(mlen); free(hin); free(hout);
+        return ORC_ERR_NOMEM;
+    }
+    int st = ORC_OK;
+    for (int t = 0; t < S && st == ORC_OK; ++t) {
+        for (int b = 0; b < B; ++b)
+            memcpy(hin + (size_t)b * seg, x + ((size_t)b * S + t) * seg, sizeof(double) * seg);
+        for (int l = 0; l < L && st == ORC_OK; ++l) {
+            const int m = mlen[l];
+            /* the memory buffer holds [B][M][D]; pass its first m rows per batch
+             * as a compact [B][m][D] block */
+            double *mcompact = malloc(sizeof(double) * (size_t)B * (m > 0 ? m : 1) * D);
+            for (int b = 0; b < B; ++b)
+                memcpy(mcompact + (size_t)b * m * D, mems + (((size_t)l * B + b) * M) * D,
+                       sizeof(double) * (size_t)m * D);
+            if (full_layer)
+                st = orc_layer_fwd(B, W, D, H, F, m, hin, mcompact,
+                                   Wq + l * DD, WkE + l * DD, WkR + l * DD, Wv + l * DD, Wo + l * DD,
+                                   u + (size_t)l * D, v + (size_t)l * D,
+                                   ln1_g + (size_t)l * D, ln1_b + (size_t)l * D,
+                                   W1 + (size_t)l * F * D, b1 + (size_t)l * F,
+                                   W2 + (size_t)l * D * F, b2 + (size_t)l * D,
+                                   ln2_g + (size_t)l * D, ln2_b + (size_t)l * D,
+                                   R, R_len, hout);
+            else
+                st = orc_rel_attn(B, W, D, H, m, hin, mcompact,
+                                  Wq + l * DD, WkE + l * DD, WkR + l * DD, Wv + l * DD, Wo + l * DD,
+                                  u + (size_t)l * D, v + (size_t)l * D, R, R_len,
+                                  hout, NULL, NULL, NULL);
+            if (st == ORC_OK) {
+                int nm = 0;
+                /* the layer's input rows go to its memory */
+                st = orc_mem_update(B, M, D, m, mcompact, W, hin, tmp_mem, &nm);
+                memcpy(mems + (size_t)l * B * M * D, tmp_mem, sizeof(double) * (size_t)B * M * D);
+                mlen[l] = nm;
+            }
+            free(mcompact);
+            double *sw = hin; hin = hout; hout = sw;   /* next layer's input */
+        }
+        for (int b = 0; b < B; ++b)
+            memcpy(y + ((size_t)b * S + t) * seg, hin + (size_t)b * seg, sizeof(double) * seg);
+    }
+    if (mems_out) memcpy(mems_out, mems, sizeof(double) * (size_t)L * B * M * D);
+    if (mem_len_out) memcpy(mem_len_out, mlen, sizeof(int) * (size_t)L);
+    free(mems); free(tmp_mem); free(mlen); free(hin); free(hout);
+    return st;
+}

@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here checks the oracle against something other than itself: values
+the pages state (fixtures under tests/golden/), closed forms, invariants,
+special cases that reduce to a library routine (torch's scaled-dot-product
+attention, numpy/torch linear algebra), and brute force over the whole stream
+on tiny inputs. None of them needs a GPU.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from transformer_xl_segment_amd import synthetic as syn
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _params(rng, D, F=None, scale=0.3, affine=False):
+    # larger than the workloads' 0.02 so that every term moves the scores visibly
+    return syn.draw_layer_params(rng, D, F, "fp32", affine=affine, scale=scale)
+
+
+def _R(K, D):
+    return orc.sinusoid_table(K, D)
+
+
+# --------------------------------------------------------------------------
+# Relative-encoding table: closed forms of the [sin | cos] reading.
+# --------------------------------------------------------------------------
+
+def test_sinusoid_closed_forms():
+    D, L = 10, 40
+    R = _R(L, D)
+    half = D // 2
+    # distance 0: sin 0 = 0 in the first half, cos 0 = 1 in the second
+    assert np.all(R[0, :half] == 0.0) and np.all(R[0, half:] == 1.0)
+    # the first frequency is 1: column 0 is sin(d), column D/2 is cos(d)
+    d = np.arange(L)
+    np.testing.assert_allclose(R[:, 0], np.sin(d), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(R[:, half], np.cos(d), rtol=0, atol=1e-15)
+    # every (k, D/2 + k) pair lies on the unit circle
+    np.testing.assert_allclose(R[:, :half] ** 2 + R[:, half:] ** 2, 1.0, atol=1e-14)
+    # the last frequency is 10000^(-(D-2)/D)
+    w = 10000.0 ** (-(D - 2) / D)
+    np.testing.assert_allclose(R[:, half - 1], np.sin(d * w), atol=1e-15)
+    # no trained parameters: any longer table extends a shorter one unchanged
+    np.testing.assert_array_equal(_R(L + 17, D)[:L], R)
+
+
+# --------------------------------------------------------------------------
+# Linear maps and LayerNorm.
+# --------------------------------------------------------------------------
+
+def test_linear_matches_library_matmul():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((7, 5, 13))
+    Wt = rng.standard_normal((11, 13))
+    np.testing.assert_allclose(orc.linear(x, Wt), x @ Wt.T, rtol=1e-13, atol=1e-13)
+
+
+def test_layer_norm_invariants():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((9, 24)) * 3.0 + 1.5
+    g = 1.0 + rng.standard_normal(24) * 0.1
+    b = rng.standard_normal(24) * 0.1
+    y = orc.layer_norm(x, g, b)
+    z = (y - b) / g
+    sd = x.std(axis=-1)
+    # normalised rows have mean 0 and population std sigma / (sigma + 1e-6)
+    np.testing.assert_allclose(z.mean(axis=-1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(z.std(axis=-1), sd / (sd + 1e-6), rtol=1e-12)
+    # a constant row has sigma = 0 and maps to the offset exactly
+    yc = orc.layer_norm(np.full((1, 24), 7.25), g, b)
+    np.testing.assert_array_equal(yc[0], b)
+    # close to torch's LayerNorm (its eps sits under the square root instead)
+    yt = torch.nn.functional.layer_norm(torch.from_numpy(x), (24,), torch.from_numpy(g),
+                                        torch.from_numpy(b), eps=0.0).numpy()
+    np.testing.assert_allclose(y, yt, rtol=1e-5, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# Relative attention: special cases, invariants, brute force.
+# --------------------------------------------------------------------------
+
+def _attn_case(seed=3, B=2, W=5, m=3, D=12, H=3, scale=0.3):
+    rng = np.random.default_rng(seed)
+    p = _params(rng, D, scale=scale)
+    h = rng.standard_normal((B, W, D))
+    mem = rng.standard_normal((B, m, D)) if m > 0 else None
+    return p, h, mem, _R(m + W, D)
+
+
+def test_probability_rows_and_mask():
+    p, h, mem, R = _attn_case()
+    W, m = h.shape[1], mem.shape[1]
+    out, P, AC, BD = orc.rel_attn(h, mem, p, R, H=3, return_terms=True)
+    np.testing.assert_allclose(P.sum(-1), 1.0, atol=1e-12)
+    for i in range(W):
+        assert np.all(P[:, :, i, m + i + 1:] == 0.0)
+        assert np.all(P[:, :, i, :m + i + 1] > 0.0)
+        assert np.all(np.isnan(AC[:, :, i, m + i + 1:])) and np.all(np.isnan(BD[:, :, i, m + i + 1:]))
+
+
+def test_key_counts_match_glossary_loop():
+    # tests/golden/key_counts_glossary.txt: 3 segments of 4 tokens, dim 16, 2 heads,
+    # empty first memory, the previous segment cached -> 4, 8, 8 keys.
+    with open(os.path.join(GOLDEN, "key_counts_glossary.txt")) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    meta = dict(kv.split("=") for kv in lines[0].split())
+    expect = [int(t) for t in lines[1].split("=")[1].split()]
+    W, D, H, S = int(meta["seg_len"]), int(meta["dim"]), int(meta["heads"]), int(meta["segments"])
+    rng = np.random.default_rng(7)
+    p = _params(rng, D)
+    x = rng.standard_normal((1, S * W, D))
+    mem = None
+    counts = []
+    for t in range(S):
+        h = x[:, t * W:(t + 1) * W]
+        m = 0 if mem is None else mem.shape[1]
+        _, P, _, _ = orc.rel_attn(h, mem, p, _R(m + W, D), H, return_terms=True)
+        counts.append(P.shape[-1])
+        # the last query of the segment sees every key
+        assert int((P[0, 0, W - 1] > 0).sum()) == P.shape[-1]
+        mem = orc.mem_update(mem, h, M=W)
+    assert counts == expect
+
+
+def test_plain_attention_special_case_matches_sdpa():
+    # u = v = 0 and W_kR = 0 remove both distance terms and both biases: the
+    # result is causal softmax(Q K^T / sqrt(dh)) V over [mem; h], then W_o.
+    B, W, m, D, H = 2, 6, 4, 16, 4
+    p, h, mem, R = _attn_case(seed=11, B=B, W=W, m=m, D=D, H=H)
+    p = dict(p)
+    p["u"] = np.zeros(D)
+    p["v"] = np.zeros(D)
+    p["WkR"] = np.zeros((D, D))
+    out = orc.rel_attn(h, mem, p, R, H)
+    ctx = np.concatenate([mem, h], axis=1)
+    dh = D // H
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    q = t(h @ p["Wq"].T).reshape(B, W, H, dh).transpose(1, 2)
+    k = t(ctx @ p["WkE"].T).reshape(B, m + W, H, dh).transpose(1, 2)
+    v = t(ctx @ p["Wv"].T).reshape(B, m + W, H, dh).transpose(1, 2)
+    mask = torch.ones(W, m + W, dtype=torch.bool).tril(diagonal=m)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    ref = o.transpose(1, 2).reshape(B, W, D).numpy() @ p["Wo"].T
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_first_query_sees_only_itself_without_memory():
+    p, h, _, R = _attn_case(seed=5, m=0)
+    out = orc.rel_attn(h, None, p, R[:h.shape[1]], H=3)
+    ref = (h[:, 0] @ p["Wv"].T) @ p["Wo"].T
+    np.testing.assert_allclose(out[:, 0], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_uniform_scores_give_running_mean():
+    # W_q = 0, u = v = 0: every visible score is 0, so query i averages the values
+    # of keys 0..m+i.
+    p, h, mem, R = _attn_case(seed=6)
+    p = dict(p)
+    D = h.shape[2]
+    p["Wq"] = np.zeros((D, D))
+    p["u"] = np.zeros(D)
+    p["v"] = np.zeros(D)
+    out = orc.rel_attn(h, mem, p, R, H=3)
+    ctx = np.concatenate([mem, h], axis=1)
+    V = ctx @ p["Wv"].T
+    m = mem.shape[1]
+    csum = np.cumsum(V, axis=1)
+    ref = np.stack([csum[:, m + i] / (m + i + 1) for i in range(h.shape[1])], axis=1) @ p["Wo"].T
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_distance_only_scores_ignore_content():
+    # W_q = 0 and u = 0: the score is v . r_delta, a function of the distance
+    # only, so the probabilities are the same for every batch row and content.
+    p, h, mem, R = _attn_case(seed=8, B=3)
+    p = dict(p)
+    D = h.shape[2]
+    p["Wq"] = np.zeros((D, D))
+    p["u"] = np.zeros(D)
+    _, P1, _, BD1 = orc.rel_attn(h, mem, p, R, H=3, return_terms=True)
+    rng = np.random.default_rng(99)
+    _, P2, _, _ = orc.rel_attn(rng.standard_normal(h.shape), rng.standard_normal(mem.shape), p, R,
+                               H=3, return_terms=True)
+    np.testing.assert_array_equal(P1, P2)
+    np.testing.assert_array_equal(P1[0], P1[1])
+    # and BD is Toeplitz: it depends on i - j only
+    W, K = P1.shape[2], P1.shape[3]
+    for i in range(W - 1):
+        for j in range(K - 1):
+            if not np.isnan(BD1[0, 0, i, j]):
+                assert BD1[0, 0, i, j] == BD1[0, 0, i + 1, j + 1]
+
+
+def test_equal_rows_make_scores_toeplitz():
+    # with every input row equal, q and k are the same for all positions, AC is a
+    # constant and BD depends on the distance only
+    B, W, m, D, H = 1, 5, 4, 12, 3
+    rng = np.random.default_rng(12)
+    p = _params(rng, D)
+    row = rng.standard_normal(D)
+    h = np.tile(row, (B, W, 1))
+    mem = np.tile(row, (B, m, 1))
+    _, _, AC, BD = orc.rel_attn(h, mem, p, _R(m + W, D), H, return_terms=True)
+    vis = ~np.isnan(AC)
+    for hd in range(H):
+        a = AC[0, hd][vis[0, hd]]
+        assert np.all(a == a[0])
+    for i in range(W - 1):
+        for j in range(m + W - 1):
+            if vis[0, 0, i, j]:
+                np.testing.assert_array_equal(BD[0, :, i, j], BD[0, :, i + 1, j + 1])
+
+
+def test_pair_score_is_translation_invariant():
+    # tests/golden/relative_distance_explainer.txt: the pair (5, 3) and the pair
+    # (105, 103) have the same distance 2; with the same two tokens at those
+    # positions the oracle gives the same score terms, bit for bit.
+    with open(os.path.join(GOLDEN, "relative_distance_explainer.txt")) as f:
+        pairs = [tuple(int(t) for t in ln.split()) for ln in f if ln.strip() and not ln.startswith("#")]
+    (q0, k0, d0), (q1, k1, d1) = pairs
+    assert q0 - k0 == d0 and q1 - k1 == d1 and d0 == d1
+    D, H, W = 8, 2, 8
+    rng = np.random.default_rng(4)
+    p = _params(rng, D)
+    tok_q, tok_k = rng.standard_normal(D), rng.standard_normal(D)
+
+    def terms(qpos, kpos):
+        # the stream holds other random tokens, the two tokens at qpos and kpos;
+        # the query's segment starts at a multiple of W and its memory holds the
+        # previous W positions
+        T = (qpos // W + 1) * W
+        x = np.random.default_rng(qpos).standard_normal((1, T, D))
+        x[0, qpos], x[0, kpos] = tok_q, tok_k
+        s0 = (qpos // W) * W
+        mem = x[:, max(0, s0 - W):s0]
+        m = mem.shape[1]
+        h = x[:, s0:s0 + W]
+        _, _, AC, BD = orc.rel_attn(h, mem if m else None, p, _R(m + W, D), H, return_terms=True)
+        i, j = qpos - s0, kpos - (s0 - m)
+        assert m + i - j == qpos - kpos
+        return AC[0, :, i, j], BD[0, :, i, j]
+
+    a0, b0 = terms(q0, k0)
+    a1, b1 = terms(q1, k1)
+    np.testing.assert_array_equal(a0, a1)
+    np.testing.assert_array_equal(b0, b1)
+
+
+def test_shift_trick_equals_per_pair_loop():
+    # The explainer's step 5: score the distance term once against every
+    # distance and shift each row into place. Written here in the classic
+    # pad-and-reshape form, independently of the oracle's per-pair loop.
+    B, W, m, D, H = 2, 7, 5, 12, 3
+    p, h, mem, R = _attn_case(seed=9, B=B, W=W, m=m, D=D, H=H)
+    _, _, _, BD = orc.rel_attn(h, mem, p, R, H, return_terms=True)
+    K, dh = m + W, D // H
+    qv = (h @ p["Wq"].T + p["v"]).reshape(B, W, H, dh)
+    rk = (R[:K] @ p["WkR"].T).reshape(K, H, dh)
+    # columns ordered by decreasing distance: column c holds distance K-1-c
+    rk_rev = rk[::-1]
+    full = np.einsum("bihc,khc->bhik", qv, rk_rev)          # [B, H, W, K]
+    padded = np.concatenate([np.zeros((B, H, W, 1)), full], axis=-1)
+    shifted = padded.reshape(B, H, K + 1, W)[:, :, 1:].reshape(B, H, W, K)
+    vis = ~np.isnan(BD)
+    np.testing.assert_allclose(shifted[vis], BD[vis], rtol=1e-12, atol=1e-13)
+
+
+def _stream_brute_force(x, p, R, H, W, M):
+    """Single-layer attention over the whole stream with the segment window.
+
+    Query t (segment tau = t // W) sees key s iff s <= t and s >= tau*W - m(tau),
+    with m(tau) = min(M, tau*W); the distance is t - s in stream positions.
+    Pure Python loops over (t, s); numpy only for the projections.
+    """
+    B, T, D = x.shape
+    dh = D // H
+    Q = x @ p["Wq"].T
+    Kc = x @ p["WkE"].T
+    V = x @ p["Wv"].T
+    Rk = R @ p["WkR"].T
+    out = np.zeros((B, T, D))
+    for b in range(B):
+        for hd in range(H):
+            cs = slice(hd * dh, (hd + 1) * dh)
+            for t in range(T):
+                tau = t // W
+                lo = tau * W - min(M, tau * W)
+                keys = list(range(lo, t + 1))
+                sc = []
+                for s in keys:
+                    ac = float(np.dot(Q[b, t, cs] + p["u"][cs], Kc[b, s, cs]))
+                    bd = float(np.dot(Q[b, t, cs] + p["v"][cs], Rk[t - s, cs]))
+                    sc.append((ac + bd) / math.sqrt(dh))
+                mx = max(sc)
+                e = [math.exp(z - mx) for z in sc]
+                tot = sum(e)
+                for s, w in zip(keys, e):
+                    out[b, t, cs] += (w / tot) * V[b, s, cs]
+    return out @ p["Wo"].T
+
+
+@pytest.mark.parametrize("W,M", [(3, 5), (4, 4), (4, 2)])
+def test_segments_equal_stream_brute_force(W, M):
+    B, S, D, H = 2, 4, 8, 2
+    rng = np.random.default_rng(20 + W + M)
+    p = _params(rng, D)
+    x = rng.standard_normal((B, S * W, D))
+    R = _R(S * W, D)
+    y, _ = orc.stack_fwd(x, [p], R, H, W, M, full_layer=False)
+    ref = _stream_brute_force(x, p, R, H, W, M)
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_layer_block_composition():
+    # post-LN block: LN1(h + attn), then LN2(h1 + FFN(h1)); FFN from torch's
+    # linear and relu, the pinned attention and LayerNorm from the oracle.
+    B, W, m, D, H, F = 2, 5, 3, 12, 3, 20
+    rng = np.random.default_rng(13)
+    p = _params(rng, D, F=F, affine=True)
+    h = rng.standard_normal((B, W, D))
+    mem = rng.standard_normal((B, m, D))
+    R = _R(m + W, D)
+    y = orc.layer_fwd(h, mem, p, R, H)
+    att = orc.rel_attn(h, mem, p, R, H)
+    h1 = orc.layer_norm(h + att, p["ln1_g"], p["ln1_b"])
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    f = torch.nn.functional.linear(torch.relu(torch.nn.functional.linear(t(h1), t(p["W1"]), t(p["b1"]))),
+                                   t(p["W2"]), t(p["b2"])).numpy()
+    ref = orc.layer_norm(h1 + f, p["ln2_g"], p["ln2_b"])
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_memory_update_keeps_last_rows():
+    # rows carry their stream position; after every segment the memory must be
+    # the min(M, tau*W) most recent positions, oldest first
+    B, D = 2, 3
+    for W, M in [(4, 4), (3, 7), (5, 2), (6, 6)]:
+        mem = None
+        for tau in range(5):
+            pos = np.arange(tau * W, (tau + 1) * W, dtype=np.float64)
+            h = np.broadcast_to(pos[None, :, None], (B, W, D)).copy()
+            mem = orc.mem_update(mem, h, M)
+            n = min(M, (tau + 1) * W)
+            assert mem.shape == (B, n, D)
+            expect = np.arange((tau + 1) * W - n, (tau + 1) * W, dtype=np.float64)
+            np.testing.assert_array_equal(mem[0, :, 0], expect)
+
+
+def test_stack_with_full_memory_equals_one_pass_stack():
+    # With M >= stream length nothing is ever dropped: the segment-recurrent stack
+    # equals one causal pass of the same stack over the whole stream as one segment.
+    B, W, S, D, H, F, L = 1, 3, 4, 8, 2, 16, 2
+    rng = np.random.default_rng(31)
+    params = [_params(rng, D, F=F, affine=True) for _ in range(L)]
+    x = rng.standard_normal((B, S * W, D))
+    R = _R(S * W, D)
+    y, mems = orc.stack_fwd(x, params, R, H, W, M=S * W, full_layer=True)
+    y1, _ = orc.stack_fwd(x, params, R, H, W=S * W, M=S * W, full_layer=True)
+    np.testing.assert_allclose(y, y1, rtol=1e-11, atol=1e-12)
+    # layer 0's memory holds the stack input, layer 1's holds layer 0's output
+    np.testing.assert_array_equal(mems[0], x)
+
+
+def test_reach_grows_one_segment_per_layer():
+    # M = W, two layers: the output at segment tau depends on input segments
+    # tau-2..tau only. Perturbing segment 0 changes segments 0..2 and leaves
+    # segments 3 and 4 bit-identical.
+    B, W, S, D, H, F, L = 1, 3, 5, 8, 2, 16, 2
+    rng = np.random.default_rng(32)
+    params = [_params(rng, D, F=F) for _ in range(L)]
+    x = rng.standard_normal((B, S * W, D))
+    R = _R(2 * W, D)
+    y, _ = orc.stack_fwd(x, params, R, H, W, M=W, full_layer=True)
+    x2 = x.copy()
+    x2[:, :W] += 1.0
+    y2, _ = orc.stack_fwd(x2, params, R, H, W, M=W, full_layer=True)
+    for tau in range(S):
+        seg = slice(tau * W, (tau + 1) * W)
+        if tau <= L:
+            assert np.max(np.abs(y[:, seg] - y2[:, seg])) > 1e-6
+        else:
+            np.testing.assert_array_equal(y[:, seg], y2[:, seg])
+
+
+def test_bad_arguments_are_rejected():
+    p, h, mem, R = _attn_case()
+    with pytest.raises(ValueError):
+        orc.rel_attn(h, mem, p, R[:3], H=3)       # table shorter than m + W
+    with pytest.raises(ValueError):
+        orc.rel_attn(h, mem, p, R, H=5)           # D % H != 0
