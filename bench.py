@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Benchmark of the Transformer-XL relative-attention path on one MI355X.
+
+One step = one steady segment of the hot path on the attn_w512_bf16 workload
+(batch 16, d_model 512, 8 heads of 64, segment W = 512, memory M = 512 full):
+the fused Q/K/V/R projections, the relative-attention kernel, the output
+projection and the memory-ring update, all through the C ABI
+(txl_rel_attn_fwd + txl_mem_update). Inputs are seeded synthetic tensors
+already resident in HBM when the timed region starts.
+
+Prints ONE JSON line with the whole-job throughput (tokens/s), the attention
+kernel's roofline position (its own launches timed with HIP events inside the
+timed region) and the CPU oracle timed on a bounded sample of the same work.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+WORKLOAD = "attn_w512_bf16"
+BF16_PEAK_TFLOPS = 2516.6        # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+HBM_PEAK_GBS = 8000.0
+
+
+def attn_flops(B, H, dh, W, m):
+    """Algorithmic flops of one attention launch: every causally visible
+    (query, key) pair costs 2*dh for the content term, 2*dh for the distance
+    term and 2*dh for P.V."""
+    pairs = W * m + W * (W + 1) // 2
+    return 6.0 * dh * H * B * pairs
+
+
+def proj_flops(B, W, m, D):
+    return 4.0 * B * W * D * D + 4.0 * B * (m + W) * D * D + 2.0 * (m + W) * D * D + 2.0 * B * W * D * D
+
+
+def attn_bytes(B, W, m, D, es):
+    """Compulsory HBM bytes of one attention launch: (q+u), (q+v), keys, values,
+    distance keys in, attention output out."""
+    K = m + W
+    return es * (2 * B * W * D + 2 * B * K * D + K * D + B * W * D)
+
+
+def traffic_for(kernel_src: str, path: str):
+    """Measured HBM bytes per launch from a committed counter summary, or None
+    if the kernel source has changed since the counters were taken."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(kernel_src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(prob, R64, H):
+    """The oracle on one full steady segment (m = 512, all batch rows)."""
+    from oracle import oracle as orc
+    wl = prob.wl
+    W = wl.W
+    h = prob.x[:, W:2 * W].astype(np.float64)
+    mem = prob.x[:, :W].astype(np.float64)
+    t0 = time.perf_counter()
+    orc.rel_attn(h, mem, prob.params[0], R64, H)
+    dt = time.perf_counter() - t0
+    tokens = h.shape[0] * W
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
+            "sample": f"one steady segment of {WORKLOAD} (all {h.shape[0]} batch rows, m={W}), "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every run here uses a "
+              f"single MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from transformer_xl_segment_amd import binding as tb
+    from transformer_xl_segment_amd import synthetic as syn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    wl = syn.WORKLOADS[WORKLOAD]
+    B, D, H, W, M = wl.B, wl.D, wl.H, wl.W, wl.M
+    dh = D // H
+    prob = syn.draw_problem(wl)
+    bf = torch.bfloat16
+    x = torch.from_numpy(prob.x).to(dev).to(bf)                 # [B, S*W, D]
+    params = tb.LayerParams.from_numpy(prob.params[0], bf, dev)
+    R = tb.sinusoid_table(M + W, D, bf, dev)                    # built by the library
+    ring = tb.MemoryRing.empty(B, M, D, bf, dev)
+    out = torch.empty(B, W, D, dtype=bf, device=dev)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN, bf, B, W, M, D, H), dtype=torch.uint8, device=dev)
+    segs = [x[:, t * W:(t + 1) * W] for t in range(wl.S)]
+
+    def step(k):
+        h = segs[k % len(segs)]
+        tb.rel_attn_fwd(h, ring, params, R, H, out=out, workspace=ws)
+        tb.mem_update(ring, h)
+
+    # fill the memory, then warm up at the steady state m = M
+    for k in range(max(args.warmup, 1) + (M + W - 1) // W):
+        step(k)
+    torch.cuda.synchronize()
+    assert ring.len == M
+    m = ring.len
+
+    tb.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms, launches = tb.profile_end()
+    assert launches == args.steps
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens = B * W * args.steps
+    a_flops = attn_flops(B, H, dh, W, m)
+    a_avg_s = attn_ms * 1e-3 / launches
+    a_tflops = a_flops / a_avg_s / 1e12
+    traffic = traffic_for(os.path.join(ROOT, "transformer_xl_segment_amd", "csrc", "txl_attn.hip"),
+                          os.path.join(ROOT, "profiles", "traffic_rel_attn_kernel_attn_w512_bf16.json"))
+    rec = {
+        "metric": "rel-attn tokens/s and TFLOP/s (% bf16 MFMA peak) at W=M=512, d_head=64, 1 GPU",
+        "value": tokens / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "B": B, "W": W, "M": M, "m": m, "D": D, "H": H, "d_head": dh,
+                   "step": "txl_rel_attn_fwd + txl_mem_update, one steady segment"},
+        "roofline": {"kernel": "rel_attn_kernel", "bound": "mfma", "achieved": a_tflops,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": a_tflops / BF16_PEAK_TFLOPS,
+                     "traffic": traffic, "avg_launch_us": a_avg_s * 1e6,
+                     "algorithmic_flops_per_launch": a_flops,
+                     "compulsory_bytes_per_launch": attn_bytes(B, W, m, D, 2)},
+        "attn_tokens_per_s": B * W / a_avg_s,
+        "step_tflops": (a_flops + proj_flops(B, W, m, D)) / (ms_per_step * 1e-3) / 1e12,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as orc
+        R64 = orc.sinusoid_table(M + W, D)
+        rb = syn.round_to_bf16(R64.astype(np.float32)).astype(np.float64)
+        rec["cpu_baseline"] = cpu_baseline(prob, rb, H)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * txl.h -- C ABI of libtxl: Transformer-XL relative-position attention over a
+ * cached segment memory, on MI355X (gfx950).
+ *
+ * Method (web pages on Transformer-XL):
+ *  - "Transformer-XL, explained." (vibeengines.com), the numbered method steps:
+ *    keys and values span the cached states of the previous segment followed by
+ *    the current segment, queries come from the current segment only, under a
+ *    causal mask (step 3); the score of query i and key j adds a content term and
+ *    a term in a sinusoidal encoding of the distance i - j, with separate key
+ *    projections for content and distance and two learned global biases u and v
+ *    (step 4, and the legend of the score equation); the distance term is
+ *    computed once against all distances and shifted into place (step 5); the
+ *    memory may be longer at evaluation than in training (step 7).
+ *  - the segment-recurrence simulator (mysimulator.uk): h~ = [SG(mem); h],
+ *    K,V = h~ W, Q = h W, mem = last M rows of h~, softmax(Q K^T / sqrt(d)) V.
+ *  - "Implementing Transformer-XL" (mbrenndoerfer.com), the NumPy layer: the
+ *    output projection W_o, post-LN residual blocks with LayerNorm
+ *    gamma * (x - mean) / (std + 1e-6) + beta (population std) and a ReLU FFN.
+ *
+ * What one call computes, per batch row b and head hd (columns
+ * [hd*dh, (hd+1)*dh) of every D-wide tensor, dh = D / H), with m = mem->len
+ * cached rows (oldest first) and K = m + W keys:
+ *    ctx = [mem rows; h rows]                       (K x D)
+ *    q = h Wq^T,  k = ctx WkE^T,  val = ctx Wv^T,  r = R[0:K] WkR^T
+ *    s_ij = ((q_i + u).k_j + (q_i + v).r_{m+i-j}) / sqrt(dh)   for j <= m + i
+ *    p_ij = softmax_j(s_ij),  o_i = sum_j p_ij val_j,  out = o Wo^T
+ *
+ * Conventions:
+ *  - Every weight matrix is stored out-major, W[d_out][d_in], row-major, and
+ *    a projection computes y = x W^T (the torch.nn.Linear layout).
+ *  - All tensors of one call share one storage dtype (txl_dtype). Products
+ *    and sums accumulate in fp32; softmax statistics, LayerNorm statistics and
+ *    pre-LayerNorm residual sums are kept in fp32.
+ *  - All pointers are device pointers unless stated otherwise; every buffer
+ *    belongs to the caller. The library never allocates device memory: scratch
+ *    space is the caller's workspace, sized by txl_workspace_bytes().
+ *  - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and
+ *    nothing waits for it: results are ready when the stream reaches them.
+ *  - Strides are in elements. `*_bstride` is the distance between batch rows;
+ *    rows within a batch row are D elements apart.
+ *  - Pointers must be aligned to 4 bytes; 16-byte aligned pointers with D a
+ *    multiple of 8 take the vectorised load path.
+ *
+ * Errors: a call returns a txl_status. Arguments are checked before anything is
+ * enqueued; a call that returns anything but TXL_OK has enqueued no work, except
+ * TXL_ERR_HIP, which reports a launch failure after earlier launches of the same
+ * call may have been enqueued. txl_last_error() gives a message for the calling
+ * thread's last failure.
+ */
+#ifndef TXL_H
+#define TXL_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TXL_OK = 0,
+    TXL_ERR_ARG = 1,          /* bad size, null or misaligned pointer, inconsistent memory */
+    TXL_ERR_UNSUPPORTED = 2,  /* a head width or dtype this build has no kernel for */
+    TXL_ERR_WORKSPACE = 3,    /* workspace missing or smaller than txl_workspace_bytes() */
+    TXL_ERR_HIP = 4           /* a HIP runtime call failed */
+} txl_status;
+
+typedef enum { TXL_FP32 = 0, TXL_BF16 = 1 } txl_dtype;
+
+typedef enum {
+    TXL_OP_REL_ATTN = 0,      /* txl_rel_attn_fwd */
+    TXL_OP_LAYER = 1,         /* txl_layer_fwd */
+    TXL_OP_STACK = 2          /* txl_stack_fwd_segments */
+} txl_op;
+
+/* One layer's parameters, all device pointers of the call's dtype.
+ * Attention (pages: W_q, W_k,E, W_k,R, W_v, W_o and the global biases u, v):
+ *   Wq, WkE, WkR, Wv, Wo  [D][D] out-major;  u, v  [D].
+ * Post-LN block (only read by txl_layer_fwd / txl_stack_fwd_segments):
+ *   ln1_g, ln1_b  [D];  W1 [F][D], b1 [F];  W2 [D][F], b2 [D];  ln2_g, ln2_b [D]. */
+typedef struct {
+    const void *Wq, *WkE, *WkR, *Wv, *Wo;
+    const void *u, *v;
+    const void *ln1_g, *ln1_b;
+    const void *W1, *b1;
+    const void *W2, *b2;
+    const void *ln2_g, *ln2_b;
+} txl_layer_params;
+
+/* Segment memory of one layer: a ring of M rows per batch row.
+ *   data  device, [B][M][D] of the call's dtype, owned by the caller;
+ *   M     capacity in rows (>= 1);
+ *   len   valid rows m, 0 <= len <= M (0 = empty memory);
+ *   head  physical row of the oldest valid row, 0 <= head < M.
+ * Logical row l (0 = oldest) of batch row b is data[b][(head + l) % M][:].
+ * Attention calls only read the ring; txl_mem_update advances it. */
+typedef struct {
+    void *data;
+    int M;
+    int len;
+    int head;
+} txl_mem;
+
+/* Workspace bytes that `op` needs for these sizes (M = memory capacity; F is
+ * ignored for TXL_OP_REL_ATTN). Returns 0 for invalid sizes. The same value
+ * serves every call of that op with sizes no larger than these. */
+size_t txl_workspace_bytes(txl_op op, txl_dtype dtype, int B, int W, int M, int D, int H, int F);
+
+/* Relative-encoding table R [R_len][D] (explainer, step 4: a sinusoidal encoding
+ * of the distance with no trained parameters). Row d holds
+ *   R[d][k] = sin(d * 10000^(-2k/D)),  R[d][D/2 + k] = cos(d * 10000^(-2k/D)),
+ * for k < D/2, evaluated in double precision and rounded to `dtype`.
+ * D must be even. */
+txl_status txl_sinusoid_table(txl_dtype dtype, int R_len, int D, void *R, void *stream);
+
+/* Relative multi-head attention of one segment over [mem; h], then the output
+ * projection (explainer steps 3-5; simulator equations; NumPy layer's
+ * relative_attention without its attention-weight output).
+ *   h    [B][W][D], batch stride h_bstride (>= W*D);
+ *   mem  NULL or a ring with len == 0 for an empty memory; read only;
+ *   p    reads Wq, WkE, WkR, Wv, Wo, u, v;
+ *   R    [R_len][D] distance table, R_len >= mem->len + W;
+ *   out  [B][W][D], batch stride out_bstride; must not overlap h or mem.
+ * D % H == 0 and D / H <= 64 (dh of 8, 32, 41 and 64 are the tested widths). */
+txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H,
+                            const void *h, long long h_bstride,
+                            const txl_mem *mem, const txl_layer_params *p,
+                            const void *R, int R_len,
+                            void *out, long long out_bstride,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Memory update (simulator: mem = last M rows of h~ = [mem; h]). Appends the
+ * last min(W, M) rows of h [B][W][D] (batch stride h_bstride) to the ring,
+ * dropping the oldest rows beyond M, and advances mem->len and mem->head on the
+ * host. The copy is exact. Enqueue it after every attention call that reads the
+ * old memory: the new rows overwrite the oldest ones. */
+txl_status txl_mem_update(txl_dtype dtype, int B, int D, txl_mem *mem,
+                          const void *h, long long h_bstride, int W, void *stream);
+
+/* One post-LN Transformer-XL block (NumPy layer's forward):
+ *   a = rel_attn(h, mem);  h1 = LN1(h + a);
+ *   y = LN2(h1 + ReLU(h1 W1^T + b1) W2^T + b2).
+ * y [B][W][D] with batch stride y_bstride must not overlap h or mem. The memory
+ * is not updated (call txl_mem_update with the same h afterwards). */
+txl_status txl_layer_fwd(txl_dtype dtype, int B, int W, int D, int H, int F,
+                         const void *h, long long h_bstride,
+                         const txl_mem *mem, const txl_layer_params *p,
+                         const void *R, int R_len,
+                         void *y, long long y_bstride,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/* Segment-by-segment forward of a stack of n_layers blocks over a stream
+ * (explainer steps 1-3 and 6): x [B][n_seg*W][D] is split into n_seg segments;
+ * for each segment in order and each layer n in order, layer n runs on its
+ * input h_n with memory mems[n], then mems[n] receives h_n (the layer's input
+ * rows) and h_{n+1} is the layer's output. y [B][n_seg*W][D] receives the last
+ * layer's output of every segment. mems[n] may start non-empty (resuming a
+ * stream); every ring must have the same M. R_len >= M + W. */
+txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, int F,
+                                  int n_layers, int n_seg, const void *x,
+                                  txl_mem *mems, const txl_layer_params *params,
+                                  const void *R, int R_len, void *y,
+                                  void *ws, size_t ws_bytes, void *stream);
+
+/* Event timing of the relative-attention kernel. Between txl_profile_begin and
+ * txl_profile_end, every attention-kernel launch (from any entry point, on its
+ * own stream) is bracketed by a pair of HIP events, up to max_launches
+ * launches. txl_profile_end waits for those events and returns the summed
+ * kernel time in milliseconds and the number of timed launches. Not
+ * thread-safe; meant for benchmarks. */
+txl_status txl_profile_begin(int max_launches);
+txl_status txl_profile_end(double *total_ms, int *launches);
+
+/* Static description of a status code, and the calling thread's last error. */
+const char *txl_status_string(txl_status s);
+const char *txl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TXL_H */

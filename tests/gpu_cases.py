@@ -1,0 +1,87 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and
+the oracle on the same seeded inputs, and compare.
+
+Error metric: for each output tensor and segment, e = max|gpu - oracle| / max|oracle|.
+Thresholds: 1e-4 for fp32 storage, 2e-2 for bf16 storage with fp32 accumulation.
+"""
+from __future__ import annotations
+
+import sys
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from oracle import oracle as orc
+from transformer_xl_segment_amd import binding as tb
+from transformer_xl_segment_amd import synthetic as syn
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+TDT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(g: np.ndarray, o: np.ndarray) -> float:
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    assert g.shape == o.shape, (g.shape, o.shape)
+    assert np.all(np.isfinite(g)), "non-finite GPU output"
+    return float(np.max(np.abs(g - o)) / max(np.max(np.abs(o)), 1e-30))
+
+
+def table(R_len: int, D: int, dtype: str) -> np.ndarray:
+    """Oracle distance table stored in the workload's dtype (fp32 values)."""
+    R = orc.sinusoid_table(R_len, D).astype(np.float32)
+    return syn.round_to_bf16(R) if dtype == "bf16" else R
+
+
+def dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(TDT[dtype])
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def nan_workspace(nbytes: int) -> torch.Tensor:
+    """Workspace filled with 0xFF bytes (NaN in fp32 and bf16): any scratch the
+    kernels read without writing first shows up as a non-finite output."""
+    return torch.full((max(nbytes, 256),), 255, dtype=torch.uint8, device="cuda")
+
+
+def run_attn_segments(prob: syn.Problem, R: np.ndarray, batch: Optional[Sequence[int]] = None,
+                      warm: bool = False, check_every: bool = True) -> Dict[str, float]:
+    """Single-layer attention workloads: per segment rel_attn_fwd then mem_update,
+    compared with the oracle segment by segment (optionally on a batch subset)."""
+    wl = prob.wl
+    dt = wl.dtype
+    p = prob.params[0]
+    B, W, D, H, M = prob.x.shape[0], wl.W, wl.D, wl.H, wl.M
+    x = dev(prob.x, dt)
+    params = tb.LayerParams.from_numpy(p, TDT[dt], "cuda")
+    Rd = dev(R, dt)
+    ring = tb.MemoryRing.empty(B, M, D, TDT[dt], "cuda")
+    ws = nan_workspace(tb.workspace_bytes(tb.OP_REL_ATTN, TDT[dt], B, W, M, D, H))
+    omem = None
+    bsel = list(range(B)) if batch is None else list(batch)
+    if warm:
+        assert prob.warm_mem is not None
+        tb.mem_update(ring, dev(prob.warm_mem, dt))
+        omem = prob.warm_mem[bsel].astype(np.float64)
+    errs = {}
+    for t in range(wl.S):
+        h = x[:, t * W:(t + 1) * W]
+        out = tb.rel_attn_fwd(h, ring, params, Rd, H, workspace=ws)
+        tb.mem_update(ring, h)
+        torch.cuda.synchronize()
+        hn = prob.x[bsel, t * W:(t + 1) * W].astype(np.float64)
+        ref = orc.rel_attn(hn, omem, p, R, H)
+        errs[f"seg{t}"] = rel_err(host(out)[bsel], ref)
+        omem = orc.mem_update(omem, hn, M)
+        # the ring's logical content equals the oracle's memory, bit for bit
+        np.testing.assert_array_equal(host(ring.logical())[bsel], omem)
+    return errs

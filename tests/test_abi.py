@@ -1,0 +1,142 @@
+"""C-ABI contract tests that need no GPU.
+
+The library must load, export every function include/txl.h declares, size
+workspaces, and reject bad arguments with a status code before it touches the
+HIP runtime (so these calls are safe without a device: the pointers passed
+here are never dereferenced).
+"""
+import ctypes
+
+import pytest
+
+from transformer_xl_segment_amd import binding as tb
+
+
+def test_header_functions_are_exported():
+    L = tb.lib()
+    names = tb.exported_names()
+    assert "txl_rel_attn_fwd" in names and "txl_stack_fwd_segments" in names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in txl.h but not exported"
+    assert len(names) >= 10
+
+
+def test_status_strings():
+    L = tb.lib()
+    for st in range(5):
+        assert L.txl_status_string(st)
+    assert L.txl_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes():
+    L = tb.lib()
+    ws = L.txl_workspace_bytes
+    a = ws(tb.OP_REL_ATTN, tb.TXL_BF16, 16, 512, 512, 512, 8, 0)
+    assert a > 0 and a % 256 == 0
+    # a layer needs at least what attention needs; the stack at least the layer
+    lay = ws(tb.OP_LAYER, tb.TXL_BF16, 16, 512, 512, 512, 8, 2048)
+    stk = ws(tb.OP_STACK, tb.TXL_BF16, 16, 512, 512, 512, 8, 2048)
+    assert a < lay < stk
+    # fp32 operands take more room than bf16
+    assert ws(tb.OP_REL_ATTN, tb.TXL_FP32, 16, 512, 512, 512, 8, 0) > a
+    # monotone in the memory capacity
+    assert ws(tb.OP_REL_ATTN, tb.TXL_BF16, 16, 512, 1024, 512, 8, 0) > a
+    # invalid sizes
+    assert ws(tb.OP_REL_ATTN, tb.TXL_BF16, 16, 512, 512, 510, 8, 0) == 0   # D % H
+    assert ws(tb.OP_REL_ATTN, tb.TXL_BF16, 0, 512, 512, 512, 8, 0) == 0
+    assert ws(tb.OP_LAYER, tb.TXL_BF16, 1, 4, 4, 16, 2, 0) == 0          # F missing
+    assert ws(7, tb.TXL_BF16, 1, 4, 4, 16, 2, 0) == 0
+
+
+FAKE = 1 << 20   # an aligned, never-dereferenced address
+
+
+def _params():
+    return tb._Params(*[FAKE] * len(tb._PARAM_FIELDS))
+
+
+def _attn(dt=tb.TXL_FP32, B=1, W=4, D=16, H=2, hs=64, mem=None, p=None, R=FAKE, R_len=8,
+          out=FAKE, os_=64, ws=None, wsb=0):
+    L = tb.lib()
+    p = p if p is not None else _params()
+    return L.txl_rel_attn_fwd(dt, B, W, D, H, FAKE, hs, ctypes.byref(mem) if mem else None,
+                              ctypes.byref(p), R, R_len, out, os_, ws, wsb, None)
+
+
+def test_rel_attn_rejects_bad_arguments():
+    assert _attn(D=18, H=4) == tb.TXL_ERR_ARG            # D % H
+    assert _attn(D=15, H=3) == tb.TXL_ERR_ARG            # odd D
+    assert _attn(B=0) == tb.TXL_ERR_ARG
+    assert _attn(dt=5) == tb.TXL_ERR_UNSUPPORTED
+    assert _attn(D=130, H=1, hs=520, os_=520, R_len=8) == tb.TXL_ERR_UNSUPPORTED   # dh > 64
+    assert _attn(hs=10) == tb.TXL_ERR_ARG                # batch stride < W*D
+    assert _attn(out=FAKE + 2) == tb.TXL_ERR_ARG          # misaligned
+    assert _attn(R=None) == tb.TXL_ERR_ARG
+    assert _attn(R_len=3) == tb.TXL_ERR_ARG               # R_len < m + W
+    p = _params()
+    p.WkR = None
+    assert _attn(p=p) == tb.TXL_ERR_ARG
+    bad_len = tb._Mem(FAKE, 4, 5, 0)                       # len > M
+    assert _attn(mem=bad_len) == tb.TXL_ERR_ARG
+    bad_head = tb._Mem(FAKE, 4, 2, 4)                      # head >= M
+    assert _attn(mem=bad_head) == tb.TXL_ERR_ARG
+    ok_mem = tb._Mem(FAKE, 4, 4, 1)
+    assert _attn(mem=ok_mem, R_len=7) == tb.TXL_ERR_ARG    # needs 4 + 4 rows
+    # everything valid but no workspace
+    assert _attn(mem=ok_mem, R_len=8) == tb.TXL_ERR_WORKSPACE
+    assert b"workspace" in tb.lib().txl_last_error()
+
+
+def test_mem_update_rejects_bad_arguments():
+    L = tb.lib()
+    m = tb._Mem(FAKE, 4, 0, 0)
+    assert L.txl_mem_update(tb.TXL_FP32, 1, 16, None, FAKE, 64, 4, None) == tb.TXL_ERR_ARG
+    assert L.txl_mem_update(tb.TXL_FP32, 1, 16, ctypes.byref(m), None, 64, 4, None) == tb.TXL_ERR_ARG
+    assert L.txl_mem_update(tb.TXL_FP32, 1, 16, ctypes.byref(m), FAKE, 63, 4, None) == tb.TXL_ERR_ARG
+    m.len = 9
+    assert L.txl_mem_update(tb.TXL_FP32, 1, 16, ctypes.byref(m), FAKE, 64, 4, None) == tb.TXL_ERR_ARG
+    assert (m.len, m.head) == (9, 0)     # untouched on failure
+
+
+def test_layer_and_stack_reject_bad_arguments():
+    L = tb.lib()
+    p = _params()
+    # missing FFN weight
+    q = _params()
+    q.W1 = None
+    assert L.txl_layer_fwd(tb.TXL_FP32, 1, 4, 16, 2, 32, FAKE, 64, None, ctypes.byref(q), FAKE, 4,
+                           FAKE, 64, None, 0, None) == tb.TXL_ERR_ARG
+    # odd F
+    assert L.txl_layer_fwd(tb.TXL_FP32, 1, 4, 16, 2, 31, FAKE, 64, None, ctypes.byref(p), FAKE, 4,
+                           FAKE, 64, None, 0, None) == tb.TXL_ERR_ARG
+    # D > 1024 for the LayerNorm kernels
+    assert L.txl_layer_fwd(tb.TXL_FP32, 1, 4, 1040, 26, 32, FAKE, 4160, None, ctypes.byref(p), FAKE, 4,
+                           FAKE, 4160, None, 0, None) == tb.TXL_ERR_UNSUPPORTED
+    assert L.txl_layer_fwd(tb.TXL_FP32, 1, 4, 16, 2, 32, FAKE, 64, None, ctypes.byref(p), FAKE, 4,
+                           FAKE, 64, None, 0, None) == tb.TXL_ERR_WORKSPACE
+    mems = (tb._Mem * 2)(tb._Mem(FAKE, 4, 0, 0), tb._Mem(FAKE, 8, 0, 0))   # unequal M
+    ps = (tb._Params * 2)(_params(), _params())
+    assert L.txl_stack_fwd_segments(tb.TXL_FP32, 1, 4, 16, 2, 32, 2, 3, FAKE, mems, ps, FAKE, 16,
+                                    FAKE, None, 0, None) == tb.TXL_ERR_ARG
+    mems[1].M = 4
+    assert L.txl_stack_fwd_segments(tb.TXL_FP32, 1, 4, 16, 2, 32, 2, 3, FAKE, mems, ps, FAKE, 7,
+                                    FAKE, None, 0, None) == tb.TXL_ERR_ARG      # R_len < M + W
+    assert L.txl_stack_fwd_segments(tb.TXL_FP32, 1, 4, 16, 2, 32, 2, 3, FAKE, mems, ps, FAKE, 8,
+                                    FAKE, None, 0, None) == tb.TXL_ERR_WORKSPACE
+
+
+def test_sinusoid_and_profiler_reject_bad_arguments():
+    L = tb.lib()
+    assert L.txl_sinusoid_table(tb.TXL_FP32, 8, 15, FAKE, None) == tb.TXL_ERR_ARG
+    assert L.txl_sinusoid_table(tb.TXL_FP32, 0, 16, FAKE, None) == tb.TXL_ERR_ARG
+    assert L.txl_sinusoid_table(3, 8, 16, FAKE, None) == tb.TXL_ERR_UNSUPPORTED
+    assert L.txl_profile_begin(0) == tb.TXL_ERR_ARG
+    ms, n = ctypes.c_double(), ctypes.c_int()
+    assert L.txl_profile_end(ctypes.byref(ms), ctypes.byref(n)) == tb.TXL_ERR_ARG   # not active
+
+
+def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(tb, "_lib", None)
+    monkeypatch.setattr(tb, "LIB_PATH", str(tmp_path / "libtxl.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        tb.lib()

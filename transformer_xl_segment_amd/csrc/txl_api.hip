@@ -1,0 +1,465 @@
+// txl_api.hip -- the C ABI declared in include/txl.h: argument checks,
+// workspace layout and the launch sequence of each entry point.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/txl.h"
+#include "txl_internal.hpp"
+
+using namespace txl;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+txl_status fail(txl_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+txl_status hip_check(hipError_t e, const char *what) {
+    if (e == hipSuccess) return TXL_OK;
+    return fail(TXL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define TXL_TRY(expr)                          \
+    do {                                       \
+        txl_status st_ = (expr);               \
+        if (st_ != TXL_OK) return st_;         \
+    } while (0)
+
+size_t es_of(txl_dtype dt) { return dt == TXL_BF16 ? 2 : 4; }
+long long round_up(long long x, long long a) { return (x + a - 1) / a * a; }
+bool al4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+// ---------------------------------------------------------------------------
+// Workspace layout. Every buffer starts on a 256-byte boundary.
+// ---------------------------------------------------------------------------
+struct Layout {
+    size_t qu, qv, ke, vt, rk, o;      // attention operands and output
+    size_t z, h1, f;                   // block: fp32 pre-LN sums, LN1 output, FFN hidden
+    size_t hb0, hb1;                   // stack: inter-layer activations
+    size_t total;
+    int Wp, Kp, dp;
+};
+
+Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F) {
+    Layout L;
+    memset(&L, 0, sizeof(L));
+    const size_t es = es_of(dt);
+    const int dh = D / H;
+    L.dp = attn_dp(dh);
+    L.Wp = (int)round_up(W, ATTN_QBLOCK);
+    L.Kp = (int)round_up(Kmax, ATTN_KBLOCK);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = (size_t)round_up((long long)(off + bytes), 256);
+        return at;
+    };
+    const size_t q_bytes = (size_t)B * H * L.Wp * L.dp * es;
+    const size_t k_bytes = (size_t)B * H * L.Kp * L.dp * es;
+    L.qu = take(q_bytes);
+    L.qv = take(q_bytes);
+    L.ke = take(k_bytes);
+    L.vt = take(k_bytes);
+    L.rk = take((size_t)H * L.Kp * L.dp * es);
+    L.o = take((size_t)B * W * D * es);
+    if (op == TXL_OP_LAYER || op == TXL_OP_STACK) {
+        L.z = take((size_t)B * W * D * 4);
+        L.h1 = take((size_t)B * W * D * es);
+        L.f = take((size_t)B * W * F * es);
+    }
+    if (op == TXL_OP_STACK) {
+        L.hb0 = take((size_t)B * W * D * es);
+        L.hb1 = take((size_t)B * W * D * es);
+    }
+    L.total = off;
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// Attention-kernel timing (txl_profile_begin / txl_profile_end).
+// ---------------------------------------------------------------------------
+struct Profiler {
+    bool on = false;
+    int used = 0;
+    std::vector<hipEvent_t> start, stop;
+} g_prof;
+
+hipError_t attn_launch(bool bf16, const AttnArgs &a, hipStream_t s) {
+    const bool timed = g_prof.on && g_prof.used < (int)g_prof.start.size();
+    if (timed) {
+        hipError_t e = hipEventRecord(g_prof.start[g_prof.used], s);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch_rel_attn(bf16, a, s);
+    if (e != hipSuccess) return e;
+    if (timed) {
+        e = hipEventRecord(g_prof.stop[g_prof.used], s);
+        if (e != hipSuccess) return e;
+        ++g_prof.used;
+    }
+    return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------
+// Argument checks shared by the entry points.
+// ---------------------------------------------------------------------------
+txl_status check_shape(txl_dtype dt, int B, int W, int D, int H) {
+    if (dt != TXL_FP32 && dt != TXL_BF16) return fail(TXL_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if (B < 1 || W < 1 || D < 2 || H < 1) return fail(TXL_ERR_ARG, "sizes must be positive (B=%d W=%d D=%d H=%d)", B, W, D, H);
+    if (D % H) return fail(TXL_ERR_ARG, "D=%d is not a multiple of H=%d", D, H);
+    if (D % 2) return fail(TXL_ERR_ARG, "D=%d must be even", D);
+    if (!rel_attn_supported(D / H)) return fail(TXL_ERR_UNSUPPORTED, "head width %d > 64 is not supported", D / H);
+    if ((long long)B * W > (1LL << 22) / 2) return fail(TXL_ERR_UNSUPPORTED, "B*W=%lld too large", (long long)B * W);
+    return TXL_OK;
+}
+
+txl_status check_mem(const txl_mem *mem, int W) {
+    if (!mem) return TXL_OK;
+    if (mem->M < 1) return fail(TXL_ERR_ARG, "memory capacity M=%d must be >= 1", mem->M);
+    if (mem->len < 0 || mem->len > mem->M) return fail(TXL_ERR_ARG, "memory len=%d outside [0, M=%d]", mem->len, mem->M);
+    if (mem->head < 0 || mem->head >= mem->M) return fail(TXL_ERR_ARG, "memory head=%d outside [0, M=%d)", mem->head, mem->M);
+    if (!mem->data) return fail(TXL_ERR_ARG, "memory data is NULL");
+    if (!al4(mem->data)) return fail(TXL_ERR_ARG, "memory data must be 4-byte aligned");
+    if ((long long)mem->M + W > (1LL << 20)) return fail(TXL_ERR_UNSUPPORTED, "M + W too large");
+    return TXL_OK;
+}
+
+// The GEMM epilogue splits row indices with a float reciprocal, exact below 2^22.
+txl_status check_rows_budget(int B, int W, int M) {
+    const long long kp = round_up((long long)M + W, ATTN_KBLOCK);
+    if ((long long)B * kp >= (1LL << 22) || (long long)B * round_up(W, ATTN_QBLOCK) >= (1LL << 22))
+        return fail(TXL_ERR_UNSUPPORTED, "B * (M + W) = %lld rows exceeds 2^22", (long long)B * kp);
+    return TXL_OK;
+}
+
+txl_status check_attn_params(const txl_layer_params *p) {
+    if (!p) return fail(TXL_ERR_ARG, "params is NULL");
+    const void *ptrs[] = {p->Wq, p->WkE, p->WkR, p->Wv, p->Wo, p->u, p->v};
+    const char *names[] = {"Wq", "WkE", "WkR", "Wv", "Wo", "u", "v"};
+    for (int i = 0; i < 7; ++i) {
+        if (!ptrs[i]) return fail(TXL_ERR_ARG, "parameter %s is NULL", names[i]);
+        if (!al4(ptrs[i])) return fail(TXL_ERR_ARG, "parameter %s must be 4-byte aligned", names[i]);
+    }
+    return TXL_OK;
+}
+
+txl_status check_block_params(const txl_layer_params *p, int F) {
+    TXL_TRY(check_attn_params(p));
+    if (F < 2 || F % 2) return fail(TXL_ERR_ARG, "F=%d must be even and >= 2", F);
+    const void *ptrs[] = {p->ln1_g, p->ln1_b, p->W1, p->b1, p->W2, p->b2, p->ln2_g, p->ln2_b};
+    const char *names[] = {"ln1_g", "ln1_b", "W1", "b1", "W2", "b2", "ln2_g", "ln2_b"};
+    for (int i = 0; i < 8; ++i) {
+        if (!ptrs[i]) return fail(TXL_ERR_ARG, "parameter %s is NULL", names[i]);
+        if (!al4(ptrs[i])) return fail(TXL_ERR_ARG, "parameter %s must be 4-byte aligned", names[i]);
+    }
+    return TXL_OK;
+}
+
+txl_status check_rows(const void *p, long long bstride, int W, int D, txl_dtype dt, const char *name) {
+    if (!p) return fail(TXL_ERR_ARG, "%s is NULL", name);
+    if (!al4(p)) return fail(TXL_ERR_ARG, "%s must be 4-byte aligned", name);
+    if (bstride < (long long)W * D) return fail(TXL_ERR_ARG, "%s batch stride %lld < W*D", name, bstride);
+    if ((bstride * (long long)es_of(dt)) % 4) return fail(TXL_ERR_ARG, "%s batch stride must keep rows 4-byte aligned", name);
+    return TXL_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Enqueue projections + fused attention; the attention output lands in ws+L.o
+// as [B][W][D] rows.
+// ---------------------------------------------------------------------------
+txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const void *h, long long h_bstride,
+                             const txl_mem *mem, const txl_layer_params *p, const void *R, char *ws,
+                             const Layout &L, hipStream_t s) {
+    const bool bf = dt == TXL_BF16;
+    const int dh = D / H, dp = L.dp;
+    const int m = mem ? mem->len : 0;
+    const int K = m + W;
+    const int Kp = (int)round_up(K, ATTN_KBLOCK);
+
+    GemmLaunch g;
+    memset(&g, 0, sizeof(g));
+    // Q: (h Wq^T + u, + v) * log2(e)/sqrt(dh), head-major
+    GemmProblem &q = g.p[0];
+    q.rows = B * L.Wp; q.cols = H * dp; q.kdim = D;
+    q.seg_rows = L.Wp; q.valid_rows = W;
+    q.a_mode = A_ROWS; q.a = h; q.a_ld = D; q.a_bstride = h_bstride;
+    q.b_mode = B_HEADS; q.b0 = p->Wq; q.b_split = q.cols; q.b_ld = D;
+    q.dh = dh; q.dhp = dp; q.heads = H;
+    q.epi = EPI_QUV; q.c0 = ws + L.qu; q.c1 = ws + L.qv; q.u = p->u; q.v = p->v;
+    q.qscale = (float)(1.4426950408889634 / sqrt((double)dh));
+    // K_E and V from the context [mem; h]
+    GemmProblem &kv = g.p[1];
+    kv.rows = B * Kp; kv.cols = 2 * H * dp; kv.kdim = D;
+    kv.seg_rows = Kp; kv.valid_rows = W;
+    kv.a_mode = A_CONTEXT; kv.a = h; kv.a_ld = D; kv.a_bstride = h_bstride;
+    kv.ring = m > 0 ? mem->data : h; kv.ring_bstride = m > 0 ? (long long)mem->M * D : 0;
+    kv.ring_M = m > 0 ? mem->M : 1; kv.ring_head = m > 0 ? mem->head : 0; kv.mem_len = m;
+    kv.b_mode = B_HEADS; kv.b0 = p->WkE; kv.b1 = p->Wv; kv.b_split = H * dp; kv.b_ld = D;
+    kv.dh = dh; kv.dhp = dp; kv.heads = H;
+    kv.epi = EPI_KV; kv.c0 = ws + L.ke; kv.c1 = ws + L.vt;
+    // r = R[0:K] WkR^T, shared by the batch
+    GemmProblem &r = g.p[2];
+    r.rows = Kp; r.cols = H * dp; r.kdim = D;
+    r.seg_rows = Kp; r.valid_rows = K;
+    r.a_mode = A_ROWS; r.a = R; r.a_ld = D; r.a_bstride = 0;
+    r.b_mode = B_HEADS; r.b0 = p->WkR; r.b_split = r.cols; r.b_ld = D;
+    r.dh = dh; r.dhp = dp; r.heads = H;
+    r.epi = EPI_HEADS; r.c0 = ws + L.rk;
+    g.count = 3;
+    int t = 0;
+    for (int i = 0; i < 3; ++i) {
+        GemmProblem &P = g.p[i];
+        P.tiles_n = (P.cols + 127) / 128;
+        P.tile_begin = t;
+        P.tile_count = ((P.rows + 127) / 128) * P.tiles_n;
+        t += P.tile_count;
+    }
+    g.total_tiles = t;
+    TXL_TRY(hip_check(launch_gemm(bf, g, s), "projection GEMM launch"));
+
+    AttnArgs a;
+    a.qu = ws + L.qu; a.qv = ws + L.qv; a.ke = ws + L.ke; a.vt = ws + L.vt; a.rk = ws + L.rk;
+    a.o = ws + L.o; a.o_bstride = (long long)W * D;
+    a.B = B; a.H = H; a.W = W; a.Wp = L.Wp; a.m = m; a.K = K; a.Kp = Kp; a.dh = dh; a.dp = dp; a.D = D;
+    TXL_TRY(hip_check(attn_launch(bf, a, s), "attention launch"));
+    return TXL_OK;
+}
+
+GemmLaunch single(const GemmProblem &p) {
+    GemmLaunch g;
+    memset(&g, 0, sizeof(g));
+    g.p[0] = p;
+    g.p[0].tiles_n = (p.cols + 127) / 128;
+    g.p[0].tile_begin = 0;
+    g.p[0].tile_count = ((p.rows + 127) / 128) * g.p[0].tiles_n;
+    g.count = 1;
+    g.total_tiles = g.p[0].tile_count;
+    return g;
+}
+
+// Dense rows GEMM: C(b, t) = A(b, t) W^T (+bias, relu, +res), A/C [B][W][*].
+GemmProblem rows_problem(int B, int W, int kdim, int cols, const void *a, long long a_ld, long long a_bstride,
+                         const void *w, void *c, long long c_ld, long long c_bstride) {
+    GemmProblem p;
+    memset(&p, 0, sizeof(p));
+    p.rows = B * W; p.cols = cols; p.kdim = kdim;
+    p.seg_rows = W; p.valid_rows = W;
+    p.a_mode = A_ROWS; p.a = a; p.a_ld = a_ld; p.a_bstride = a_bstride;
+    p.b_mode = B_ROWS; p.b0 = w; p.b_split = cols; p.b_ld = kdim;
+    p.dh = 1; p.dhp = 1; p.heads = 1;
+    p.epi = EPI_ROWS; p.c0 = c; p.c_ld = c_ld; p.c_bstride = c_bstride;
+    return p;
+}
+
+txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const void *h, long long h_bstride,
+                         const txl_mem *mem, const txl_layer_params *p, const void *R, void *y,
+                         long long y_bstride, char *ws, const Layout &L, hipStream_t s) {
+    const bool bf = dt == TXL_BF16;
+    TXL_TRY(enqueue_attention(dt, B, W, D, H, h, h_bstride, mem, p, R, ws, L, s));
+    const long long WD = (long long)W * D;
+    // z = h + O Wo^T (fp32)
+    GemmProblem wo = rows_problem(B, W, D, D, ws + L.o, D, WD, p->Wo, ws + L.z, D, WD);
+    wo.res = h; wo.res_ld = D; wo.res_bstride = h_bstride; wo.out_f32 = 1;
+    TXL_TRY(hip_check(launch_gemm(bf, single(wo), s), "output projection launch"));
+    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), p->ln1_g, p->ln1_b, ws + L.h1, WD, B, W, D, s),
+                      "LayerNorm launch"));
+    // f = ReLU(h1 W1^T + b1)
+    GemmProblem f1 = rows_problem(B, W, D, F, ws + L.h1, D, WD, p->W1, ws + L.f, F, (long long)W * F);
+    f1.bias = p->b1; f1.relu = 1;
+    TXL_TRY(hip_check(launch_gemm(bf, single(f1), s), "FFN1 launch"));
+    // z = h1 + f W2^T + b2 (fp32)
+    GemmProblem f2 = rows_problem(B, W, F, D, ws + L.f, F, (long long)W * F, p->W2, ws + L.z, D, WD);
+    f2.bias = p->b2; f2.res = ws + L.h1; f2.res_ld = D; f2.res_bstride = WD; f2.out_f32 = 1;
+    TXL_TRY(hip_check(launch_gemm(bf, single(f2), s), "FFN2 launch"));
+    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), p->ln2_g, p->ln2_b, y, y_bstride, B, W, D, s),
+                      "LayerNorm launch"));
+    return TXL_OK;
+}
+
+txl_status enqueue_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const void *h, long long h_bstride, int W,
+                              hipStream_t s) {
+    const int n = W < mem->M ? W : mem->M;
+    const int pos0 = (int)(((long long)mem->head + mem->len) % mem->M);
+    TXL_TRY(hip_check(launch_ring_write(dt == TXL_BF16, mem->data, mem->M, D, pos0, h, h_bstride, W - n, n, B, s),
+                      "memory update launch"));
+    if (mem->len + n <= mem->M) {
+        mem->len += n;
+    } else {
+        mem->head = (int)(((long long)mem->head + mem->len + n - mem->M) % mem->M);
+        mem->len = mem->M;
+    }
+    return TXL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t txl_workspace_bytes(txl_op op, txl_dtype dtype, int B, int W, int M, int D, int H, int F) {
+    if (B < 1 || W < 1 || D < 2 || H < 1 || D % H || M < 0) return 0;
+    if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
+    if (op != TXL_OP_REL_ATTN && op != TXL_OP_LAYER && op != TXL_OP_STACK) return 0;
+    if (op != TXL_OP_REL_ATTN && F < 1) return 0;
+    return plan(op, dtype, B, W, M + W, D, H, op == TXL_OP_REL_ATTN ? 0 : F).total;
+}
+
+txl_status txl_sinusoid_table(txl_dtype dtype, int R_len, int D, void *R, void *stream) {
+    if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (R_len < 1 || D < 2 || D % 2) return fail(TXL_ERR_ARG, "need R_len >= 1 and an even D >= 2");
+    if (!R || !al4(R)) return fail(TXL_ERR_ARG, "R must be a non-NULL 4-byte aligned pointer");
+    return hip_check(launch_sinusoid(dtype == TXL_BF16, R, R_len, D, (hipStream_t)stream), "sinusoid launch");
+}
+
+txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H, const void *h, long long h_bstride,
+                            const txl_mem *mem, const txl_layer_params *p, const void *R, int R_len, void *out,
+                            long long out_bstride, void *ws, size_t ws_bytes, void *stream) {
+    TXL_TRY(check_shape(dtype, B, W, D, H));
+    TXL_TRY(check_rows(h, h_bstride, W, D, dtype, "h"));
+    TXL_TRY(check_rows(out, out_bstride, W, D, dtype, "out"));
+    TXL_TRY(check_mem(mem, W));
+    TXL_TRY(check_attn_params(p));
+    const int m = mem ? mem->len : 0;
+    TXL_TRY(check_rows_budget(B, W, m));
+    if (!R || !al4(R)) return fail(TXL_ERR_ARG, "R must be a non-NULL 4-byte aligned pointer");
+    if (R_len < m + W) return fail(TXL_ERR_ARG, "R_len=%d < mem len + W = %d", R_len, m + W);
+    const Layout L = plan(TXL_OP_REL_ATTN, dtype, B, W, m + W, D, H, 0);
+    if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+    if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, mem, p, R, w, L, s));
+    GemmProblem wo = rows_problem(B, W, D, D, w + L.o, D, (long long)W * D, p->Wo, out, D, out_bstride);
+    return hip_check(launch_gemm(dtype == TXL_BF16, single(wo), s), "output projection launch");
+}
+
+txl_status txl_mem_update(txl_dtype dtype, int B, int D, txl_mem *mem, const void *h, long long h_bstride, int W,
+                          void *stream) {
+    if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (B < 1 || D < 2 || W < 1 || D % 2) return fail(TXL_ERR_ARG, "need B, W >= 1 and an even D >= 2");
+    if (!mem) return fail(TXL_ERR_ARG, "memory is NULL");
+    TXL_TRY(check_mem(mem, W));
+    TXL_TRY(check_rows(h, h_bstride, W, D, dtype, "h"));
+    return enqueue_mem_update(dtype, B, D, mem, h, h_bstride, W, (hipStream_t)stream);
+}
+
+txl_status txl_layer_fwd(txl_dtype dtype, int B, int W, int D, int H, int F, const void *h, long long h_bstride,
+                         const txl_mem *mem, const txl_layer_params *p, const void *R, int R_len, void *y,
+                         long long y_bstride, void *ws, size_t ws_bytes, void *stream) {
+    TXL_TRY(check_shape(dtype, B, W, D, H));
+    if (D > 1024) return fail(TXL_ERR_UNSUPPORTED, "LayerNorm supports D <= 1024 (got %d)", D);
+    TXL_TRY(check_rows(h, h_bstride, W, D, dtype, "h"));
+    TXL_TRY(check_rows(y, y_bstride, W, D, dtype, "y"));
+    TXL_TRY(check_mem(mem, W));
+    TXL_TRY(check_block_params(p, F));
+    const int m = mem ? mem->len : 0;
+    TXL_TRY(check_rows_budget(B, W, m));
+    if (!R || !al4(R)) return fail(TXL_ERR_ARG, "R must be a non-NULL 4-byte aligned pointer");
+    if (R_len < m + W) return fail(TXL_ERR_ARG, "R_len=%d < mem len + W = %d", R_len, m + W);
+    const Layout L = plan(TXL_OP_LAYER, dtype, B, W, m + W, D, H, F);
+    if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+    if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
+    return enqueue_block(dtype, B, W, D, H, F, h, h_bstride, mem, p, R, y, y_bstride, (char *)ws, L,
+                         (hipStream_t)stream);
+}
+
+txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, int F, int n_layers, int n_seg,
+                                  const void *x, txl_mem *mems, const txl_layer_params *params, const void *R,
+                                  int R_len, void *y, void *ws, size_t ws_bytes, void *stream) {
+    TXL_TRY(check_shape(dtype, B, W, D, H));
+    if (D > 1024) return fail(TXL_ERR_UNSUPPORTED, "LayerNorm supports D <= 1024 (got %d)", D);
+    if (n_layers < 1 || n_seg < 1) return fail(TXL_ERR_ARG, "n_layers and n_seg must be >= 1");
+    const long long seq = (long long)n_seg * W;
+    TXL_TRY(check_rows(x, seq * D, W, D, dtype, "x"));
+    TXL_TRY(check_rows(y, seq * D, W, D, dtype, "y"));
+    if (!mems || !params) return fail(TXL_ERR_ARG, "mems and params must not be NULL");
+    const int M = mems[0].M;
+    for (int l = 0; l < n_layers; ++l) {
+        TXL_TRY(check_mem(&mems[l], W));
+        if (mems[l].M != M) return fail(TXL_ERR_ARG, "every memory ring must have the same M");
+        TXL_TRY(check_block_params(&params[l], F));
+    }
+    TXL_TRY(check_rows_budget(B, W, M));
+    if (!R || !al4(R)) return fail(TXL_ERR_ARG, "R must be a non-NULL 4-byte aligned pointer");
+    if (R_len < M + W) return fail(TXL_ERR_ARG, "R_len=%d < M + W = %d", R_len, M + W);
+    const Layout L = plan(TXL_OP_STACK, dtype, B, W, M + W, D, H, F);
+    if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+    if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    const size_t es = es_of(dtype);
+    for (int t = 0; t < n_seg; ++t) {
+        const char *hin = (const char *)x + (size_t)t * W * D * es;
+        long long hin_bs = seq * D;
+        for (int l = 0; l < n_layers; ++l) {
+            const bool last = l == n_layers - 1;
+            char *hout = last ? (char *)y + (size_t)t * W * D * es : w + ((l & 1) ? L.hb1 : L.hb0);
+            const long long hout_bs = last ? seq * D : (long long)W * D;
+            TXL_TRY(enqueue_block(dtype, B, W, D, H, F, hin, hin_bs, &mems[l], &params[l], R, hout, hout_bs, w, L, s));
+            TXL_TRY(enqueue_mem_update(dtype, B, D, &mems[l], hin, hin_bs, W, s));
+            hin = hout;
+            hin_bs = hout_bs;
+        }
+    }
+    return TXL_OK;
+}
+
+txl_status txl_profile_begin(int max_launches) {
+    if (max_launches < 1) return fail(TXL_ERR_ARG, "max_launches must be >= 1");
+    if (g_prof.on) return fail(TXL_ERR_ARG, "profiling already active");
+    for (size_t i = 0; i < g_prof.start.size(); ++i) {
+        (void)hipEventDestroy(g_prof.start[i]);
+        (void)hipEventDestroy(g_prof.stop[i]);
+    }
+    g_prof.start.assign(max_launches, nullptr);
+    g_prof.stop.assign(max_launches, nullptr);
+    for (int i = 0; i < max_launches; ++i) {
+        TXL_TRY(hip_check(hipEventCreate(&g_prof.start[i]), "hipEventCreate"));
+        TXL_TRY(hip_check(hipEventCreate(&g_prof.stop[i]), "hipEventCreate"));
+    }
+    g_prof.used = 0;
+    g_prof.on = true;
+    return TXL_OK;
+}
+
+txl_status txl_profile_end(double *total_ms, int *launches) {
+    if (!g_prof.on) return fail(TXL_ERR_ARG, "profiling is not active");
+    g_prof.on = false;
+    double sum = 0.0;
+    for (int i = 0; i < g_prof.used; ++i) {
+        TXL_TRY(hip_check(hipEventSynchronize(g_prof.stop[i]), "hipEventSynchronize"));
+        float ms = 0.f;
+        TXL_TRY(hip_check(hipEventElapsedTime(&ms, g_prof.start[i], g_prof.stop[i]), "hipEventElapsedTime"));
+        sum += ms;
+    }
+    if (total_ms) *total_ms = sum;
+    if (launches) *launches = g_prof.used;
+    return TXL_OK;
+}
+
+const char *txl_status_string(txl_status s) {
+    switch (s) {
+        case TXL_OK: return "ok";
+        case TXL_ERR_ARG: return "invalid argument";
+        case TXL_ERR_UNSUPPORTED: return "unsupported configuration";
+        case TXL_ERR_WORKSPACE: return "workspace missing or too small";
+        case TXL_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *txl_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,295 @@
+// txl_gemm.hip -- grouped GEMM on the gfx950 matrix cores.
+//
+// Computes C = A B^T for up to three independent problems per launch, where B
+// is a weight stored out-major ([n][k], the layout every projection of the
+// layer uses: y = x W^T). Both operands are therefore contiguous along the
+// reduction axis and load straight into MFMA fragments without a transpose.
+//
+// Work split: a 256-thread workgroup computes a 128 x 128 tile of C; each of
+// its four waves owns a 64 x 64 quarter as 2 x 2 blocks of 32 x 32 MFMA
+// output. The reduction runs in k-tiles of 128 bytes per row (64 bf16 or 32
+// fp32 values), double-buffered in LDS with 16 bytes of padding per row so
+// that the fragment reads of 32 rows hit distinct banks. Global loads of the
+// next k-tile are issued before the MFMAs of the current one.
+//
+// Tiles are numbered so that tiles sharing rows of A are consecutive, and the
+// workgroup index is remapped so that consecutive tiles land on the same XCD
+// (workgroups are dealt round-robin over the 8 XCDs, each with its own L2).
+#include "txl_device.hpp"
+#include "txl_internal.hpp"
+
+namespace txl {
+
+namespace {
+
+constexpr int kBM = 128, kBN = 128, kThreads = 256;
+constexpr int kRowBytes = 128;                       // bytes per row of one k-tile
+constexpr int kPitch = kRowBytes + 16;               // LDS bytes per row
+constexpr int kChunks = kBM * (kRowBytes / 16) / kThreads;   // 16-byte chunks per thread per operand (4)
+
+struct GemmSmem {
+    char a[2][kBM * kPitch];
+    char b[2][kBN * kPitch];
+};
+static_assert(sizeof(GemmSmem) >= 128 * 129 * 4, "C tile staging must fit in the operand buffers");
+
+// Fast floor(x / d) for 0 <= x < 2^22 with a float reciprocal and one fix-up.
+__device__ __forceinline__ int fdiv(int x, int d, float inv) {
+    int q = (int)((float)x * inv);
+    int r = x - q * d;
+    if (r < 0) q -= 1;
+    else if (r >= d) q += 1;
+    return q;
+}
+
+template <typename T>
+__device__ __forceinline__ const char *a_row_ptr(const GemmProblem &P, int row, float inv_seg) {
+    if (row >= P.rows) return nullptr;
+    int b = fdiv(row, P.seg_rows, inv_seg);
+    int t = row - b * P.seg_rows;
+    if (P.a_mode == A_CONTEXT) {
+        if (t < P.mem_len) {
+            int pr = P.ring_head + t;
+            if (pr >= P.ring_M) pr -= P.ring_M;
+            return (const char *)P.ring + ((long long)b * P.ring_bstride + (long long)pr * P.a_ld) * (long long)sizeof(T);
+        }
+        t -= P.mem_len;
+    }
+    if (t >= P.valid_rows) return nullptr;
+    return (const char *)P.a + ((long long)b * P.a_bstride + (long long)t * P.a_ld) * (long long)sizeof(T);
+}
+
+template <typename T>
+__device__ __forceinline__ const char *b_row_ptr(const GemmProblem &P, int n) {
+    if (n >= P.cols) return nullptr;
+    const void *w = P.b0;
+    if (n >= P.b_split) { n -= P.b_split; w = P.b1; }
+    int wrow = n;
+    if (P.b_mode == B_HEADS) {
+        int hh = n / P.dhp, c = n - hh * P.dhp;
+        if (c >= P.dh) return nullptr;
+        wrow = hh * P.dh + c;
+    }
+    return (const char *)w + (long long)wrow * P.b_ld * (long long)sizeof(T);
+}
+
+// Load one 16-byte chunk (elements [k, k + 16/sizeof(T))) of a row, zero past kdim.
+template <typename T, bool VEC>
+__device__ __forceinline__ u32x4 load_chunk(const char *row, int k, int kdim) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    if (!row) return z;
+    if (VEC) {
+        if (k < kdim) z = *reinterpret_cast<const u32x4 *>(row + (long long)k * sizeof(T));
+    } else {
+        constexpr int per = 4 / sizeof(T);   // elements per dword
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            int kk = k + q * per;
+            if (kk < kdim) z[q] = *reinterpret_cast<const uint32_t *>(row + (long long)kk * sizeof(T));
+        }
+    }
+    return z;
+}
+
+constexpr int kCPitch = 129;   // floats per row of the staged C tile
+
+// Write the 128 x 128 C tile staged in LDS (cs) to its destination. Threads
+// walk the tile along the destination's contiguous axis: columns for
+// row-major outputs, rows for the transposed value output.
+template <typename T>
+__device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, int m0, int n0, int tid,
+                                         float inv_seg) {
+    const bool trans = P.epi == EPI_KV && n0 >= P.b_split;
+    if (!trans) {
+        const int nl = tid & 127;
+        const int n = n0 + nl;
+        if (n >= P.cols) return;
+        // per-column constants
+        float bias = 0.f, uu = 0.f, vv = 0.f;
+        int hh = 0, c = 0;
+        bool second = false;
+        if (P.epi == EPI_ROWS) {
+            if (P.bias) bias = to_f32(((const T *)P.bias)[n]);
+        } else {
+            int nn = n;
+            if (P.epi == EPI_KV && n >= P.b_split) { nn = n - P.b_split; second = true; }
+            hh = nn / P.dhp;
+            c = nn - hh * P.dhp;
+            if (P.epi == EPI_QUV && c < P.dh) {
+                uu = to_f32(((const T *)P.u)[hh * P.dh + c]);
+                vv = to_f32(((const T *)P.v)[hh * P.dh + c]);
+            }
+        }
+        for (int rl = tid >> 7; rl < 128; rl += 2) {
+            const int row = m0 + rl;
+            if (row >= P.rows) break;
+            const float x = cs[rl * kCPitch + nl];
+            const int b = fdiv(row, P.seg_rows, inv_seg);
+            const int t = row - b * P.seg_rows;
+            if (P.epi == EPI_ROWS) {
+                float y = x + bias;
+                if (P.relu) y = fmaxf(y, 0.f);
+                if (P.res) y += to_f32(((const T *)P.res)[(long long)b * P.res_bstride + (long long)t * P.res_ld + n]);
+                const long long idx = (long long)b * P.c_bstride + (long long)t * P.c_ld + n;
+                if (P.out_f32) ((float *)P.c0)[idx] = y;
+                else ((T *)P.c0)[idx] = from_f32<T>(y);
+            } else {
+                const long long bh = (long long)b * P.heads + hh;
+                if (P.epi == EPI_QUV) {
+                    const long long idx = (bh * P.seg_rows + t) * P.dhp + c;
+                    ((T *)P.c0)[idx] = from_f32<T>((x + uu) * P.qscale);
+                    ((T *)P.c1)[idx] = from_f32<T>((x + vv) * P.qscale);
+                } else if (second) {
+                    ((T *)P.c1)[(bh * P.dhp + c) * P.seg_rows + t] = from_f32<T>(x);
+                } else {
+                    ((T *)P.c0)[(bh * P.seg_rows + t) * P.dhp + c] = from_f32<T>(x);
+                }
+            }
+        }
+    } else {
+        const int rl = tid & 127;
+        const int row = m0 + rl;
+        if (row >= P.rows) return;
+        const int b = fdiv(row, P.seg_rows, inv_seg);
+        const int t = row - b * P.seg_rows;
+        for (int nl = tid >> 7; nl < 128; nl += 2) {
+            const int n = n0 + nl;
+            if (n >= P.cols) break;
+            const int nn = n - P.b_split;
+            const int hh = nn / P.dhp, c = nn - hh * P.dhp;
+            const long long bh = (long long)b * P.heads + hh;
+            ((T *)P.c1)[(bh * P.dhp + c) * P.seg_rows + t] = from_f32<T>(cs[rl * kCPitch + nl]);
+        }
+    }
+}
+
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
+    __shared__ GemmSmem sm;
+    // XCD-aware remap: deal consecutive tiles to the same XCD.
+    const int total = g.total_tiles;
+    const int gid = blockIdx.x;
+    const int full = total - (total & 7);
+    const int tile = gid < full ? (gid & 7) * (full >> 3) + (gid >> 3) : gid;
+    // select the problem with uniform branches (a dynamic index into the
+    // kernel-argument struct would copy it to private memory)
+    GemmProblem P;
+    if (g.count > 2 && tile >= g.p[2].tile_begin) P = g.p[2];
+    else if (g.count > 1 && tile >= g.p[1].tile_begin) P = g.p[1];
+    else P = g.p[0];
+    const int lt = tile - P.tile_begin;
+    const int tm = lt / P.tiles_n, tn = lt - tm * P.tiles_n;
+    const int m0 = tm * kBM, n0 = tn * kBN;
+    const float inv_seg = 1.0f / (float)P.seg_rows;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    constexpr int EPC = 16 / sizeof(T);          // elements per 16-byte chunk
+    constexpr int BK = kRowBytes / sizeof(T);    // elements per k-tile
+
+    // Rows and chunk column this thread stages: rows tid/8 + 32c, chunk tid%8.
+    const int ccol = tid & 7;
+    const char *arow[kChunks], *brow[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        arow[c] = a_row_ptr<T>(P, m0 + (tid >> 3) + 32 * c, inv_seg);
+        brow[c] = b_row_ptr<T>(P, n0 + (tid >> 3) + 32 * c);
+    }
+    const int nk = (P.kdim + BK - 1) / BK;
+
+    u32x4 ra[kChunks], rb[kChunks];
+#define TXL_GLOAD(kt_)                                                    \
+    do {                                                                  \
+        const int k_ = (kt_) * BK + ccol * EPC;                           \
+        _Pragma("unroll") for (int c = 0; c < kChunks; ++c) {             \
+            ra[c] = load_chunk<T, VEC>(arow[c], k_, P.kdim);              \
+            rb[c] = load_chunk<T, VEC>(brow[c], k_, P.kdim);              \
+        }                                                                 \
+    } while (0)
+#define TXL_SSTORE(buf_)                                                  \
+    do {                                                                  \
+        _Pragma("unroll") for (int c = 0; c < kChunks; ++c) {             \
+            const int r_ = (tid >> 3) + 32 * c;                           \
+            *reinterpret_cast<u32x4 *>(&sm.a[buf_][r_ * kPitch + ccol * 16]) = ra[c]; \
+            *reinterpret_cast<u32x4 *>(&sm.b[buf_][r_ * kPitch + ccol * 16]) = rb[c]; \
+        }                                                                 \
+    } while (0)
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+
+    TXL_GLOAD(0);
+    TXL_SSTORE(0);
+    __syncthreads();
+    const int fr = lane & 31, fh = lane >> 5;
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) TXL_GLOAD(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            Frag<T> fa[2], fb[2];
+            const int koff = (ks * 16 + fh * 8) * (int)sizeof(T);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                load8(fa[i], reinterpret_cast<const T *>(&sm.a[buf][(wm * 64 + i * 32 + fr) * kPitch + koff]));
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                load8(fb[j], reinterpret_cast<const T *>(&sm.b[buf][(wn * 64 + j * 32 + fr) * kPitch + koff]));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) mma16(acc[i][j], fa[i], fb[j]);
+        }
+        if (kt + 1 < nk) TXL_SSTORE(buf ^ 1);
+        __syncthreads();
+    }
+
+    // stage the C tile in LDS (the k-loop ended with a barrier), then write it out
+    float *cs = reinterpret_cast<float *>(&sm);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                cs[(wm * 64 + i * 32 + crow(r, lane)) * kCPitch + wn * 64 + j * 32 + fr] = acc[i][j][r];
+    __syncthreads();
+    epilogue<T>(P, cs, m0, n0, tid, inv_seg);
+#undef TXL_GLOAD
+#undef TXL_SSTORE
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+bool gemm_vec_ok(bool is_bf16, const GemmProblem &p) {
+    const long long es = is_bf16 ? 2 : 4;
+    const long long epc = 16 / es;
+    if (p.kdim % epc) return false;
+    if ((p.a_ld * es) % 16 || (p.a_bstride * es) % 16 || !aligned16(p.a)) return false;
+    if (p.a_mode == A_CONTEXT && (!aligned16(p.ring) || (p.ring_bstride * es) % 16)) return false;
+    if ((p.b_ld * es) % 16 || !aligned16(p.b0) || (p.b1 && !aligned16(p.b1))) return false;
+    return true;
+}
+
+hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s) {
+    if (g.total_tiles <= 0) return hipSuccess;
+    bool vec = true;
+    for (int i = 0; i < g.count; ++i) vec = vec && gemm_vec_ok(is_bf16, g.p[i]);
+    dim3 grid(g.total_tiles), block(kThreads);
+    if (is_bf16) {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<bf16, true>), grid, block, 0, s, g);
+        else hipLaunchKernelGGL((gemm_kernel<bf16, false>), grid, block, 0, s, g);
+    } else {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<float, true>), grid, block, 0, s, g);
+        else hipLaunchKernelGGL((gemm_kernel<float, false>), grid, block, 0, s, g);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace txl

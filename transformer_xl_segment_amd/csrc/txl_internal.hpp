@@ -1,0 +1,107 @@
+// txl_internal.hpp -- launchers behind the C ABI and the descriptors they take.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace txl {
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM: C = A B^T with B out-major [n][k] (a weight), up to 3
+// independent problems in one launch. Rows of A and C are addressed as
+// (batch b, row t) with t < seg_rows; columns of C may live in a padded
+// per-head space (head hh, column c < dhp; columns c >= dh of every head are
+// exact zeros because the matching weight rows read as zero).
+// ---------------------------------------------------------------------------
+enum ARowMode {
+    A_ROWS = 0,      // row (b, t): t < valid_rows -> a + b*a_bstride + t*a_ld, else zero
+    A_CONTEXT = 1,   // row (b, j): j < mem_len -> ring row (head + j) % ring_M of batch b,
+                     //             j < mem_len + valid_rows -> a row j - mem_len, else zero
+};
+enum BColMode {
+    B_ROWS = 0,      // column n < cols reads weight row n
+    B_HEADS = 1,     // column n -> (hh, c) = (n / dhp, n % dhp); c < dh -> weight row hh*dh + c
+};
+enum EpiMode {
+    EPI_ROWS = 0,    // dst = c0 + b*c_bstride + t*c_ld + n (+bias[n], relu, +residual), T or fp32
+    EPI_QUV = 1,     // c0 = (acc + u) * qscale, c1 = (acc + v) * qscale, head-major [b][hh][t][c]
+    EPI_KV = 2,      // n < b_split: c0 head-major [b][hh][t][c]; else c1 transposed [b][hh][c][t]
+    EPI_HEADS = 3,   // c0 head-major [b][hh][t][c]
+};
+
+struct GemmProblem {
+    int rows, cols, kdim;        // C is rows x cols; reduction over kdim
+    int tiles_n, tile_begin, tile_count;
+    int seg_rows;                // rows per batch entry (row = b*seg_rows + t)
+    int valid_rows;              // rows per batch entry that hold data (A side)
+    // A operand
+    int a_mode;
+    const void *a;
+    long long a_ld, a_bstride;
+    const void *ring;
+    long long ring_bstride;      // elements between batch entries of the ring (M*ld)
+    int ring_M, ring_head, mem_len;
+    // B operand
+    int b_mode;
+    const void *b0, *b1;
+    int b_split;                 // columns >= b_split read b1 at column n - b_split
+    long long b_ld;
+    int dh, dhp, heads;
+    // epilogue
+    int epi;
+    void *c0, *c1;
+    long long c_ld, c_bstride;
+    const void *bias;
+    const void *res;
+    long long res_ld, res_bstride;
+    const void *u, *v;
+    float qscale;
+    int relu, out_f32;
+};
+
+struct GemmLaunch {
+    GemmProblem p[3];
+    int count;
+    int total_tiles;
+};
+
+// Returns a hipError_t from the launch.
+hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s);
+
+// Is every operand row of the problem 16-byte aligned (vectorised loads)?
+bool gemm_vec_ok(bool is_bf16, const GemmProblem &p);
+
+// ---------------------------------------------------------------------------
+// Relative attention over projected, head-major operands.
+//   qu, qv  [B][H][Wp][dp]  (q + u) and (q + v), pre-scaled by log2(e)/sqrt(dh)
+//   ke      [B][H][Kp][dp]  content keys
+//   vt      [B][H][dp][Kp]  values, transposed
+//   rk      [H][Kp][dp]     distance keys for distances 0..Kp-1
+//   o       [B][W][D]       output rows (heads concatenated), batch stride o_bstride
+// Rows past W (queries) and K (keys) hold zeros.
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+    const void *qu, *qv, *ke, *vt, *rk;
+    void *o;
+    long long o_bstride;
+    int B, H, W, Wp, m, K, Kp, dh, dp, D;
+};
+hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s);
+bool rel_attn_supported(int dh);
+int attn_dp(int dh);          // padded head width used by the attention kernel
+const int ATTN_QBLOCK = 128;  // queries per workgroup
+const int ATTN_KBLOCK = 64;   // keys per step
+
+// ---------------------------------------------------------------------------
+// Small kernels.
+// ---------------------------------------------------------------------------
+// dst ring rows (pos0 + t) % M of every batch entry <- src rows (src_row0 + t), t < n
+hipError_t launch_ring_write(bool is_bf16, void *ring, int M, int D, int pos0, const void *src,
+                             long long src_bstride, int src_row0, int n, int B, hipStream_t s);
+// y[b][t] = LN(x[b][t]) with fp32 input, T output (batch stride y_bstride)
+hipError_t launch_layer_norm(bool is_bf16, const float *x, const void *g, const void *b, void *y,
+                             long long y_bstride, int B, int W, int D, hipStream_t s);
+hipError_t launch_sinusoid(bool is_bf16, void *R, int R_len, int D, hipStream_t s);
+
+}  // namespace txl

@@ -1,0 +1,134 @@
+// txl_misc.hip -- memory ring update, LayerNorm and the distance table.
+//
+// These are bandwidth kernels: every byte is read once and written once, with
+// consecutive lanes on consecutive addresses (16-byte accesses where the
+// operands allow) so each wave moves whole cache lines.
+#include <math.h>
+
+#include "txl_device.hpp"
+#include "txl_internal.hpp"
+
+namespace txl {
+
+namespace {
+
+// Memory update (segment-recurrence simulator: mem = last M rows of [mem; h]).
+// One workgroup row-strip per (batch, row); 16-byte or 4-byte words per lane.
+template <bool VEC>
+__global__ void ring_write_kernel(char *ring, int M, long long row_bytes, int pos0, const char *src,
+                                  long long src_bstride_bytes, int src_row0, int n, int B) {
+    const int r = blockIdx.x;            // r = b * n + t
+    const int b = r / n, t = r - b * n;
+    int pr = pos0 + t;
+    if (pr >= M) pr -= M;
+    char *dst = ring + ((long long)b * M + pr) * row_bytes;
+    const char *s = src + (long long)b * src_bstride_bytes + (long long)(src_row0 + t) * row_bytes;
+    if (VEC) {
+        for (long long o = threadIdx.x * 16LL; o < row_bytes; o += blockDim.x * 16LL)
+            *reinterpret_cast<u32x4 *>(dst + o) = *reinterpret_cast<const u32x4 *>(s + o);
+    } else {
+        for (long long o = threadIdx.x * 4LL; o < row_bytes; o += blockDim.x * 4LL)
+            *reinterpret_cast<uint32_t *>(dst + o) = *reinterpret_cast<const uint32_t *>(s + o);
+    }
+}
+
+// LayerNorm of the NumPy layer on "Implementing Transformer-XL":
+// gamma * (x - mean) / (std + 1e-6) + beta with the population std. One wave
+// per row; statistics in fp32 from an fp32 input row.
+template <typename T>
+__global__ void layer_norm_kernel(const float *x, const T *g, const T *bt, T *y, long long y_bstride,
+                                  int rows, int W, int D) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const float *xr = x + (long long)row * D;
+    constexpr int MAXE = 16;                 // D <= 1024
+    float v[MAXE];
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        const int c = lane + 64 * e;
+        v[e] = c < D ? xr[c] : 0.f;
+        s += v[e];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    const float mean = s / (float)D;
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        const int c = lane + 64 * e;
+        const float d = c < D ? v[e] - mean : 0.f;
+        q += d * d;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) q += __shfl_xor(q, off);
+    const float inv = 1.f / (sqrtf(q / (float)D) + 1e-6f);
+    const int b = row / W, t = row - b * W;
+    T *yr = y + (long long)b * y_bstride + (long long)t * D;
+#pragma unroll
+    for (int e = 0; e < MAXE; ++e) {
+        const int c = lane + 64 * e;
+        if (c < D) yr[c] = from_f32<T>(to_f32(g[c]) * (v[e] - mean) * inv + to_f32(bt[c]));
+    }
+}
+
+// Distance table: R[d][k] = sin(d w_k), R[d][D/2 + k] = cos(d w_k),
+// w_k = 10000^(-2k/D), evaluated in double precision.
+template <typename T>
+__global__ void sinusoid_kernel(T *R, int R_len, int D) {
+    const int half = D / 2;
+    const long long n = (long long)R_len * half;
+    for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
+         idx += (long long)gridDim.x * blockDim.x) {
+        const int d = (int)(idx / half), k = (int)(idx - (long long)d * half);
+        const double w = pow(10000.0, -2.0 * (double)k / (double)D);
+        const double a = (double)d * w;
+        R[(long long)d * D + k] = from_f32<T>((float)sin(a));
+        R[(long long)d * D + half + k] = from_f32<T>((float)cos(a));
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ring_write(bool is_bf16, void *ring, int M, int D, int pos0, const void *src,
+                             long long src_bstride, int src_row0, int n, int B, hipStream_t s) {
+    if (n <= 0 || B <= 0) return hipSuccess;
+    const long long es = is_bf16 ? 2 : 4;
+    const long long row_bytes = D * es;
+    const bool vec = (row_bytes % 16 == 0) && (((uintptr_t)ring | (uintptr_t)src) % 16 == 0) &&
+                     ((src_bstride * es) % 16 == 0);
+    dim3 grid(B * n), block(row_bytes >= 2048 ? 128 : 64);
+    if (vec)
+        hipLaunchKernelGGL(ring_write_kernel<true>, grid, block, 0, s, (char *)ring, M, row_bytes, pos0,
+                           (const char *)src, src_bstride * es, src_row0, n, B);
+    else
+        hipLaunchKernelGGL(ring_write_kernel<false>, grid, block, 0, s, (char *)ring, M, row_bytes, pos0,
+                           (const char *)src, src_bstride * es, src_row0, n, B);
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_norm(bool is_bf16, const float *x, const void *g, const void *b, void *y,
+                             long long y_bstride, int B, int W, int D, hipStream_t s) {
+    const int rows = B * W;
+    dim3 grid((rows + 3) / 4), block(256);
+    if (is_bf16)
+        hipLaunchKernelGGL(layer_norm_kernel<bf16>, grid, block, 0, s, x, (const bf16 *)g, (const bf16 *)b,
+                           (bf16 *)y, y_bstride, rows, W, D);
+    else
+        hipLaunchKernelGGL(layer_norm_kernel<float>, grid, block, 0, s, x, (const float *)g,
+                           (const float *)b, (float *)y, y_bstride, rows, W, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_sinusoid(bool is_bf16, void *R, int R_len, int D, hipStream_t s) {
+    const long long n = (long long)R_len * (D / 2);
+    if (n <= 0) return hipSuccess;
+    int blocks = (int)((n + 255) / 256);
+    if (blocks > 4096) blocks = 4096;
+    if (is_bf16) hipLaunchKernelGGL(sinusoid_kernel<bf16>, dim3(blocks), dim3(256), 0, s, (bf16 *)R, R_len, D);
+    else hipLaunchKernelGGL(sinusoid_kernel<float>, dim3(blocks), dim3(256), 0, s, (float *)R, R_len, D);
+    return hipGetLastError();
+}
+
+}  // namespace txl
