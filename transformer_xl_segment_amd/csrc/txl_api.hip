@@ -73,7 +73,7 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
     L.qv = take(q_bytes);
     L.ke = take(k_bytes);
     L.vt = take(k_bytes);
-    L.rk = take((size_t)H * L.Kp * L.dp * es);
+    L.rk = take((size_t)H * (L.Kp + 2 * ATTN_RPAD) * L.dp * es);
     L.o = take((size_t)B * W * D * es);
     if (op == TXL_OP_LAYER || op == TXL_OP_STACK) {
         L.z = take((size_t)B * W * D * 4);
@@ -212,8 +212,8 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     kv.epi = EPI_KV; kv.c0 = ws + L.ke; kv.c1 = ws + L.vt;
     // r = R[0:K] WkR^T, shared by the batch
     GemmProblem &r = g.p[2];
-    r.rows = Kp; r.cols = H * dp; r.kdim = D;
-    r.seg_rows = Kp; r.valid_rows = K;
+    r.rows = Kp + 2 * ATTN_RPAD; r.cols = H * dp; r.kdim = D;
+    r.seg_rows = Kp + 2 * ATTN_RPAD; r.valid_rows = K; r.a_first = ATTN_RPAD;
     r.a_mode = A_ROWS; r.a = R; r.a_ld = D; r.a_bstride = 0;
     r.b_mode = B_HEADS; r.b0 = p->WkR; r.b_split = r.cols; r.b_ld = D;
     r.dh = dh; r.dhp = dp; r.heads = H;

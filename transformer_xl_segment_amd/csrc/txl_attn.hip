@@ -23,17 +23,23 @@
 // explainer's step 5 says, never per pair. The shift of that step becomes index
 // arithmetic in LDS: each wave writes its chunk (plus the first 32 distances of
 // the previous chunk, kept in registers) into a per-query row at position
-// 95 - e_rel, where e_rel = a - b + 63 is the distance's offset in the band; then
-// the value for key b sits at position 32 - a + b, which a lane reads with a
-// per-lane base and a compile-time offset per register. Those values seed the
-// accumulators of the content-term MFMAs, so the two terms add for free.
+// e_rel, the distance's offset in the band (four accumulator registers per
+// aligned 16-byte store); the value for key b of query a sits at position
+// a - b + 63, which a lane reads with a per-lane base and a compile-time offset
+// per register. Those values seed the accumulators of the content-term MFMAs,
+// so the two terms add for free.
 //
-// The row pitch of that buffer (100 floats) keeps both the 16-byte writes of
-// 16 consecutive lanes and the 4-byte skewed reads of 32 lanes on distinct
-// banks. K and V^T tiles are staged in LDS with 16 bytes of row padding.
+// The row pitch of that buffer (100 floats) keeps both the 16-byte writes and
+// the 4-byte skewed reads on distinct banks. K and V^T tiles are staged in LDS
+// with row padding chosen for their 16- and 8-byte fragment reads. The row sum
+// of the probabilities is taken with packed bf16 dot products over the very
+// values the P.V product consumes.
+//
 // Softmax uses a lazy maximum: the running maximum only moves (and the output
 // accumulators are only rescaled) when a block's maximum exceeds it by more
 // than 8 in log2 units, which keeps every exp2 below 2^8.
+#include <type_traits>
+
 #include "txl_device.hpp"
 #include "txl_internal.hpp"
 
@@ -45,13 +51,15 @@ constexpr int kWaves = 4;
 constexpr int kQB = 128;          // queries per workgroup (32 per wave)
 constexpr int kKB = 64;           // keys per block
 constexpr int kGPitch = 100;      // floats per query row of the distance buffer
-constexpr int kGX = kKB + 31;     // position of band offset 0
 
 template <typename T, int DP>
 struct AttnSmem {
     static constexpr int NO = (DP + 31) / 32;                  // 32-row blocks of O^T
     static constexpr int kPitchK = DP * (int)sizeof(T) + 16;   // bytes per key row
-    static constexpr int kPitchV = kKB * (int)sizeof(T) + 16;  // bytes per value row (V^T)
+    // bytes per value row (V^T): bf16 rows are read 8 bytes per lane, so an
+    // 8-byte pad (34 dwords) spreads 32 lanes over distinct bank pairs; fp32
+    // rows are read 16 bytes per lane and take a 16-byte pad
+    static constexpr int kPitchV = kKB * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
     float g[kWaves][32 * kGPitch];
     char k[kKB * kPitchK];
     char v[NO * 32 * kPitchV];
@@ -84,18 +92,34 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Write the 16 values of one 32-distance block of G (register i holds band
-// offset e0 + crow(i)) at positions X - e for every band offset e.
-__device__ __forceinline__ void write_gblock(float *grow, const f32x16 &g, int x_minus_e0, int hf) {
+// Write one 32-distance block of G to the wave's distance buffer: register i of
+// lane (a, hf) holds band offset e0 + crow(i), stored at position e0 + crow(i)
+// of row a, so each group of four registers is one aligned 16-byte store.
+__device__ __forceinline__ void write_gblock(float *grow, const f32x16 &g, int e0, int hf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int pos = x_minus_e0 - 8 * q - 4 * hf - 3;   // lowest position of the group
-        *reinterpret_cast<f32x4 *>(grow + pos) = f32x4{g[4 * q + 3], g[4 * q + 2], g[4 * q + 1], g[4 * q]};
-    }
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4 *>(grow + e0 + 8 * q + 4 * hf) = f32x4{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
 }
 
+// Row sum of eight probabilities already packed as the bf16 B operand.
+__device__ __forceinline__ float psum(const Frag<bf16> &f, float acc) {
+    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f.v[2 * q], f.v[2 * q + 1]}, one, acc, false);
+    return acc;
+}
+__device__ __forceinline__ float psum(const Frag<float> &f, float acc) {
+    return acc + ((f.lo[0] + f.lo[1]) + (f.lo[2] + f.lo[3])) + ((f.hi[0] + f.hi[1]) + (f.hi[2] + f.hi[3]));
+}
+
+// bf16: two workgroups per CU when their LDS fits in the CU's 160 KB (two
+// waves per SIMD hide each other's latency). fp32 operands double the fragment
+// registers, so fp32 runs one workgroup per CU with the full register file.
 template <typename T, int DP>
-__global__ void __launch_bounds__(256, 2) rel_attn_kernel(const AttnArgs A) {
+constexpr int attn_wgs_per_cu() { return sizeof(T) == 2 && 2 * sizeof(AttnSmem<T, DP>) <= 160 * 1024 ? 2 : 1; }
+
+template <typename T, int DP>
+__global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kernel(const AttnArgs A) {
     typedef AttnSmem<T, DP> SM;
     constexpr int NS = DP / 16;
     constexpr int NO = SM::NO;
@@ -122,7 +146,8 @@ __global__ void __launch_bounds__(256, 2) rel_attn_kernel(const AttnArgs A) {
     const T *qv = (const T *)A.qv + ((long long)bh * A.Wp) * DP;
     const T *ke = (const T *)A.ke + ((long long)bh * A.Kp) * DP;
     const T *vt = (const T *)A.vt + ((long long)bh * DP) * A.Kp;
-    const T *rk = (const T *)A.rk + ((long long)h * A.Kp) * DP;
+    // row 0 of rk = distance 0; ATTN_RPAD zero rows on either side
+    const T *rk = (const T *)A.rk + ((long long)h * (A.Kp + 2 * ATTN_RPAD) + ATTN_RPAD) * DP;
 
     // zero the V^T rows past DP once (they pad the last 32-row block of O^T)
     for (int idx = tid; idx < (NO * 32 - DP) * (SM::kPitchV / 4); idx += 256)
@@ -138,9 +163,22 @@ __global__ void __launch_bounds__(256, 2) rel_attn_kernel(const AttnArgs A) {
         }
     }
 
-    auto r_frag = [&](Frag<T> &f, int delta, int s) {
-        if (delta >= 0 && delta < A.Kp) load8(f, rk + (long long)delta * DP + 16 * s + 8 * hf);
-        else zero8(f);
+    // r fragments of one 64-distance chunk: distances d0 + 32*bb + fr.
+    // Every distance a wave touches lies in [-ATTN_RPAD, Kp + ATTN_RPAD).
+    auto r_chunk = [&](Frag<T> (&f)[2][NS], int d0) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                load8(f[bb][s], rk + (long long)(d0 + 32 * bb + fr) * DP + 16 * s + 8 * hf);
+    };
+    auto g_chunk = [&](f32x16 (&g)[2], const Frag<T> (&f)[2][NS]) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+            g[bb] = zero16();
+#pragma unroll
+            for (int s = 0; s < NS; ++s) mma16(g[bb], f[bb][s], fqv[s]);
+        }
     };
 
     float *grow = sm.g[w] + fr * kGPitch;
@@ -149,17 +187,28 @@ __global__ void __launch_bounds__(256, 2) rel_attn_kernel(const AttnArgs A) {
     for (int o = 0; o < NO; ++o) oacc[o] = zero16();
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Distances [c0 + 1, c0 + 32] with c0 = m + iw: the part of the band below
-    // the first key block that no chunk of the loop covers.
-    f32x16 gprev = zero16();
+    // Band of key block kb: distances cw-63 .. cw+31 with cw = m + iw - 64*kb.
+    // gb[kb & 1] holds the chunk cw-63 .. cw (two 32-distance blocks); the band's
+    // top part cw+1 .. cw+31 is block 0 of the previous chunk, gb[(kb+1) & 1][0],
+    // or for kb = 0 the block gtop computed here (written to LDS before the
+    // loop). rnext holds r of the next chunk.
+    // The two chunk buffers alternate with the parity of kb (the loop is unrolled
+    // by two), so no register tile is copied from one step to the next.
+    f32x16 gtop = zero16(), gb[2][2];
+    Frag<T> rnext[2][NS];
     if (wave_has_queries) {
-        const int d0 = m + iw + 1 + fr;
+        const int c0 = m + iw;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            Frag<T> fr_;
-            r_frag(fr_, d0, s);
-            mma16(gprev, fr_, fqv[s]);
+            Frag<T> f;
+            load8(f, rk + (long long)(c0 + 1 + fr) * DP + 16 * s + 8 * hf);
+            mma16(gtop, f, fqv[s]);
         }
+        r_chunk(rnext, c0 - 63);
+        g_chunk(gb[0], rnext);
+        r_chunk(rnext, c0 - 127);
+        // the band top of block 0 goes to LDS once; later blocks rewrite it
+        write_gblock(grow, gtop, 64, hf);
     }
 
     // cooperative K / V^T staging
@@ -169,81 +218,69 @@ __global__ void __launch_bounds__(256, 2) rel_attn_kernel(const AttnArgs A) {
     constexpr int KCPR = DP * (int)sizeof(T) / 16;         // chunks per key row
     constexpr int VCPR = kKB * (int)sizeof(T) / 16;        // chunks per V^T row
     u32x4 rkt[KPT], rvt[VPT];
-    auto gload = [&](int kb) {
-        const int j0 = kb * kKB;
-#pragma unroll
-        for (int c = 0; c < KPT; ++c) {
-            const int idx = tid + 256 * c;
-            if (idx < KCH) {
-                const int r = idx / KCPR, q = idx - r * KCPR;
-                rkt[c] = *reinterpret_cast<const u32x4 *>((const char *)(ke + (long long)(j0 + r) * DP) + q * 16);
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < VPT; ++c) {
-            const int idx = tid + 256 * c;
-            if (idx < VCH) {
-                const int r = idx / VCPR, q = idx - r * VCPR;
-                rvt[c] = *reinterpret_cast<const u32x4 *>((const char *)(vt + (long long)r * A.Kp + j0) + q * 16);
-            }
-        }
-    };
-    auto sstore = [&]() {
-#pragma unroll
-        for (int c = 0; c < KPT; ++c) {
-            const int idx = tid + 256 * c;
-            if (idx < KCH) {
-                const int r = idx / KCPR, q = idx - r * KCPR;
-                *reinterpret_cast<u32x4 *>(sm.k + r * SM::kPitchK + q * 16) = rkt[c];
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < VPT; ++c) {
-            const int idx = tid + 256 * c;
-            if (idx < VCH) {
-                const int r = idx / VCPR, q = idx - r * VCPR;
-                *reinterpret_cast<u32x4 *>(sm.v + r * SM::kPitchV + q * 16) = rvt[c];
-            }
-        }
-    };
+#define TXL_KV_GLOAD(kb_)                                                                          \
+    do {                                                                                           \
+        const int j0_ = (kb_) * kKB;                                                               \
+        _Pragma("unroll") for (int c = 0; c < KPT; ++c) {                                          \
+            const int idx = tid + 256 * c;                                                         \
+            if (KCH % 256 == 0 || idx < KCH) {                                                     \
+                const int r_ = idx / KCPR, q_ = idx - r_ * KCPR;                                   \
+                rkt[c] = *reinterpret_cast<const u32x4 *>((const char *)(ke + (long long)(j0_ + r_) * DP) + q_ * 16); \
+            }                                                                                      \
+        }                                                                                          \
+        _Pragma("unroll") for (int c = 0; c < VPT; ++c) {                                          \
+            const int idx = tid + 256 * c;                                                         \
+            if (VCH % 256 == 0 || idx < VCH) {                                                     \
+                const int r_ = idx / VCPR, q_ = idx - r_ * VCPR;                                   \
+                rvt[c] = *reinterpret_cast<const u32x4 *>((const char *)(vt + (long long)r_ * A.Kp + j0_) + q_ * 16); \
+            }                                                                                      \
+        }                                                                                          \
+    } while (0)
+#define TXL_KV_SSTORE()                                                                            \
+    do {                                                                                           \
+        _Pragma("unroll") for (int c = 0; c < KPT; ++c) {                                          \
+            const int idx = tid + 256 * c;                                                         \
+            if (KCH % 256 == 0 || idx < KCH) {                                                     \
+                const int r_ = idx / KCPR, q_ = idx - r_ * KCPR;                                   \
+                *reinterpret_cast<u32x4 *>(sm.k + r_ * SM::kPitchK + q_ * 16) = rkt[c];             \
+            }                                                                                      \
+        }                                                                                          \
+        _Pragma("unroll") for (int c = 0; c < VPT; ++c) {                                          \
+            const int idx = tid + 256 * c;                                                         \
+            if (VCH % 256 == 0 || idx < VCH) {                                                     \
+                const int r_ = idx / VCPR, q_ = idx - r_ * VCPR;                                   \
+                u32x2 *dv_ = reinterpret_cast<u32x2 *>(sm.v + r_ * SM::kPitchV + q_ * 16);          \
+                dv_[0] = u32x2{rvt[c][0], rvt[c][1]};                                              \
+                dv_[1] = u32x2{rvt[c][2], rvt[c][3]};                                              \
+            }                                                                                      \
+        }                                                                                          \
+    } while (0)
 
-    gload(0);
-    for (int kb = 0; kb < nkb; ++kb) {
+    // One key block; P is the parity of kb (compile time), so gb[P] / gb[Q] are
+    // fixed register tiles.
+    auto step = [&](auto parity, int kb) {
+        constexpr int P = decltype(parity)::value, Q = 1 - P;
         __syncthreads();
-        sstore();
+        TXL_KV_SSTORE();
         __syncthreads();
-        if (kb + 1 < nkb) gload(kb + 1);
+        if (kb + 1 < nkb) TXL_KV_GLOAD(kb + 1);
         const int j0 = kb * kKB;
-        if (!wave_has_queries || j0 > last_key_wave) continue;
+        if (!wave_has_queries || j0 > last_key_wave) return;
 
-        // ---- new distance chunk: band offsets 0..63 = distances cw-63 .. cw
-        const int cw = m + iw - j0;
-        f32x16 gcur[2];
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-            gcur[bb] = zero16();
-            const int d = cw - 63 + 32 * bb + fr;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                Frag<T> f;
-                r_frag(f, d, s);
-                mma16(gcur[bb], f, fqv[s]);
-            }
-        }
-        // ---- shift into place through LDS
-        write_gblock(grow, gcur[0], kGX - 0, hf);
-        write_gblock(grow, gcur[1], kGX - 32, hf);
-        write_gblock(grow, gprev, kGX - 64, hf);
+        // ---- shift the distance term into place through LDS
+        write_gblock(grow, gb[P][0], 0, hf);
+        write_gblock(grow, gb[P][1], 32, hf);
+        if (P == 1 || kb > 0) write_gblock(grow, gb[Q][0], 64, hf);
         wave_lds_sync();
+        // key b = 32*sb + crow(i) of query a needs band offset a - b + 63
         f32x16 sacc[2];
         {
-            const float *rb = grow + 32 - fr + 4 * hf;
+            const float *rb = grow + fr - 4 * hf;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[sb][i] = rb[32 * sb + 8 * (i >> 2) + (i & 3)];
+                for (int i = 0; i < 16; ++i) sacc[sb][i] = rb[63 - 32 * sb - 8 * (i >> 2) - (i & 3)];
         }
-        gprev = gcur[0];
         // ---- content term on top: S^T += K (q+u)^T
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -262,7 +299,7 @@ __global__ void __launch_bounds__(256, 2) rel_attn_kernel(const AttnArgs A) {
                 for (int i = 0; i < 16; ++i)
                     if (32 * sb + crow(i, lane) > lim) sacc[sb][i] = -INFINITY;
         }
-        // ---- online softmax (log2 domain)
+        // ---- online softmax (log2 domain): maximum and lazy rescale
         float mx = sacc[0][0];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
@@ -270,7 +307,7 @@ __global__ void __launch_bounds__(256, 2) rel_attn_kernel(const AttnArgs A) {
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[sb][i]);
         mx = fmaxf(mx, swap_half(mx));
         const float m_new = fmaxf(m_run, mx);
-        if (__builtin_amdgcn_read_exec() && __any(m_new > m_run + 8.f)) {
+        if (__any(m_new > m_run + 8.f)) {
             const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
             for (int o = 0; o < NO; ++o)
@@ -279,29 +316,42 @@ __global__ void __launch_bounds__(256, 2) rel_attn_kernel(const AttnArgs A) {
             l_run *= alpha;
             m_run = m_new;
         }
-        float lsum = 0.f;
+        // ---- next distance chunk (MFMA) interleaved with exp / pack / row sum (VALU)
+        g_chunk(gb[Q], rnext);
+        // prefetch for block kb+2 only while that block is still visible to the
+        // wave; this keeps every distance read >= -94 (inside the zero padding)
+        if (j0 + 2 * kKB <= last_key_wave) r_chunk(rnext, m + iw - j0 - kKB - 127);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(sacc[sb][i] - m_run);
-                sacc[sb][i] = p;
-                lsum += p;
-            }
+            for (int i = 0; i < 16; ++i) sacc[sb][i] = __builtin_amdgcn_exp2f(sacc[sb][i] - m_run);
+        Frag<T> fp4[4];
+        float lsum = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            p_frag(fp4[p], sacc[p >> 1], 8 * (p & 1));
+            lsum = psum(fp4[p], lsum);       // sums exactly the values P.V uses
+        }
         l_run += lsum;
         // ---- O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            Frag<T> fp;
-            p_frag(fp, sacc[p >> 1], 8 * (p & 1));
 #pragma unroll
             for (int o = 0; o < NO; ++o) {
                 Frag<T> fv;
                 load_vt(fv, sm.v + (32 * o + fr) * SM::kPitchV, 16 * p + 4 * hf);
-                mma16(oacc[o], fv, fp);
+                mma16(oacc[o], fv, fp4[p]);
             }
         }
+    };
+
+    TXL_KV_GLOAD(0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        step(std::integral_constant<int, 0>(), kb);
+        if (kb + 1 < nkb) step(std::integral_constant<int, 1>(), kb + 1);
     }
+#undef TXL_KV_GLOAD
+#undef TXL_KV_SSTORE
 
     if (!wave_has_queries) return;
     const float l_tot = l_run + swap_half(l_run);

@@ -31,7 +31,7 @@ struct GemmSmem {
     char a[2][kBM * kPitch];
     char b[2][kBN * kPitch];
 };
-static_assert(sizeof(GemmSmem) >= 128 * 129 * 4, "C tile staging must fit in the operand buffers");
+static_assert(sizeof(GemmSmem) >= 128 * 132 * 4, "C tile staging must fit in the operand buffers");
 
 // Fast floor(x / d) for 0 <= x < 2^22 with a float reciprocal and one fix-up.
 __device__ __forceinline__ int fdiv(int x, int d, float inv) {
@@ -55,7 +55,8 @@ __device__ __forceinline__ const char *a_row_ptr(const GemmProblem &P, int row, 
         }
         t -= P.mem_len;
     }
-    if (t >= P.valid_rows) return nullptr;
+    t -= P.a_first;
+    if (t < 0 || t >= P.valid_rows) return nullptr;
     return (const char *)P.a + ((long long)b * P.a_bstride + (long long)t * P.a_ld) * (long long)sizeof(T);
 }
 
@@ -91,74 +92,157 @@ __device__ __forceinline__ u32x4 load_chunk(const char *row, int k, int kdim) {
     return z;
 }
 
-constexpr int kCPitch = 129;   // floats per row of the staged C tile
+constexpr int kCPitch = 132;   // floats per row of the staged C tile (16-byte aligned rows)
 
-// Write the 128 x 128 C tile staged in LDS (cs) to its destination. Threads
-// walk the tile along the destination's contiguous axis: columns for
-// row-major outputs, rows for the transposed value output.
-template <typename T>
+// Eight consecutive output elements as one store (16 bytes for bf16, 32 for fp32).
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> { bf16x8 v; };
+template <> struct Vec8<float> { f32x4 lo, hi; };
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void store8(T *dst, const float (&x)[8]) {
+    if (VEC) {
+        if constexpr (sizeof(T) == 2) {
+            bf16x8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = (bf16)x[i];
+            *reinterpret_cast<bf16x8 *>(dst) = v;
+        } else {
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+            *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[i] = from_f32<T>(x[i]);
+    }
+}
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void load8f(float (&x)[8], const T *src) {
+    if (VEC && sizeof(T) == 2) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8 *>(src);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = to_f32(((const T *)&v)[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = to_f32(src[i]);
+    }
+}
+
+// Write the 128 x 128 C tile staged in LDS (cs). Row-major destinations: a
+// thread owns eight consecutive columns and walks every 32nd row of the tile
+// (rows advance incrementally, no division). The transposed value output: a
+// wave covers 64 consecutive columns of one 8-row group, each lane writing
+// eight consecutive rows of its column as one store.
+template <typename T, bool VEC>
 __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, int m0, int n0, int tid,
                                          float inv_seg) {
     const bool trans = P.epi == EPI_KV && n0 >= P.b_split;
     if (!trans) {
-        const int nl = tid & 127;
-        const int n = n0 + nl;
+        const int cg = tid & 15;                       // column group: columns n0 + 8*cg .. +7
+        const int n = n0 + 8 * cg;
         if (n >= P.cols) return;
-        // per-column constants
-        float bias = 0.f, uu = 0.f, vv = 0.f;
+        const bool full = n + 8 <= P.cols;
+        float bias[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float uu[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float vv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         int hh = 0, c = 0;
         bool second = false;
         if (P.epi == EPI_ROWS) {
-            if (P.bias) bias = to_f32(((const T *)P.bias)[n]);
+            if (P.bias)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bias[i] = n + i < P.cols ? to_f32(((const T *)P.bias)[n + i]) : 0.f;
         } else {
             int nn = n;
             if (P.epi == EPI_KV && n >= P.b_split) { nn = n - P.b_split; second = true; }
-            hh = nn / P.dhp;
+            hh = nn / P.dhp;                           // the 8 columns share one head (dhp % 16 == 0)
             c = nn - hh * P.dhp;
-            if (P.epi == EPI_QUV && c < P.dh) {
-                uu = to_f32(((const T *)P.u)[hh * P.dh + c]);
-                vv = to_f32(((const T *)P.v)[hh * P.dh + c]);
-            }
+            if (P.epi == EPI_QUV)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (c + i < P.dh) {
+                        uu[i] = to_f32(((const T *)P.u)[hh * P.dh + c + i]);
+                        vv[i] = to_f32(((const T *)P.v)[hh * P.dh + c + i]);
+                    }
         }
-        for (int rl = tid >> 7; rl < 128; rl += 2) {
-            const int row = m0 + rl;
+        int rl = tid >> 4;                              // 0..15, then +16 per iteration
+        int row = m0 + rl;
+        int b = fdiv(row, P.seg_rows, inv_seg);
+        int t = row - b * P.seg_rows;
+        for (; rl < 128; rl += 16) {
             if (row >= P.rows) break;
-            const float x = cs[rl * kCPitch + nl];
-            const int b = fdiv(row, P.seg_rows, inv_seg);
-            const int t = row - b * P.seg_rows;
+            float x[8];
+            const f32x4 lo = *reinterpret_cast<const f32x4 *>(cs + rl * kCPitch + 8 * cg);
+            const f32x4 hi = *reinterpret_cast<const f32x4 *>(cs + rl * kCPitch + 8 * cg + 4);
+            x[0] = lo[0]; x[1] = lo[1]; x[2] = lo[2]; x[3] = lo[3];
+            x[4] = hi[0]; x[5] = hi[1]; x[6] = hi[2]; x[7] = hi[3];
             if (P.epi == EPI_ROWS) {
-                float y = x + bias;
-                if (P.relu) y = fmaxf(y, 0.f);
-                if (P.res) y += to_f32(((const T *)P.res)[(long long)b * P.res_bstride + (long long)t * P.res_ld + n]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    x[i] += bias[i];
+                    if (P.relu) x[i] = fmaxf(x[i], 0.f);
+                }
+                const long long ridx = (long long)b * P.res_bstride + (long long)t * P.res_ld + n;
                 const long long idx = (long long)b * P.c_bstride + (long long)t * P.c_ld + n;
-                if (P.out_f32) ((float *)P.c0)[idx] = y;
-                else ((T *)P.c0)[idx] = from_f32<T>(y);
+                if (full) {
+                    if (P.res) {
+                        float r[8];
+                        load8f<T, VEC>(r, (const T *)P.res + ridx);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) x[i] += r[i];
+                    }
+                    if (P.out_f32) store8<float, VEC>((float *)P.c0 + idx, x);
+                    else store8<T, VEC>((T *)P.c0 + idx, x);
+                } else {
+                    for (int i = 0; i < 8 && n + i < P.cols; ++i) {
+                        float y = x[i];
+                        if (P.res) y += to_f32(((const T *)P.res)[ridx + i]);
+                        if (P.out_f32) ((float *)P.c0)[idx + i] = y;
+                        else ((T *)P.c0)[idx + i] = from_f32<T>(y);
+                    }
+                }
             } else {
                 const long long bh = (long long)b * P.heads + hh;
                 if (P.epi == EPI_QUV) {
                     const long long idx = (bh * P.seg_rows + t) * P.dhp + c;
-                    ((T *)P.c0)[idx] = from_f32<T>((x + uu) * P.qscale);
-                    ((T *)P.c1)[idx] = from_f32<T>((x + vv) * P.qscale);
+                    float xu[8], xv[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        xu[i] = (x[i] + uu[i]) * P.qscale;
+                        xv[i] = (x[i] + vv[i]) * P.qscale;
+                    }
+                    store8<T, true>((T *)P.c0 + idx, xu);
+                    store8<T, true>((T *)P.c1 + idx, xv);
                 } else if (second) {
-                    ((T *)P.c1)[(bh * P.dhp + c) * P.seg_rows + t] = from_f32<T>(x);
+                    // a tile that straddles the K_E / V split writes its V columns here
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        ((T *)P.c1)[(bh * P.dhp + c + i) * P.seg_rows + t] = from_f32<T>(x[i]);
                 } else {
-                    ((T *)P.c0)[(bh * P.seg_rows + t) * P.dhp + c] = from_f32<T>(x);
+                    store8<T, true>((T *)P.c0 + (bh * P.seg_rows + t) * P.dhp + c, x);
                 }
             }
+            row += 16;
+            t += 16;
+            while (t >= P.seg_rows) { t -= P.seg_rows; ++b; }
         }
     } else {
-        const int rl = tid & 127;
-        const int row = m0 + rl;
-        if (row >= P.rows) return;
-        const int b = fdiv(row, P.seg_rows, inv_seg);
-        const int t = row - b * P.seg_rows;
-        for (int nl = tid >> 7; nl < 128; nl += 2) {
+        // V^T [b][hh][c][t]: rows of the tile are consecutive t (seg_rows % 8 == 0)
+        const int lane = tid & 63, wv = tid >> 6;
+        for (int task = wv; task < 32; task += 4) {      // task = (row group rg, column half ch)
+            const int rg = task >> 1, ch = task & 1;
+            const int nl = 64 * ch + lane;
             const int n = n0 + nl;
-            if (n >= P.cols) break;
+            const int row = m0 + 8 * rg;
+            if (n >= P.cols || row >= P.rows) continue;
+            const int b = fdiv(row, P.seg_rows, inv_seg);
+            const int t = row - b * P.seg_rows;
             const int nn = n - P.b_split;
             const int hh = nn / P.dhp, c = nn - hh * P.dhp;
-            const long long bh = (long long)b * P.heads + hh;
-            ((T *)P.c1)[(bh * P.dhp + c) * P.seg_rows + t] = from_f32<T>(cs[rl * kCPitch + nl]);
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = cs[(8 * rg + i) * kCPitch + nl];
+            store8<T, true>((T *)P.c1 + (((long long)b * P.heads + hh) * P.dhp + c) * P.seg_rows + t, x);
         }
     }
 }
@@ -258,7 +342,7 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
             for (int r = 0; r < 16; ++r)
                 cs[(wm * 64 + i * 32 + crow(r, lane)) * kCPitch + wn * 64 + j * 32 + fr] = acc[i][j][r];
     __syncthreads();
-    epilogue<T>(P, cs, m0, n0, tid, inv_seg);
+    epilogue<T, VEC>(P, cs, m0, n0, tid, inv_seg);
 #undef TXL_GLOAD
 #undef TXL_SSTORE
 }
@@ -274,6 +358,12 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p) {
     if ((p.a_ld * es) % 16 || (p.a_bstride * es) % 16 || !aligned16(p.a)) return false;
     if (p.a_mode == A_CONTEXT && (!aligned16(p.ring) || (p.ring_bstride * es) % 16)) return false;
     if ((p.b_ld * es) % 16 || !aligned16(p.b0) || (p.b1 && !aligned16(p.b1))) return false;
+    if (p.epi == EPI_ROWS) {
+        // eight-column vector stores of the output (and loads of the residual)
+        const long long oes = p.out_f32 ? 4 : es;
+        if (!aligned16(p.c0) || (p.c_ld * oes) % 16 || (p.c_bstride * oes) % 16) return false;
+        if (p.res && (!aligned16(p.res) || (p.res_ld * es) % 16 || (p.res_bstride * es) % 16)) return false;
+    }
     return true;
 }
 

@@ -15,7 +15,8 @@ namespace txl {
 // exact zeros because the matching weight rows read as zero).
 // ---------------------------------------------------------------------------
 enum ARowMode {
-    A_ROWS = 0,      // row (b, t): t < valid_rows -> a + b*a_bstride + t*a_ld, else zero
+    A_ROWS = 0,      // row (b, t): a_first <= t < a_first + valid_rows -> a + b*a_bstride + (t - a_first)*a_ld,
+                     //             else zero
     A_CONTEXT = 1,   // row (b, j): j < mem_len -> ring row (head + j) % ring_M of batch b,
                      //             j < mem_len + valid_rows -> a row j - mem_len, else zero
 };
@@ -35,6 +36,7 @@ struct GemmProblem {
     int tiles_n, tile_begin, tile_count;
     int seg_rows;                // rows per batch entry (row = b*seg_rows + t)
     int valid_rows;              // rows per batch entry that hold data (A side)
+    int a_first;                 // A_ROWS: first output row that holds data
     // A operand
     int a_mode;
     const void *a;
@@ -77,7 +79,9 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p);
 //   qu, qv  [B][H][Wp][dp]  (q + u) and (q + v), pre-scaled by log2(e)/sqrt(dh)
 //   ke      [B][H][Kp][dp]  content keys
 //   vt      [B][H][dp][Kp]  values, transposed
-//   rk      [H][Kp][dp]     distance keys for distances 0..Kp-1
+//   rk      [H][ATTN_RPAD + Kp + ATTN_RPAD][dp]  distance keys; row ATTN_RPAD + d holds
+//           distance d for 0 <= d < K and zeros elsewhere, so reads of distances in
+//           [-ATTN_RPAD, Kp + ATTN_RPAD) need no bounds checks
 //   o       [B][W][D]       output rows (heads concatenated), batch stride o_bstride
 // Rows past W (queries) and K (keys) hold zeros.
 // ---------------------------------------------------------------------------
@@ -92,6 +96,7 @@ bool rel_attn_supported(int dh);
 int attn_dp(int dh);          // padded head width used by the attention kernel
 const int ATTN_QBLOCK = 128;  // queries per workgroup
 const int ATTN_KBLOCK = 64;   // keys per step
+const int ATTN_RPAD = 128;    // zero rows before and after the distance keys
 
 // ---------------------------------------------------------------------------
 // Small kernels.
