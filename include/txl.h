@@ -164,10 +164,10 @@ txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, i
 
 /* Event timing of the relative-attention kernel. Between txl_profile_begin and
  * txl_profile_end, every attention-kernel launch (from any entry point, on its
- * own stream) is bracketed by a pair of HIP events, up to max_launches
- * launches. txl_profile_end waits for those events and returns the summed
- * kernel time in milliseconds and the number of timed launches. Not
- * thread-safe; meant for benchmarks. */
+ * own stream) gets a pair of HIP events stamped by the kernel's own dispatch
+ * at its start and end, up to max_launches launches. txl_profile_end waits for
+ * those events and returns the summed kernel time in milliseconds and the
+ * number of timed launches. Not thread-safe; meant for benchmarks. */
 txl_status txl_profile_begin(int max_launches);
 txl_status txl_profile_end(double *total_ms, int *launches);
 

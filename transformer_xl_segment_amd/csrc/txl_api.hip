@@ -98,19 +98,11 @@ struct Profiler {
 } g_prof;
 
 hipError_t attn_launch(bool bf16, const AttnArgs &a, hipStream_t s) {
-    const bool timed = g_prof.on && g_prof.used < (int)g_prof.start.size();
-    if (timed) {
-        hipError_t e = hipEventRecord(g_prof.start[g_prof.used], s);
-        if (e != hipSuccess) return e;
+    if (g_prof.on && g_prof.used < (int)g_prof.start.size()) {
+        const int i = g_prof.used++;
+        return launch_rel_attn(bf16, a, s, g_prof.start[i], g_prof.stop[i]);
     }
-    hipError_t e = launch_rel_attn(bf16, a, s);
-    if (e != hipSuccess) return e;
-    if (timed) {
-        e = hipEventRecord(g_prof.stop[g_prof.used], s);
-        if (e != hipSuccess) return e;
-        ++g_prof.used;
-    }
-    return hipSuccess;
+    return launch_rel_attn(bf16, a, s);
 }
 
 // ---------------------------------------------------------------------------

@@ -38,6 +38,8 @@
 // Softmax uses a lazy maximum: the running maximum only moves (and the output
 // accumulators are only rescaled) when a block's maximum exceeds it by more
 // than 8 in log2 units, which keeps every exp2 below 2^8.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "txl_device.hpp"
@@ -368,21 +370,23 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
         }
 }
 
+// start/stop (may be null) are stamped by the kernel's own dispatch, so they
+// bracket exactly this kernel on its stream.
 template <typename T, int DP>
-hipError_t launch_dp(const AttnArgs &a, hipStream_t s) {
+hipError_t launch_dp(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const int nqb = (a.W + kQB - 1) / kQB;
     dim3 grid(a.B * a.H * nqb), block(256);
-    hipLaunchKernelGGL((rel_attn_kernel<T, DP>), grid, block, 0, s, a);
+    hipExtLaunchKernelGGL((rel_attn_kernel<T, DP>), grid, block, 0, s, start, stop, 0, a);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
+hipError_t launch_t(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     switch (a.dp) {
-        case 16: return launch_dp<T, 16>(a, s);
-        case 32: return launch_dp<T, 32>(a, s);
-        case 48: return launch_dp<T, 48>(a, s);
-        case 64: return launch_dp<T, 64>(a, s);
+        case 16: return launch_dp<T, 16>(a, s, start, stop);
+        case 32: return launch_dp<T, 32>(a, s, start, stop);
+        case 48: return launch_dp<T, 48>(a, s, start, stop);
+        case 64: return launch_dp<T, 64>(a, s, start, stop);
         default: return hipErrorInvalidValue;
     }
 }
@@ -392,8 +396,8 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 int attn_dp(int dh) { return (dh + 15) / 16 * 16; }
 bool rel_attn_supported(int dh) { return dh >= 1 && dh <= 64; }
 
-hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s) {
-    return is_bf16 ? launch_t<bf16>(a, s) : launch_t<float>(a, s);
+hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    return is_bf16 ? launch_t<bf16>(a, s, start, stop) : launch_t<float>(a, s, start, stop);
 }
 
 }  // namespace txl

@@ -91,7 +91,9 @@ struct AttnArgs {
     long long o_bstride;
     int B, H, W, Wp, m, K, Kp, dh, dp, D;
 };
-hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s);
+// start / stop: optional events stamped at this kernel's own start and end.
+hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s, hipEvent_t start = nullptr,
+                           hipEvent_t stop = nullptr);
 bool rel_attn_supported(int dh);
 int attn_dp(int dh);          // padded head width used by the attention kernel
 const int ATTN_QBLOCK = 128;  // queries per workgroup
