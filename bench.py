@@ -11,6 +11,8 @@ already resident in HBM when the timed region starts.
 Prints ONE JSON line with the whole-job throughput (tokens/s), the attention
 kernel's roofline position (its own launches timed with HIP events inside the
 timed region) and the CPU oracle timed on a bounded sample of the same work.
+A second timed region runs the same segments with the memory kept as projected
+keys and values (txl_rel_attn_fwd_cached), reported under "kv_cache".
 """
 from __future__ import annotations
 
@@ -60,6 +62,31 @@ def traffic_for(kernel_src: str, path: str):
     if rec.get("kernel_sha256") != digest:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, steps, warmup):
+    """The same segment stream through txl_rel_attn_fwd_cached: the memory is
+    held as projected keys and values, so each segment projects W rows, not M + W."""
+    bf = torch.bfloat16
+    cache = tb.KVCache.empty(B, M, W, D, H, bf, out.device)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN_CACHED, bf, B, W, M, D, H), dtype=torch.uint8,
+                     device=out.device)
+
+    def step(k):
+        tb.rel_attn_fwd_cached(segs[k % len(segs)], cache, params, R, H, out=out, workspace=ws)
+
+    for k in range(max(warmup, 1) + (M + W - 1) // W):
+        step(k)
+    torch.cuda.synchronize()
+    assert cache.len == M
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return {"value": B * W * steps / elapsed, "unit": "tokens/s", "ms_per_step": elapsed * 1e3 / steps,
+            "step": "txl_rel_attn_fwd_cached, one steady segment (m = M)",
+            "cache_bytes": 2 * B * M * D * 2}
 
 
 def cpu_baseline(prob, R64, H):
@@ -175,6 +202,9 @@ def main():
         "attn_tokens_per_s": B * W / a_avg_s,
         "step_tflops": (a_flops + proj_flops(B, W, m, D)) / (ms_per_step * 1e-3) / 1e12,
     }
+    kv = time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, args.steps, args.warmup)
+    kv["speedup_vs_row_memory"] = kv["value"] / rec["value"]
+    rec["kv_cache"] = kv
     if not args.no_cpu_baseline:
         from oracle import oracle as orc
         R64 = orc.sinusoid_table(M + W, D)

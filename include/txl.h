@@ -70,7 +70,8 @@ typedef enum { TXL_FP32 = 0, TXL_BF16 = 1 } txl_dtype;
 typedef enum {
     TXL_OP_REL_ATTN = 0,      /* txl_rel_attn_fwd */
     TXL_OP_LAYER = 1,         /* txl_layer_fwd */
-    TXL_OP_STACK = 2          /* txl_stack_fwd_segments */
+    TXL_OP_STACK = 2,         /* txl_stack_fwd_segments */
+    TXL_OP_REL_ATTN_CACHED = 3 /* txl_rel_attn_fwd_cached */
 } txl_op;
 
 /* One layer's parameters, all device pointers of the call's dtype.
@@ -101,8 +102,34 @@ typedef struct {
     int head;
 } txl_mem;
 
+/* Projected key/value cache of one attention layer: the memory kept as the
+ * keys k = x WkE^T and values val = x Wv^T of its rows instead of the rows x
+ * themselves, so a segment projects only its own W rows ("Transformer-XL,
+ * explained.", closing assessment: computed keys and values are cached rather
+ * than recomputed; Ultralytics glossary, comparison with related models, the
+ * key/value cache). A ring of C slots per (batch row, head), head-major:
+ *   k   device [B][H][C][dp]   keys, dp = D/H rounded up to a multiple of 16
+ *   vt  device [B][H][dp][C]   values transposed (one row per head column)
+ * Slot s of (b, hh) is k[b][hh][s][:] and vt[b][hh][:][s]; padding columns
+ * (dh <= c < dp) hold zeros.
+ *   M     memory length in rows, a positive multiple of 8;
+ *   C     slots, txl_kv_cache_capacity(M, W) for the largest W used;
+ *   len   cached rows (0 = empty), a multiple of 8, len <= M;
+ *   head  slot of the oldest cached row, a multiple of 8, head < C.
+ * Both buffers belong to the caller and must be zero-filled before first use
+ * (slots outside the window are read for masked keys and must be finite).
+ * The calls below advance len and head on the host. */
+typedef struct {
+    void *k;
+    void *vt;
+    int C;
+    int M;
+    int len;
+    int head;
+} txl_kv_cache;
+
 /* Workspace bytes that `op` needs for these sizes (M = memory capacity; F is
- * ignored for TXL_OP_REL_ATTN). Returns 0 for invalid sizes. The same value
+ * ignored for TXL_OP_REL_ATTN and TXL_OP_REL_ATTN_CACHED). Returns 0 for invalid sizes. The same value
  * serves every call of that op with sizes no larger than these. */
 size_t txl_workspace_bytes(txl_op op, txl_dtype dtype, int B, int W, int M, int D, int H, int F);
 
@@ -161,6 +188,31 @@ txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, i
                                   txl_mem *mems, const txl_layer_params *params,
                                   const void *R, int R_len, void *y,
                                   void *ws, size_t ws_bytes, void *stream);
+
+/* Slots a key/value cache needs for memory length M and segments of up to W
+ * rows: M + W rounded up to a multiple of 64. Returns 0 for M < 0 or W < 1. */
+int txl_kv_cache_capacity(int M, int W);
+
+/* Projects rows x [B][n][D] (batch stride x_bstride) with WkE and Wv and
+ * appends the last min(n, M) of them to the cache, dropping the oldest rows
+ * beyond M (filling a cache from known rows, e.g. a warm start). Reads p->WkE
+ * and p->Wv; min(n, M) must be a multiple of 8. No workspace. */
+txl_status txl_kv_cache_append(txl_dtype dtype, int B, int D, int H, txl_kv_cache *cache,
+                               const txl_layer_params *p, const void *x, long long x_bstride, int n,
+                               void *stream);
+
+/* txl_rel_attn_fwd over a key/value cache instead of a row memory: projects
+ * the W segment rows into the cache, attends over the cached rows followed by
+ * the segment (keys and values of the cached rows are reused, not recomputed),
+ * applies Wo, then advances the cache window by W rows as txl_mem_update does.
+ * The result equals txl_rel_attn_fwd followed by txl_mem_update on a row memory
+ * that holds the same rows, bit for bit. W must be a multiple of 8 and
+ * cache->C >= cache->M + W. Workspace: txl_workspace_bytes(TXL_OP_REL_ATTN_CACHED, ...). */
+txl_status txl_rel_attn_fwd_cached(txl_dtype dtype, int B, int W, int D, int H,
+                                   const void *h, long long h_bstride, txl_kv_cache *cache,
+                                   const txl_layer_params *p, const void *R, int R_len,
+                                   void *out, long long out_bstride,
+                                   void *ws, size_t ws_bytes, void *stream);
 
 /* Event timing of the relative-attention kernel. Between txl_profile_begin and
  * txl_profile_end, every attention-kernel launch (from any entry point, on its

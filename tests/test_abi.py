@@ -125,6 +125,56 @@ def test_layer_and_stack_reject_bad_arguments():
                                     FAKE, None, 0, None) == tb.TXL_ERR_WORKSPACE
 
 
+def test_kv_cache_capacity_and_workspace():
+    L = tb.lib()
+    assert L.txl_kv_cache_capacity(512, 512) == 1024
+    assert L.txl_kv_cache_capacity(1600, 128) == 1728
+    assert L.txl_kv_cache_capacity(8, 8) == 64
+    assert L.txl_kv_cache_capacity(0, 64) == 64
+    assert L.txl_kv_cache_capacity(-1, 64) == 0 and L.txl_kv_cache_capacity(8, 0) == 0
+    ws = L.txl_workspace_bytes
+    c = ws(tb.OP_REL_ATTN_CACHED, tb.TXL_BF16, 16, 512, 512, 512, 8, 0)
+    # no context keys and values in the workspace: they live in the cache
+    assert 0 < c < ws(tb.OP_REL_ATTN, tb.TXL_BF16, 16, 512, 512, 512, 8, 0)
+
+
+def _cache(M=8, C=64, len_=0, head=0, k=FAKE, vt=FAKE):
+    return tb._KV(k, vt, C, M, len_, head)
+
+
+def _cached(c, dt=tb.TXL_FP32, B=1, W=8, D=16, H=2, R_len=16, wsb=0):
+    L = tb.lib()
+    p = _params()
+    return L.txl_rel_attn_fwd_cached(dt, B, W, D, H, FAKE, W * D, ctypes.byref(c) if c else None,
+                                     ctypes.byref(p), FAKE, R_len, FAKE, W * D, None, wsb, None)
+
+
+def test_kv_cache_calls_reject_bad_arguments():
+    assert _cached(None) == tb.TXL_ERR_ARG
+    assert _cached(_cache(M=12)) == tb.TXL_ERR_UNSUPPORTED          # M % 8
+    assert _cached(_cache(), W=4, R_len=8) == tb.TXL_ERR_UNSUPPORTED  # W % 8
+    assert _cached(_cache(C=60)) == tb.TXL_ERR_ARG                   # C % 64
+    assert _cached(_cache(M=64, C=64)) == tb.TXL_ERR_ARG             # C < M + W
+    assert _cached(_cache(len_=16)) == tb.TXL_ERR_ARG                # len > M
+    assert _cached(_cache(len_=4)) == tb.TXL_ERR_ARG                 # len % 8
+    assert _cached(_cache(head=64)) == tb.TXL_ERR_ARG                # head >= C
+    assert _cached(_cache(head=4)) == tb.TXL_ERR_ARG                 # head % 8
+    assert _cached(_cache(k=None)) == tb.TXL_ERR_ARG
+    assert _cached(_cache(vt=FAKE + 8)) == tb.TXL_ERR_ARG            # 16-byte alignment
+    c = _cache(len_=8, head=56)
+    assert _cached(c, R_len=15) == tb.TXL_ERR_ARG                    # R_len < len + W
+    assert _cached(c, R_len=16) == tb.TXL_ERR_WORKSPACE
+    assert (c.len, c.head) == (8, 56)                                # untouched on failure
+    L = tb.lib()
+    p = _params()
+    app = lambda c, n, xs=128: L.txl_kv_cache_append(tb.TXL_FP32, 1, 16, 2, ctypes.byref(c),
+                                                     ctypes.byref(p), FAKE, xs, n, None)
+    assert app(_cache(), 0) == tb.TXL_ERR_ARG
+    assert app(_cache(), 4, xs=64) == tb.TXL_ERR_UNSUPPORTED         # n % 8
+    assert app(_cache(), 8, xs=63) == tb.TXL_ERR_ARG                 # x batch stride
+    assert app(_cache(M=16, C=16), 8) == tb.TXL_ERR_ARG              # C % 64
+
+
 def test_sinusoid_and_profiler_reject_bad_arguments():
     L = tb.lib()
     assert L.txl_sinusoid_table(tb.TXL_FP32, 8, 15, FAKE, None) == tb.TXL_ERR_ARG

@@ -23,7 +23,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "txl.h")
 
 TXL_OK, TXL_ERR_ARG, TXL_ERR_UNSUPPORTED, TXL_ERR_WORKSPACE, TXL_ERR_HIP = range(5)
 TXL_FP32, TXL_BF16 = 0, 1
-OP_REL_ATTN, OP_LAYER, OP_STACK = 0, 1, 2
+OP_REL_ATTN, OP_LAYER, OP_STACK, OP_REL_ATTN_CACHED = 0, 1, 2, 3
 
 _PARAM_FIELDS = ("Wq", "WkE", "WkR", "Wv", "Wo", "u", "v", "ln1_g", "ln1_b", "W1", "b1",
                  "W2", "b2", "ln2_g", "ln2_b")
@@ -42,6 +42,11 @@ class _Params(ctypes.Structure):
 class _Mem(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("M", ctypes.c_int), ("len", ctypes.c_int),
                 ("head", ctypes.c_int)]
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("vt", ctypes.c_void_p), ("C", ctypes.c_int),
+                ("M", ctypes.c_int), ("len", ctypes.c_int), ("head", ctypes.c_int)]
 
 
 _lib = None
@@ -64,10 +69,15 @@ def lib() -> ctypes.CDLL:
         L.txl_mem_update.argtypes = [i, i, i, Mp, vp, ll, i, vp]
         L.txl_layer_fwd.argtypes = [i, i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_stack_fwd_segments.argtypes = [i, i, i, i, i, i, i, i, vp, Mp, P, vp, i, vp, vp, sz, vp]
+        KVp = ctypes.POINTER(_KV)
+        L.txl_kv_cache_capacity.argtypes = [i, i]
+        L.txl_kv_cache_append.argtypes = [i, i, i, i, KVp, P, vp, ll, i, vp]
+        L.txl_rel_attn_fwd_cached.argtypes = [i, i, i, i, i, vp, ll, KVp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_profile_begin.argtypes = [i]
         L.txl_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_mem_update", "txl_layer_fwd",
-                  "txl_stack_fwd_segments", "txl_profile_begin", "txl_profile_end"):
+                  "txl_stack_fwd_segments", "txl_kv_cache_capacity", "txl_kv_cache_append",
+                  "txl_rel_attn_fwd_cached", "txl_profile_begin", "txl_profile_end"):
             getattr(L, f).restype = i
         L.txl_status_string.argtypes = [i]
         L.txl_status_string.restype = ctypes.c_char_p
@@ -133,6 +143,48 @@ class MemoryRing:
         return self.data[:, idx]
 
 
+def head_pad(dh: int) -> int:
+    """Padded head width of the head-major projected layouts (dh rounded up to 16)."""
+    return (dh + 15) // 16 * 16
+
+
+def kv_cache_capacity(M: int, W: int) -> int:
+    return int(lib().txl_kv_cache_capacity(M, W))
+
+
+@dataclass
+class KVCache:
+    """Projected key/value cache of one layer: k [B, H, C, dp], vt [B, H, dp, C] plus
+    (M, len, head); key j of the window lives in slot (head + j) % C."""
+    k: torch.Tensor
+    vt: torch.Tensor
+    M: int
+    len: int = 0
+    head: int = 0
+
+    @classmethod
+    def empty(cls, B: int, M: int, W: int, D: int, H: int, dtype: torch.dtype, device) -> "KVCache":
+        C = kv_cache_capacity(M, W)
+        dp = head_pad(D // H)
+        return cls(torch.zeros(B, H, C, dp, dtype=dtype, device=device),
+                   torch.zeros(B, H, dp, C, dtype=dtype, device=device), M)
+
+    @property
+    def C(self) -> int:
+        return self.k.shape[2]
+
+    def _struct(self) -> _KV:
+        return _KV(self.k.data_ptr(), self.vt.data_ptr(), self.C, self.M, self.len, self.head)
+
+    def _update_from(self, s: _KV) -> None:
+        self.len, self.head = int(s.len), int(s.head)
+
+    def logical(self, dh: int):
+        """Cached keys and values in logical order: ([B, H, len, dh], [B, H, len, dh])."""
+        idx = (torch.arange(self.len, device=self.k.device) + self.head) % self.C
+        return self.k[:, :, idx, :dh], self.vt[:, :, :dh, idx].transpose(2, 3)
+
+
 class LayerParams:
     """One layer's parameter tensors (device, one dtype), by the names of txl.h."""
 
@@ -182,6 +234,35 @@ def rel_attn_fwd(h: torch.Tensor, mem: Optional[MemoryRing], params: LayerParams
                                   R.data_ptr(), R.shape[0], out.data_ptr(), os_, ws.data_ptr(),
                                   ws.numel() * ws.element_size(), _stream(h.device)),
            "txl_rel_attn_fwd")
+    return out
+
+
+def kv_cache_append(cache: KVCache, params: LayerParams, x: torch.Tensor, H: int) -> None:
+    B, n, D = x.shape
+    xs = _rows_view(x, "x")
+    cs, ps = cache._struct(), params._struct()
+    _check(lib().txl_kv_cache_append(dtype_code(x.dtype), B, D, H, ctypes.byref(cs), ctypes.byref(ps),
+                                     x.data_ptr(), xs, n, _stream(x.device)), "txl_kv_cache_append")
+    cache._update_from(cs)
+
+
+def rel_attn_fwd_cached(h: torch.Tensor, cache: KVCache, params: LayerParams, R: torch.Tensor,
+                        H: int, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    B, W, D = h.shape
+    hs = _rows_view(h, "h")
+    if out is None:
+        out = torch.empty(B, W, D, dtype=h.dtype, device=h.device)
+    os_ = _rows_view(out, "out")
+    nbytes = workspace_bytes(OP_REL_ATTN_CACHED, h.dtype, B, W, cache.M, D, H)
+    ws = _workspace(nbytes, h.device, workspace)
+    cs, ps = cache._struct(), params._struct()
+    _check(lib().txl_rel_attn_fwd_cached(dtype_code(h.dtype), B, W, D, H, h.data_ptr(), hs,
+                                         ctypes.byref(cs), ctypes.byref(ps), R.data_ptr(), R.shape[0],
+                                         out.data_ptr(), os_, ws.data_ptr(),
+                                         ws.numel() * ws.element_size(), _stream(h.device)),
+           "txl_rel_attn_fwd_cached")
+    cache._update_from(cs)
     return out
 
 

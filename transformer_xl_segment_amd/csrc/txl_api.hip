@@ -71,8 +71,10 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
     const size_t k_bytes = (size_t)B * H * L.Kp * L.dp * es;
     L.qu = take(q_bytes);
     L.qv = take(q_bytes);
-    L.ke = take(k_bytes);
-    L.vt = take(k_bytes);
+    if (op != TXL_OP_REL_ATTN_CACHED) {
+        L.ke = take(k_bytes);
+        L.vt = take(k_bytes);
+    }
     L.rk = take((size_t)H * (L.Kp + 2 * ATTN_RPAD) * L.dp * es);
     L.o = take((size_t)B * W * D * es);
     if (op == TXL_OP_LAYER || op == TXL_OP_STACK) {
@@ -129,6 +131,30 @@ txl_status check_mem(const txl_mem *mem, int W) {
     return TXL_OK;
 }
 
+int kv_capacity(int M, int W) { return (int)round_up((long long)M + W, ATTN_KBLOCK); }
+
+// A key/value cache that takes n more rows in one call and has at least
+// `cap` slots: an attention call keeps the window and the n new rows at once
+// (cap = M + n); an append only overwrites slots of rows that leave the window
+// (cap = M + 8).
+txl_status check_kv_cache(txl_dtype dt, const txl_kv_cache *c, int n, long long cap, int B, int D, int H) {
+    if (!c) return fail(TXL_ERR_ARG, "cache is NULL");
+    if (c->M < 8 || c->M % 8) return fail(TXL_ERR_UNSUPPORTED, "cache M=%d must be a positive multiple of 8", c->M);
+    if (n % 8) return fail(TXL_ERR_UNSUPPORTED, "rows added to a cache per call (%d) must be a multiple of 8", n);
+    if (c->C % ATTN_KBLOCK || c->C < cap)
+        return fail(TXL_ERR_ARG, "cache capacity C=%d must be a multiple of %d and >= %lld "
+                    "(txl_kv_cache_capacity)", c->C, ATTN_KBLOCK, cap);
+    if (c->len < 0 || c->len > c->M || c->len % 8)
+        return fail(TXL_ERR_ARG, "cache len=%d must be a multiple of 8 in [0, M=%d]", c->len, c->M);
+    if (c->head < 0 || c->head >= c->C || c->head % 8)
+        return fail(TXL_ERR_ARG, "cache head=%d must be a multiple of 8 in [0, C=%d)", c->head, c->C);
+    if (!c->k || !c->vt) return fail(TXL_ERR_ARG, "cache k and vt must not be NULL");
+    if (((uintptr_t)c->k | (uintptr_t)c->vt) % 16) return fail(TXL_ERR_ARG, "cache k and vt must be 16-byte aligned");
+    if ((long long)B * H * c->C * attn_dp(D / H) * (long long)es_of(dt) >= (1LL << 40))
+        return fail(TXL_ERR_UNSUPPORTED, "cache too large");
+    return TXL_OK;
+}
+
 // The GEMM epilogue splits row indices with a float reciprocal, exact below 2^22.
 txl_status check_rows_budget(int B, int W, int M) {
     const long long kp = round_up((long long)M + W, ATTN_KBLOCK);
@@ -172,12 +198,35 @@ txl_status check_rows(const void *p, long long bstride, int W, int D, txl_dtype 
 // Enqueue projections + fused attention; the attention output lands in ws+L.o
 // as [B][W][D] rows.
 // ---------------------------------------------------------------------------
+// Projection of rows into a key/value cache (EPI_KV into ring slots
+// (head + len + t) mod C): rows x[b][t] for t < n.
+GemmProblem kv_cache_problem(int B, int n, int D, int H, int dp, const void *x, long long x_bstride,
+                             const txl_layer_params *p, const txl_kv_cache *c) {
+    GemmProblem kv;
+    memset(&kv, 0, sizeof(kv));
+    kv.rows = B * n; kv.cols = 2 * H * dp; kv.kdim = D;
+    kv.seg_rows = n; kv.valid_rows = n;
+    kv.a_mode = A_ROWS; kv.a = x; kv.a_ld = D; kv.a_bstride = x_bstride;
+    kv.b_mode = B_HEADS; kv.b0 = p->WkE; kv.b1 = p->Wv; kv.b_split = H * dp; kv.b_ld = D;
+    kv.dh = D / H; kv.dhp = dp; kv.heads = H;
+    kv.epi = EPI_KV; kv.c0 = c->k; kv.c1 = c->vt;
+    kv.kv_slots = c->C; kv.kv_base = (int)(((long long)c->head + c->len) % c->C);
+    return kv;
+}
+
+// Window of a key/value cache after n rows were appended.
+void kv_cache_advance(txl_kv_cache *c, int n) {
+    const int len = c->len + n < c->M ? c->len + n : c->M;
+    c->head = (int)(((long long)c->head + c->len + n - len) % c->C);
+    c->len = len;
+}
+
 txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const void *h, long long h_bstride,
-                             const txl_mem *mem, const txl_layer_params *p, const void *R, char *ws,
-                             const Layout &L, hipStream_t s) {
+                             const txl_mem *mem, const txl_kv_cache *cache, const txl_layer_params *p,
+                             const void *R, char *ws, const Layout &L, hipStream_t s) {
     const bool bf = dt == TXL_BF16;
     const int dh = D / H, dp = L.dp;
-    const int m = mem ? mem->len : 0;
+    const int m = cache ? cache->len : mem ? mem->len : 0;
     const int K = m + W;
     const int Kp = (int)round_up(K, ATTN_KBLOCK);
 
@@ -192,8 +241,11 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     q.dh = dh; q.dhp = dp; q.heads = H;
     q.epi = EPI_QUV; q.c0 = ws + L.qu; q.c1 = ws + L.qv; q.u = p->u; q.v = p->v;
     q.qscale = (float)(1.4426950408889634 / sqrt((double)dh));
-    // K_E and V from the context [mem; h]
+    // K_E and V: of the context [mem; h], or of the segment rows into the cache
     GemmProblem &kv = g.p[1];
+    if (cache) {
+        kv = kv_cache_problem(B, W, D, H, dp, h, h_bstride, p, cache);
+    } else {
     kv.rows = B * Kp; kv.cols = 2 * H * dp; kv.kdim = D;
     kv.seg_rows = Kp; kv.valid_rows = W;
     kv.a_mode = A_CONTEXT; kv.a = h; kv.a_ld = D; kv.a_bstride = h_bstride;
@@ -202,6 +254,8 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     kv.b_mode = B_HEADS; kv.b0 = p->WkE; kv.b1 = p->Wv; kv.b_split = H * dp; kv.b_ld = D;
     kv.dh = dh; kv.dhp = dp; kv.heads = H;
     kv.epi = EPI_KV; kv.c0 = ws + L.ke; kv.c1 = ws + L.vt;
+    kv.kv_slots = Kp; kv.kv_base = 0;
+    }
     // r = R[0:K] WkR^T, shared by the batch
     GemmProblem &r = g.p[2];
     r.rows = Kp + 2 * ATTN_RPAD; r.cols = H * dp; r.kdim = D;
@@ -223,9 +277,13 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     TXL_TRY(hip_check(launch_gemm(bf, g, s), "projection GEMM launch"));
 
     AttnArgs a;
-    a.qu = ws + L.qu; a.qv = ws + L.qv; a.ke = ws + L.ke; a.vt = ws + L.vt; a.rk = ws + L.rk;
+    a.qu = ws + L.qu; a.qv = ws + L.qv; a.rk = ws + L.rk;
+    a.ke = cache ? cache->k : (const void *)(ws + L.ke);
+    a.vt = cache ? cache->vt : (const void *)(ws + L.vt);
     a.o = ws + L.o; a.o_bstride = (long long)W * D;
     a.B = B; a.H = H; a.W = W; a.Wp = L.Wp; a.m = m; a.K = K; a.Kp = Kp; a.dh = dh; a.dp = dp; a.D = D;
+    a.C = cache ? cache->C : Kp;
+    a.khead = cache ? cache->head : 0;
     TXL_TRY(hip_check(attn_launch(bf, a, s), "attention launch"));
     return TXL_OK;
 }
@@ -260,7 +318,7 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
                          const txl_mem *mem, const txl_layer_params *p, const void *R, void *y,
                          long long y_bstride, char *ws, const Layout &L, hipStream_t s) {
     const bool bf = dt == TXL_BF16;
-    TXL_TRY(enqueue_attention(dt, B, W, D, H, h, h_bstride, mem, p, R, ws, L, s));
+    TXL_TRY(enqueue_attention(dt, B, W, D, H, h, h_bstride, mem, nullptr, p, R, ws, L, s));
     const long long WD = (long long)W * D;
     // z = h + O Wo^T (fp32)
     GemmProblem wo = rows_problem(B, W, D, D, ws + L.o, D, WD, p->Wo, ws + L.z, D, WD);
@@ -303,9 +361,10 @@ extern "C" {
 size_t txl_workspace_bytes(txl_op op, txl_dtype dtype, int B, int W, int M, int D, int H, int F) {
     if (B < 1 || W < 1 || D < 2 || H < 1 || D % H || M < 0) return 0;
     if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
-    if (op != TXL_OP_REL_ATTN && op != TXL_OP_LAYER && op != TXL_OP_STACK) return 0;
-    if (op != TXL_OP_REL_ATTN && F < 1) return 0;
-    return plan(op, dtype, B, W, M + W, D, H, op == TXL_OP_REL_ATTN ? 0 : F).total;
+    if (op != TXL_OP_REL_ATTN && op != TXL_OP_LAYER && op != TXL_OP_STACK && op != TXL_OP_REL_ATTN_CACHED) return 0;
+    const bool attn_only = op == TXL_OP_REL_ATTN || op == TXL_OP_REL_ATTN_CACHED;
+    if (!attn_only && F < 1) return 0;
+    return plan(op, dtype, B, W, M + W, D, H, attn_only ? 0 : F).total;
 }
 
 txl_status txl_sinusoid_table(txl_dtype dtype, int R_len, int D, void *R, void *stream) {
@@ -332,7 +391,7 @@ txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H, const v
     if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
-    TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, mem, p, R, w, L, s));
+    TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, mem, nullptr, p, R, w, L, s));
     GemmProblem wo = rows_problem(B, W, D, D, w + L.o, D, (long long)W * D, p->Wo, out, D, out_bstride);
     return hip_check(launch_gemm(dtype == TXL_BF16, single(wo), s), "output projection launch");
 }
@@ -405,6 +464,53 @@ txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, i
             hin_bs = hout_bs;
         }
     }
+    return TXL_OK;
+}
+
+int txl_kv_cache_capacity(int M, int W) {
+    if (M < 0 || W < 1) return 0;
+    return kv_capacity(M, W);
+}
+
+txl_status txl_kv_cache_append(txl_dtype dtype, int B, int D, int H, txl_kv_cache *cache,
+                               const txl_layer_params *p, const void *x, long long x_bstride, int n,
+                               void *stream) {
+    TXL_TRY(check_shape(dtype, B, n < 1 ? 1 : n, D, H));
+    if (n < 1) return fail(TXL_ERR_ARG, "n=%d must be >= 1", n);
+    TXL_TRY(check_rows(x, x_bstride, n, D, dtype, "x"));
+    TXL_TRY(check_attn_params(p));
+    const int keep = cache && n > cache->M ? cache->M : n;      // only the last M rows can stay
+    TXL_TRY(check_kv_cache(dtype, cache, keep, cache ? (long long)cache->M + 8 : 0, B, D, H));
+    if ((long long)B * keep >= (1LL << 22)) return fail(TXL_ERR_UNSUPPORTED, "B * rows = %lld exceeds 2^22", (long long)B * keep);
+    const char *first = (const char *)x + (size_t)(n - keep) * D * es_of(dtype);
+    // Rows past the new window may reuse slots of rows that leave it (C >= M + keep).
+    const GemmProblem kv = kv_cache_problem(B, keep, D, H, attn_dp(D / H), first, x_bstride, p, cache);
+    TXL_TRY(hip_check(launch_gemm(dtype == TXL_BF16, single(kv), (hipStream_t)stream), "cache projection launch"));
+    kv_cache_advance(cache, keep);
+    return TXL_OK;
+}
+
+txl_status txl_rel_attn_fwd_cached(txl_dtype dtype, int B, int W, int D, int H, const void *h, long long h_bstride,
+                                   txl_kv_cache *cache, const txl_layer_params *p, const void *R, int R_len,
+                                   void *out, long long out_bstride, void *ws, size_t ws_bytes, void *stream) {
+    TXL_TRY(check_shape(dtype, B, W, D, H));
+    TXL_TRY(check_rows(h, h_bstride, W, D, dtype, "h"));
+    TXL_TRY(check_rows(out, out_bstride, W, D, dtype, "out"));
+    TXL_TRY(check_kv_cache(dtype, cache, W, cache ? (long long)cache->M + W : 0, B, D, H));
+    TXL_TRY(check_attn_params(p));
+    const int m = cache->len;
+    TXL_TRY(check_rows_budget(B, W, m));
+    if (!R || !al4(R)) return fail(TXL_ERR_ARG, "R must be a non-NULL 4-byte aligned pointer");
+    if (R_len < m + W) return fail(TXL_ERR_ARG, "R_len=%d < cache len + W = %d", R_len, m + W);
+    const Layout L = plan(TXL_OP_REL_ATTN_CACHED, dtype, B, W, cache->M + W, D, H, 0);
+    if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+    if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, nullptr, cache, p, R, w, L, s));
+    GemmProblem wo = rows_problem(B, W, D, D, w + L.o, D, (long long)W * D, p->Wo, out, D, out_bstride);
+    TXL_TRY(hip_check(launch_gemm(dtype == TXL_BF16, single(wo), s), "output projection launch"));
+    kv_cache_advance(cache, W);
     return TXL_OK;
 }
 

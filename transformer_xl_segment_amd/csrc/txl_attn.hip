@@ -146,8 +146,8 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
 
     const T *qu = (const T *)A.qu + ((long long)bh * A.Wp) * DP;
     const T *qv = (const T *)A.qv + ((long long)bh * A.Wp) * DP;
-    const T *ke = (const T *)A.ke + ((long long)bh * A.Kp) * DP;
-    const T *vt = (const T *)A.vt + ((long long)bh * DP) * A.Kp;
+    const T *ke = (const T *)A.ke + ((long long)bh * A.C) * DP;
+    const T *vt = (const T *)A.vt + ((long long)bh * DP) * A.C;
     // row 0 of rk = distance 0; ATTN_RPAD zero rows on either side
     const T *rk = (const T *)A.rk + ((long long)h * (A.Kp + 2 * ATTN_RPAD) + ATTN_RPAD) * DP;
 
@@ -213,7 +213,10 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
         write_gblock(grow, gtop, 64, hf);
     }
 
-    // cooperative K / V^T staging
+    // cooperative K / V^T staging; key j lives in slot (khead + j) mod C, and a
+    // 16-byte V^T chunk (8 bf16 or 4 fp32 keys) never straddles the wrap
+    // because khead and C are multiples of 8
+    auto key_slot = [&](int j) { const int s = A.khead + j; return s >= A.C ? s - A.C : s; };
     constexpr int KCH = kKB * DP * (int)sizeof(T) / 16;    // 16-byte chunks per K tile
     constexpr int VCH = DP * kKB * (int)sizeof(T) / 16;    // ... per V^T tile
     constexpr int KPT = (KCH + 255) / 256, VPT = (VCH + 255) / 256;
@@ -227,14 +230,16 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
             const int idx = tid + 256 * c;                                                         \
             if (KCH % 256 == 0 || idx < KCH) {                                                     \
                 const int r_ = idx / KCPR, q_ = idx - r_ * KCPR;                                   \
-                rkt[c] = *reinterpret_cast<const u32x4 *>((const char *)(ke + (long long)(j0_ + r_) * DP) + q_ * 16); \
+                const int s_ = key_slot(j0_ + r_);                                                 \
+                rkt[c] = *reinterpret_cast<const u32x4 *>((const char *)(ke + (long long)s_ * DP) + q_ * 16); \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int c = 0; c < VPT; ++c) {                                          \
             const int idx = tid + 256 * c;                                                         \
             if (VCH % 256 == 0 || idx < VCH) {                                                     \
                 const int r_ = idx / VCPR, q_ = idx - r_ * VCPR;                                   \
-                rvt[c] = *reinterpret_cast<const u32x4 *>((const char *)(vt + (long long)r_ * A.Kp + j0_) + q_ * 16); \
+                const int s_ = key_slot(j0_ + q_ * (16 / (int)sizeof(T)));                         \
+                rvt[c] = *reinterpret_cast<const u32x4 *>(vt + (long long)r_ * A.C + s_);           \
             }                                                                                      \
         }                                                                                          \
     } while (0)

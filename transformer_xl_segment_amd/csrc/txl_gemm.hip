@@ -134,6 +134,12 @@ __device__ __forceinline__ void load8f(float (&x)[8], const T *src) {
 // (rows advance incrementally, no division). The transposed value output: a
 // wave covers 64 consecutive columns of one 8-row group, each lane writing
 // eight consecutive rows of its column as one store.
+// Key slot of segment row t for EPI_KV outputs.
+__device__ __forceinline__ int kv_slot(const GemmProblem &P, int t) {
+    const int s = P.kv_base + t;
+    return s >= P.kv_slots ? s - P.kv_slots : s;
+}
+
 template <typename T, bool VEC>
 __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, int m0, int n0, int tid,
                                          float inv_seg) {
@@ -215,9 +221,12 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
                     store8<T, true>((T *)P.c1 + idx, xv);
                 } else if (second) {
                     // a tile that straddles the K_E / V split writes its V columns here
+                    const int slot = kv_slot(P, t);
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
-                        ((T *)P.c1)[(bh * P.dhp + c + i) * P.seg_rows + t] = from_f32<T>(x[i]);
+                        ((T *)P.c1)[(bh * P.dhp + c + i) * P.kv_slots + slot] = from_f32<T>(x[i]);
+                } else if (P.epi == EPI_KV) {
+                    store8<T, true>((T *)P.c0 + (bh * P.kv_slots + kv_slot(P, t)) * P.dhp + c, x);
                 } else {
                     store8<T, true>((T *)P.c0 + (bh * P.seg_rows + t) * P.dhp + c, x);
                 }
@@ -227,7 +236,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
             while (t >= P.seg_rows) { t -= P.seg_rows; ++b; }
         }
     } else {
-        // V^T [b][hh][c][t]: rows of the tile are consecutive t (seg_rows % 8 == 0)
+        // V^T [b][hh][c][slot]: rows of the tile are consecutive t (seg_rows % 8 == 0)
         const int lane = tid & 63, wv = tid >> 6;
         for (int task = wv; task < 32; task += 4) {      // task = (row group rg, column half ch)
             const int rg = task >> 1, ch = task & 1;
@@ -242,7 +251,8 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
             float x[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) x[i] = cs[(8 * rg + i) * kCPitch + nl];
-            store8<T, true>((T *)P.c1 + (((long long)b * P.heads + hh) * P.dhp + c) * P.seg_rows + t, x);
+            // t, kv_base and kv_slots are multiples of 8: the eight slots are consecutive
+            store8<T, true>((T *)P.c1 + (((long long)b * P.heads + hh) * P.dhp + c) * P.kv_slots + kv_slot(P, t), x);
         }
     }
 }

@@ -27,7 +27,8 @@ enum BColMode {
 enum EpiMode {
     EPI_ROWS = 0,    // dst = c0 + b*c_bstride + t*c_ld + n (+bias[n], relu, +residual), T or fp32
     EPI_QUV = 1,     // c0 = (acc + u) * qscale, c1 = (acc + v) * qscale, head-major [b][hh][t][c]
-    EPI_KV = 2,      // n < b_split: c0 head-major [b][hh][t][c]; else c1 transposed [b][hh][c][t]
+    EPI_KV = 2,      // n < b_split: c0 head-major [b][hh][slot][c]; else c1 transposed [b][hh][c][slot],
+                     // slot = (kv_base + t) mod kv_slots
     EPI_HEADS = 3,   // c0 head-major [b][hh][t][c]
 };
 
@@ -60,6 +61,7 @@ struct GemmProblem {
     const void *u, *v;
     float qscale;
     int relu, out_f32;
+    int kv_slots, kv_base;       // EPI_KV: slots per (b, hh) and slot of row t = 0 (multiples of 8)
 };
 
 struct GemmLaunch {
@@ -77,19 +79,22 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p);
 // ---------------------------------------------------------------------------
 // Relative attention over projected, head-major operands.
 //   qu, qv  [B][H][Wp][dp]  (q + u) and (q + v), pre-scaled by log2(e)/sqrt(dh)
-//   ke      [B][H][Kp][dp]  content keys
-//   vt      [B][H][dp][Kp]  values, transposed
+//   ke      [B][H][C][dp]   content keys; key j lives in slot (khead + j) mod C
+//   vt      [B][H][dp][C]   values, transposed, same slots (khead and C multiples
+//                           of 8, C >= Kp)
 //   rk      [H][ATTN_RPAD + Kp + ATTN_RPAD][dp]  distance keys; row ATTN_RPAD + d holds
 //           distance d for 0 <= d < K and zeros elsewhere, so reads of distances in
 //           [-ATTN_RPAD, Kp + ATTN_RPAD) need no bounds checks
 //   o       [B][W][D]       output rows (heads concatenated), batch stride o_bstride
-// Rows past W (queries) and K (keys) hold zeros.
+// Rows past W (queries) hold zeros; key slots past K hold finite values (they
+// are masked).
 // ---------------------------------------------------------------------------
 struct AttnArgs {
     const void *qu, *qv, *ke, *vt, *rk;
     void *o;
     long long o_bstride;
     int B, H, W, Wp, m, K, Kp, dh, dp, D;
+    int C, khead;
 };
 // start / stop: optional events stamped at this kernel's own start and end.
 hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s, hipEvent_t start = nullptr,
