@@ -12,7 +12,10 @@ Prints ONE JSON line with the whole-job throughput (tokens/s), the attention
 kernel's roofline position (its own launches timed with HIP events inside the
 timed region) and the CPU oracle timed on a bounded sample of the same work.
 A second timed region runs the same segments with the memory kept as projected
-keys and values (txl_rel_attn_fwd_cached), reported under "kv_cache".
+keys and values (txl_rel_attn_fwd_cached), reported under "kv_cache". Then
+"sliding_window" compares segment-recurrent evaluation with vanilla evaluation,
+which re-encodes a window of the last M + W tokens from scratch for every new
+token, on the long-memory attention workload and on the 16-layer stack.
 """
 from __future__ import annotations
 
@@ -89,6 +92,95 @@ def time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, steps, warmup):
             "cache_bytes": 2 * B * M * D * 2}
 
 
+def _timed(torch, fn, calls, warm=2):
+    for k in range(warm):
+        fn(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(calls):
+        fn(warm + k)
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def sliding_window(tb, torch, syn, dev):
+    """Tokens/s of segment-recurrent evaluation (memory carried, W new tokens
+    per call) against vanilla evaluation (no memory; every new token re-encodes
+    the window of its last M + W tokens, one token per batch row per call)."""
+    bf = torch.bfloat16
+    res = {}
+
+    # one attention layer, long memory: window of M + W = 1728 keys
+    wl = syn.WORKLOADS["longmem_m1600_bf16"]
+    B, D, H, W, M = wl.B, wl.D, wl.H, wl.W, wl.M
+    prob = syn.draw_problem(wl)
+    stream = torch.from_numpy(np.concatenate([prob.warm_mem, prob.x], axis=1)).to(dev).to(bf)
+    T, Lw = stream.shape[1], M + W
+    params = tb.LayerParams.from_numpy(prob.params[0], bf, dev)
+    R = tb.sinusoid_table(Lw, D, bf, dev)
+    out = torch.empty(B, W, D, dtype=bf, device=dev)
+    segs = [stream[:, M + k * W:M + (k + 1) * W] for k in range(wl.S)]
+    ring = tb.MemoryRing.empty(B, M, D, bf, dev)
+    tb.mem_update(ring, stream[:, :M])
+    ws = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN, bf, B, W, M, D, H), dtype=torch.uint8, device=dev)
+
+    def rec(k):
+        tb.rel_attn_fwd(segs[k % wl.S], ring, params, R, H, out=out, workspace=ws)
+        tb.mem_update(ring, segs[k % wl.S])
+
+    n_rec = 60
+    t_rec = _timed(torch, rec, n_rec)
+    cache = tb.KVCache.empty(B, M, W, D, H, bf, dev)
+    tb.kv_cache_append(cache, params, stream[:, :M], H)
+    wsc = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN_CACHED, bf, B, W, M, D, H), dtype=torch.uint8,
+                      device=dev)
+    t_kv = _timed(torch, lambda k: tb.rel_attn_fwd_cached(segs[k % wl.S], cache, params, R, H, out=out,
+                                                         workspace=wsc), n_rec)
+    wout = torch.empty(B, Lw, D, dtype=bf, device=dev)
+    wsv = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN, bf, B, Lw, 0, D, H), dtype=torch.uint8, device=dev)
+
+    def van(k):
+        t = Lw - 1 + (k % (T - Lw + 1))      # newest token of the window
+        tb.rel_attn_fwd(stream[:, t - Lw + 1:t + 1], None, params, R, H, out=wout, workspace=wsv)
+
+    n_van = 60
+    t_van = _timed(torch, van, n_van)
+    v_rec, v_kv, v_van = B * W * n_rec / t_rec, B * W * n_rec / t_kv, B * n_van / t_van
+    res["attn_longmem"] = {"workload": wl.name, "window": Lw, "B": B,
+                           "recurrent_tokens_per_s": v_rec, "recurrent_kv_cache_tokens_per_s": v_kv,
+                           "vanilla_tokens_per_s": v_van, "vanilla_ms_per_window": t_van * 1e3 / n_van,
+                           "speedup": v_rec / v_van, "speedup_kv_cache": v_kv / v_van}
+    del stream, ring, cache, ws, wsc, wsv, wout
+
+    # the 16-layer stack: window of M + W = 300 tokens, every layer re-encoded
+    wl = syn.WORKLOADS["stack16_bf16"]
+    B, D, H, W, M, F = wl.B, wl.D, wl.H, wl.W, wl.M, wl.F
+    prob = syn.draw_problem(wl)
+    x = torch.from_numpy(prob.x).to(dev).to(bf)                    # [B, 8*W, D]
+    T, Lw = x.shape[1], M + W
+    lp = [tb.LayerParams.from_numpy(p, bf, dev) for p in prob.params]
+    R = tb.sinusoid_table(Lw, D, bf, dev)
+    mems = [tb.MemoryRing.empty(B, M, D, bf, dev) for _ in lp]
+    y = torch.empty_like(x)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_STACK, bf, B, W, M, D, H, F), dtype=torch.uint8, device=dev)
+    n_rec = 3
+    t_rec = _timed(torch, lambda k: tb.stack_fwd_segments(x, mems, lp, R, H, W, F, y=y, workspace=ws), n_rec, 1)
+    yw = torch.empty(B, Lw, D, dtype=bf, device=dev)
+    wsv = torch.empty(tb.workspace_bytes(tb.OP_STACK, bf, B, Lw, 0, D, H, F), dtype=torch.uint8, device=dev)
+
+    def van(k):
+        t = Lw - 1 + (k % (T - Lw + 1))
+        tb.stack_fwd_window(x[:, t - Lw + 1:t + 1], lp, R, H, F, y=yw, workspace=wsv)
+
+    n_van = 20
+    t_van = _timed(torch, van, n_van)
+    v_rec, v_van = B * T * n_rec / t_rec, B * n_van / t_van
+    res["stack16"] = {"workload": wl.name, "window": Lw, "B": B, "layers": len(lp),
+                      "recurrent_tokens_per_s": v_rec, "vanilla_tokens_per_s": v_van,
+                      "vanilla_ms_per_window": t_van * 1e3 / n_van, "speedup": v_rec / v_van}
+    return res
+
+
 def cpu_baseline(prob, R64, H):
     """The oracle on one full steady segment (m = 512, all batch rows)."""
     from oracle import oracle as orc
@@ -111,6 +203,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sliding-window", action="store_true",
+                    help="skip the comparison with vanilla sliding-window evaluation")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times) before the "
                          "warm-up, as the reference point for HBM byte counters")
@@ -205,6 +299,9 @@ def main():
     kv = time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, args.steps, args.warmup)
     kv["speedup_vs_row_memory"] = kv["value"] / rec["value"]
     rec["kv_cache"] = kv
+    if not args.no_sliding_window:
+        del ring, ws
+        rec["sliding_window"] = sliding_window(tb, torch, syn, dev)
     if not args.no_cpu_baseline:
         from oracle import oracle as orc
         R64 = orc.sinusoid_table(M + W, D)

@@ -189,6 +189,21 @@ txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, i
                                   const void *R, int R_len, void *y,
                                   void *ws, size_t ws_bytes, void *stream);
 
+/* Vanilla (no-memory) evaluation of a stack over one window: the model the
+ * pages compare Transformer-XL against re-encodes a window of the last W tokens
+ * from scratch for every new token, with no state carried between windows
+ * ("Transformer-XL, explained.", the evaluation-speed result; Ultralytics
+ * glossary, comparison with the vanilla Transformer). Runs n_layers blocks over
+ * x [B][W][D] (batch stride x_bstride, e.g. a window of a longer stream) with no
+ * memory, each layer attending within the window only, and writes the last
+ * layer's output to y [B][W][D] (batch stride y_bstride, must not overlap x).
+ * R_len >= W. Workspace: txl_workspace_bytes(TXL_OP_STACK, dtype, B, W, 0, D, H, F). */
+txl_status txl_stack_fwd_window(txl_dtype dtype, int B, int W, int D, int H, int F, int n_layers,
+                                const void *x, long long x_bstride,
+                                const txl_layer_params *params, const void *R, int R_len,
+                                void *y, long long y_bstride,
+                                void *ws, size_t ws_bytes, void *stream);
+
 /* Slots a key/value cache needs for memory length M and segments of up to W
  * rows: M + W rounded up to a multiple of 64. Returns 0 for M < 0 or W < 1. */
 int txl_kv_cache_capacity(int M, int W);

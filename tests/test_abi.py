@@ -125,6 +125,26 @@ def test_layer_and_stack_reject_bad_arguments():
                                     FAKE, None, 0, None) == tb.TXL_ERR_WORKSPACE
 
 
+def test_stack_window_rejects_bad_arguments():
+    L = tb.lib()
+    ps = (tb._Params * 2)(_params(), _params())
+    win = lambda n_layers=2, xs=64, R_len=4, ys=64, F=32, p=ps: L.txl_stack_fwd_window(
+        tb.TXL_FP32, 1, 4, 16, 2, F, n_layers, FAKE, xs, p, FAKE, R_len, FAKE + 4096, ys, None, 0, None)
+    assert win(n_layers=0) == tb.TXL_ERR_ARG
+    assert win(xs=63) == tb.TXL_ERR_ARG                 # x batch stride < W*D
+    assert win(ys=32) == tb.TXL_ERR_ARG
+    assert win(R_len=3) == tb.TXL_ERR_ARG               # R_len < W
+    assert win(F=31) == tb.TXL_ERR_ARG
+    assert win(p=None) == tb.TXL_ERR_ARG
+    q = (tb._Params * 2)(_params(), _params())
+    q[1].ln2_g = None
+    assert win(p=q) == tb.TXL_ERR_ARG
+    assert win(xs=1 << 20) == tb.TXL_ERR_WORKSPACE      # a window of a longer stream
+    # the window needs the stack's workspace with no memory
+    ws = L.txl_workspace_bytes(tb.OP_STACK, tb.TXL_FP32, 1, 4, 0, 16, 2, 32)
+    assert 0 < ws < L.txl_workspace_bytes(tb.OP_STACK, tb.TXL_FP32, 1, 4, 128, 16, 2, 32)
+
+
 def test_kv_cache_capacity_and_workspace():
     L = tb.lib()
     assert L.txl_kv_cache_capacity(512, 512) == 1024

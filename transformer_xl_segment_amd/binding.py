@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.txl_mem_update.argtypes = [i, i, i, Mp, vp, ll, i, vp]
         L.txl_layer_fwd.argtypes = [i, i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_stack_fwd_segments.argtypes = [i, i, i, i, i, i, i, i, vp, Mp, P, vp, i, vp, vp, sz, vp]
+        L.txl_stack_fwd_window.argtypes = [i, i, i, i, i, i, i, vp, ll, P, vp, i, vp, ll, vp, sz, vp]
         KVp = ctypes.POINTER(_KV)
         L.txl_kv_cache_capacity.argtypes = [i, i]
         L.txl_kv_cache_append.argtypes = [i, i, i, i, KVp, P, vp, ll, i, vp]
@@ -76,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.txl_profile_begin.argtypes = [i]
         L.txl_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_mem_update", "txl_layer_fwd",
-                  "txl_stack_fwd_segments", "txl_kv_cache_capacity", "txl_kv_cache_append",
+                  "txl_stack_fwd_segments", "txl_stack_fwd_window", "txl_kv_cache_capacity", "txl_kv_cache_append",
                   "txl_rel_attn_fwd_cached", "txl_profile_begin", "txl_profile_end"):
             getattr(L, f).restype = i
         L.txl_status_string.argtypes = [i]
@@ -315,6 +316,24 @@ def stack_fwd_segments(x: torch.Tensor, mems: Sequence[MemoryRing], params: Sequ
            "txl_stack_fwd_segments")
     for m, s in zip(mems, ms):
         m._update_from(s)
+    return y
+
+
+def stack_fwd_window(x: torch.Tensor, params: Sequence[LayerParams], R: torch.Tensor, H: int, F: int,
+                     y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The stack over one window x [B, W, D] (rows contiguous, any batch stride) with no memory."""
+    B, W, D = x.shape
+    xs = _rows_view(x, "x")
+    if y is None:
+        y = torch.empty(B, W, D, dtype=x.dtype, device=x.device)
+    ys = _rows_view(y, "y")
+    L = len(params)
+    ws = _workspace(workspace_bytes(OP_STACK, x.dtype, B, W, 0, D, H, F), x.device, workspace)
+    ps = (_Params * L)(*[p._struct() for p in params])
+    _check(lib().txl_stack_fwd_window(dtype_code(x.dtype), B, W, D, H, F, L, x.data_ptr(), xs, ps,
+                                      R.data_ptr(), R.shape[0], y.data_ptr(), ys, ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream(x.device)),
+           "txl_stack_fwd_window")
     return y
 
 

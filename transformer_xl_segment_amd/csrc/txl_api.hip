@@ -467,6 +467,37 @@ txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, i
     return TXL_OK;
 }
 
+txl_status txl_stack_fwd_window(txl_dtype dtype, int B, int W, int D, int H, int F, int n_layers, const void *x,
+                                long long x_bstride, const txl_layer_params *params, const void *R, int R_len,
+                                void *y, long long y_bstride, void *ws, size_t ws_bytes, void *stream) {
+    TXL_TRY(check_shape(dtype, B, W, D, H));
+    if (D > 1024) return fail(TXL_ERR_UNSUPPORTED, "LayerNorm supports D <= 1024 (got %d)", D);
+    if (n_layers < 1) return fail(TXL_ERR_ARG, "n_layers must be >= 1");
+    TXL_TRY(check_rows(x, x_bstride, W, D, dtype, "x"));
+    TXL_TRY(check_rows(y, y_bstride, W, D, dtype, "y"));
+    if (!params) return fail(TXL_ERR_ARG, "params must not be NULL");
+    for (int l = 0; l < n_layers; ++l) TXL_TRY(check_block_params(&params[l], F));
+    TXL_TRY(check_rows_budget(B, W, 0));
+    if (!R || !al4(R)) return fail(TXL_ERR_ARG, "R must be a non-NULL 4-byte aligned pointer");
+    if (R_len < W) return fail(TXL_ERR_ARG, "R_len=%d < W = %d", R_len, W);
+    const Layout L = plan(TXL_OP_STACK, dtype, B, W, W, D, H, F);
+    if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+    if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    const char *hin = (const char *)x;
+    long long hin_bs = x_bstride;
+    for (int l = 0; l < n_layers; ++l) {
+        const bool last = l == n_layers - 1;
+        char *hout = last ? (char *)y : w + ((l & 1) ? L.hb1 : L.hb0);
+        const long long hout_bs = last ? y_bstride : (long long)W * D;
+        TXL_TRY(enqueue_block(dtype, B, W, D, H, F, hin, hin_bs, nullptr, &params[l], R, hout, hout_bs, w, L, s));
+        hin = hout;
+        hin_bs = hout_bs;
+    }
+    return TXL_OK;
+}
+
 int txl_kv_cache_capacity(int M, int W) {
     if (M < 0 || W < 1) return 0;
     return kv_capacity(M, W);
