@@ -57,8 +57,11 @@ def lib() -> ctypes.CDLL:
         L.orc_mem_update.argtypes = [ctypes.c_int] * 4 + [_dp, ctypes.c_int, _dp, _dp, _ip]
         L.orc_stack_fwd.argtypes = ([ctypes.c_int] * 9 + [_dp] + [_dp] * 7 + [_dp] * 8
                                     + [_dp, ctypes.c_int, _dp, _dp, _ip])
+        L.orc_attn_variant.argtypes = [ctypes.c_int] * 6 + [_dp] * 8 + [ctypes.c_int, _dp]
+        L.orc_add_positions.argtypes = [ctypes.c_int] * 4 + [_dp, _dp]
         for f in ("orc_sinusoid_table", "orc_linear", "orc_layer_norm", "orc_rel_attn",
-                  "orc_layer_fwd", "orc_mem_update", "orc_stack_fwd"):
+                  "orc_layer_fwd", "orc_mem_update", "orc_stack_fwd", "orc_attn_variant",
+                  "orc_add_positions"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -137,6 +140,37 @@ def rel_attn(h: np.ndarray, mem: Optional[np.ndarray], p: Dict[str, np.ndarray],
                             _ptr(R), R.shape[0], _ptr(out), _ptr(P), _ptr(AC), _ptr(BD))
     _check(st, "rel_attn")
     return (out, P, AC, BD) if return_terms else out
+
+
+POS_SHAW, POS_ABSOLUTE = 1, 2
+
+
+def attn_variant(mode: int, h: np.ndarray, mem: Optional[np.ndarray], p: Dict[str, np.ndarray], H: int,
+                 aK: Optional[np.ndarray] = None, aV: Optional[np.ndarray] = None, clip: int = 0) -> np.ndarray:
+    """Attention + output projection with the encodings Transformer-XL is compared
+    against: POS_SHAW (clipped learned embeddings aK, aV [clip+1, dh] on keys and
+    values) or POS_ABSOLUTE (content attention; positions already in the rows)."""
+    h = _f64(h)
+    B, W, D = h.shape
+    m = 0 if mem is None else mem.shape[1]
+    memf = _f64(mem) if m > 0 else None
+    ps = [_f64(p[k]) for k in ("Wq", "WkE", "Wv", "Wo")]
+    ak = _f64(aK) if aK is not None else None
+    av = _f64(aV) if aV is not None else None
+    out = np.empty((B, W, D), dtype=np.float64)
+    st = lib().orc_attn_variant(mode, B, W, D, H, m, _ptr(h), _ptr(memf), *[_ptr(a) for a in ps],
+                                _ptr(ak), _ptr(av), clip, _ptr(out))
+    _check(st, "attn_variant")
+    return out
+
+
+def add_positions(x: np.ndarray, pos0: int = 0) -> np.ndarray:
+    """x [B, W, D] plus the absolute sinusoid of positions pos0 .. pos0 + W - 1."""
+    x = _f64(x)
+    B, W, D = x.shape
+    y = np.empty_like(x)
+    _check(lib().orc_add_positions(B, W, D, pos0, _ptr(x), _ptr(y)), "add_positions")
+    return y
 
 
 def layer_fwd(h: np.ndarray, mem: Optional[np.ndarray], p: Dict[str, np.ndarray], R: np.ndarray,

@@ -216,6 +216,123 @@ int orc_rel_attn(int B, int W, int D, int H, int m,
     return ORC_OK;
 }
 
+/*
+ * Attention with the position encodings Transformer-XL is compared against
+ * ([XL] "What it adds to earlier relative positions" and the ablation
+ * paragraph of its results; [IMPL] relative_attention's clip of the distance
+ * to max_rel_dist), followed by the output projection:
+ *
+ *   mode ORC_POS_SHAW (Shaw, Uszkoreit and Vaswani): learned embeddings of the
+ *     clipped distance, on the keys and on the values, and only the first two
+ *     score terms (no u, v):
+ *       score_ij = (q_i.k_j + q_i.aK[min(delta, clip)]) / sqrt(dh)
+ *       o_i      = sum_j p_ij (val_j + aV[min(delta, clip)])
+ *     aK, aV [clip+1][dh], the same tables for every head; delta = m + i - j.
+ *   mode ORC_POS_ABSOLUTE: content attention only, score_ij = q_i.k_j / sqrt(dh),
+ *     o_i = sum_j p_ij val_j; the positions are already part of the rows
+ *     (orc_add_positions on the model's input).
+ * Causal over [mem; h] as in orc_rel_attn. Reads Wq, WkE, Wv, Wo.
+ */
+#define ORC_POS_SHAW 1
+#define ORC_POS_ABSOLUTE 2
+
+int orc_attn_variant(int mode, int B, int W, int D, int H, int m,
+                     const double *h, const double *mem,
+                     const double *Wq, const double *WkE, const double *Wv, const double *Wo,
+                     const double *aK, const double *aV, int clip, double *out)
+{
+    if (mode != ORC_POS_SHAW && mode != ORC_POS_ABSOLUTE) return ORC_ERR_ARG;
+    if (B < 1 || W < 1 || D < 1 || H < 1 || D % H != 0 || m < 0) return ORC_ERR_ARG;
+    if (!h || (m > 0 && !mem) || !Wq || !WkE || !Wv || !Wo || !out) return ORC_ERR_ARG;
+    if (mode == ORC_POS_SHAW && (clip < 0 || !aK || !aV)) return ORC_ERR_ARG;
+    const int K = m + W;
+    const int dh = D / H;
+    const double inv_sqrt_dh = 1.0 / sqrt((double)dh);
+
+    double *ctx = malloc(sizeof(double) * (size_t)B * K * D);
+    double *Q = malloc(sizeof(double) * (size_t)B * W * D);
+    double *KE = malloc(sizeof(double) * (size_t)B * K * D);
+    double *V = malloc(sizeof(double) * (size_t)B * K * D);
+    double *O = malloc(sizeof(double) * (size_t)B * W * D);
+    if (!ctx || !Q || !KE || !V || !O) {
+        free(ctx); free(Q); free(KE); free(V); free(O);
+        return ORC_ERR_NOMEM;
+    }
+    for (int b = 0; b < B; ++b) {
+        for (int j = 0; j < m; ++j)
+            memcpy(ctx + ((size_t)b * K + j) * D, mem + ((size_t)b * m + j) * D, sizeof(double) * D);
+        for (int i = 0; i < W; ++i)
+            memcpy(ctx + ((size_t)b * K + m + i) * D, h + ((size_t)b * W + i) * D, sizeof(double) * D);
+    }
+    orc_linear((long)B * W, D, D, h, Wq, Q);
+    orc_linear((long)B * K, D, D, ctx, WkE, KE);
+    orc_linear((long)B * K, D, D, ctx, Wv, V);
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        for (int hd = 0; hd < H; ++hd) {
+            double *p = malloc(sizeof(double) * K);
+            const int c0 = hd * dh;
+            for (int i = 0; i < W; ++i) {
+                const double *q = Q + ((size_t)b * W + i) * D;
+                const int last = m + i;              /* keys 0..last are visible */
+                double smax = -INFINITY;
+                for (int j = 0; j <= last; ++j) {
+                    const double *k = KE + ((size_t)b * K + j) * D;
+                    double sc = 0.0;
+                    for (int c = 0; c < dh; ++c) sc += q[c0 + c] * k[c0 + c];
+                    if (mode == ORC_POS_SHAW) {
+                        const int delta = m + i - j;
+                        const double *ak = aK + (size_t)(delta < clip ? delta : clip) * dh;
+                        for (int c = 0; c < dh; ++c) sc += q[c0 + c] * ak[c];
+                    }
+                    p[j] = sc * inv_sqrt_dh;
+                    if (p[j] > smax) smax = p[j];
+                }
+                double denom = 0.0;
+                for (int j = 0; j <= last; ++j) {
+                    p[j] = exp(p[j] - smax);
+                    denom += p[j];
+                }
+                double *o = O + ((size_t)b * W + i) * D;
+                for (int c = 0; c < dh; ++c) {
+                    double acc = 0.0;
+                    for (int j = 0; j <= last; ++j) {
+                        double val = V[((size_t)b * K + j) * D + c0 + c];
+                        if (mode == ORC_POS_SHAW) {
+                            const int delta = m + i - j;
+                            val += aV[(size_t)(delta < clip ? delta : clip) * dh + c];
+                        }
+                        acc += (p[j] / denom) * val;
+                    }
+                    o[c0 + c] = acc;
+                }
+            }
+            free(p);
+        }
+    }
+    orc_linear((long)B * W, D, D, O, Wo, out);
+    free(ctx); free(Q); free(KE); free(V); free(O);
+    return ORC_OK;
+}
+
+/* Absolute positions of the ablation ([XL] results: absolute encodings with
+ * recurrence): y[b][t] = x[b][t] + U[pos0 + t], U the sinusoid of orc_sinusoid_table
+ * evaluated at the absolute position instead of a distance. */
+int orc_add_positions(int B, int W, int D, int pos0, const double *x, double *y)
+{
+    if (B < 1 || W < 1 || D < 2 || D % 2 || pos0 < 0 || !x || !y) return ORC_ERR_ARG;
+    double *U = malloc(sizeof(double) * (size_t)(pos0 + W) * D);
+    if (!U) return ORC_ERR_NOMEM;
+    orc_sinusoid_table(pos0 + W, D, U);
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < W; ++t)
+            for (int c = 0; c < D; ++c)
+                y[((size_t)b * W + t) * D + c] = x[((size_t)b * W + t) * D + c] + U[(size_t)(pos0 + t) * D + c];
+    free(U);
+    return ORC_OK;
+}
+
 /* Post-LN block of [IMPL] forward: h1 = LN1(h + attn), y = LN2(h1 + FFN(h1)),
  * FFN(x) = ReLU(x W1^T + b1) W2^T + b2. */
 int orc_layer_fwd(int B, int W, int D, int H, int F, int m,

@@ -389,6 +389,119 @@ def test_reach_grows_one_segment_per_layer():
             np.testing.assert_array_equal(y[:, seg], y2[:, seg])
 
 
+# --------------------------------------------------------------------------
+# Encodings Transformer-XL is compared against (Shaw et al.; absolute).
+# --------------------------------------------------------------------------
+
+def _sdpa_plain(h, mem, p, H):
+    """Causal softmax(Q K^T / sqrt(dh)) V over [mem; h], then W_o, by torch."""
+    B, W, D = h.shape
+    ctx = np.concatenate([mem, h], axis=1) if mem is not None else h
+    K, dh = ctx.shape[1], D // H
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    q = t(h @ p["Wq"].T).reshape(B, W, H, dh).transpose(1, 2)
+    k = t(ctx @ p["WkE"].T).reshape(B, K, H, dh).transpose(1, 2)
+    v = t(ctx @ p["Wv"].T).reshape(B, K, H, dh).transpose(1, 2)
+    mask = torch.ones(W, K, dtype=torch.bool).tril(diagonal=K - W)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask)
+    return o.transpose(1, 2).reshape(B, W, D).numpy() @ p["Wo"].T
+
+
+def test_absolute_variant_is_plain_attention():
+    p, h, mem, _ = _attn_case(seed=21, B=2, W=6, m=4, D=16, H=4)
+    out = orc.attn_variant(orc.POS_ABSOLUTE, h, mem, p, 4)
+    np.testing.assert_allclose(out, _sdpa_plain(h, mem, p, 4), rtol=1e-11, atol=1e-12)
+
+
+def test_shaw_with_zero_tables_is_plain_attention():
+    p, h, mem, _ = _attn_case(seed=22, B=2, W=6, m=4, D=16, H=4)
+    z = np.zeros((4, 4))
+    out = orc.attn_variant(orc.POS_SHAW, h, mem, p, 4, aK=z, aV=z, clip=3)
+    np.testing.assert_allclose(out, _sdpa_plain(h, mem, p, 4), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("clip", [0, 2, 5, 40])
+def test_shaw_value_term_under_uniform_attention(clip):
+    # W_q = 0: every visible key gets the same weight, so o_i is the mean of the
+    # visible values plus the mean of aV over the clipped distances 0 .. m + i
+    B, W, m, D, H = 2, 7, 5, 12, 3
+    p, h, mem, _ = _attn_case(seed=23, B=B, W=W, m=m, D=D, H=H)
+    p = dict(p)
+    p["Wq"] = np.zeros((D, D))
+    p["Wo"] = np.eye(D)
+    dh = D // H
+    rng = np.random.default_rng(24)
+    aK = rng.standard_normal((clip + 1, dh))
+    aV = rng.standard_normal((clip + 1, dh))
+    out = orc.attn_variant(orc.POS_SHAW, h, mem, p, H, aK=aK, aV=aV, clip=clip)
+    val = np.concatenate([mem, h], axis=1) @ p["Wv"].T
+    for i in range(W):
+        n = m + i + 1
+        mean_val = val[:, :n].mean(axis=1)
+        deltas = np.minimum(np.arange(n), clip)
+        mean_av = np.tile(aV[deltas].mean(axis=0), H)
+        np.testing.assert_allclose(out[:, i], mean_val + mean_av, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("clip", [1, 3, 30])
+def test_shaw_distance_weights_follow_clipped_distance(clip):
+    # All rows equal: content scores are one constant, so with aK[d] = d g the
+    # weights are p(delta) ~ exp(beta min(delta, clip)), beta = q.g / sqrt(dh),
+    # over delta = 0 .. m + i; with aV[d] = d e the output is val + E[min(delta, clip)] e.
+    B, W, m, D, H = 1, 6, 4, 8, 2
+    dh = D // H
+    rng = np.random.default_rng(25)
+    p = _params(rng, D, scale=0.5)
+    row = rng.standard_normal(D)
+    h = np.tile(row, (B, W, 1))
+    mem = np.tile(row, (B, m, 1))
+    g = rng.standard_normal(dh)
+    d = np.arange(clip + 1, dtype=np.float64)[:, None]
+    aK = d * g[None, :]
+    aV = d * np.ones((1, dh))
+    out = orc.attn_variant(orc.POS_SHAW, h, mem, p, H, aK=aK, aV=aV, clip=clip)
+    q = row @ p["Wq"].T
+    val = row @ p["Wv"].T
+    for i in range(W):
+        deltas = np.minimum(np.arange(m + i + 1), clip)
+        o = np.empty(D)
+        for hd in range(H):
+            beta = q[hd * dh:(hd + 1) * dh] @ g / math.sqrt(dh)
+            w = np.exp(beta * deltas - np.max(beta * deltas))
+            w /= w.sum()
+            o[hd * dh:(hd + 1) * dh] = val[hd * dh:(hd + 1) * dh] + (w * deltas).sum()
+        np.testing.assert_allclose(out[0, i], o @ p["Wo"].T, rtol=1e-10, atol=1e-12)
+
+
+def test_shaw_one_head_matches_relative_attention_without_biases():
+    # One head, aK[d] = (R W_kR^T)[d] with no clipping inside the window and
+    # aV = 0: Shaw's two score terms are Transformer-XL's with u = v = 0.
+    B, W, m, D = 2, 5, 6, 8
+    p, h, mem, R = _attn_case(seed=26, B=B, W=W, m=m, D=D, H=1)
+    p = dict(p)
+    p["u"] = np.zeros(D)
+    p["v"] = np.zeros(D)
+    aK = R @ p["WkR"].T
+    out = orc.attn_variant(orc.POS_SHAW, h, mem, p, 1, aK=aK, aV=np.zeros_like(aK), clip=m + W - 1)
+    np.testing.assert_allclose(out, orc.rel_attn(h, mem, p, R, 1), rtol=1e-11, atol=1e-12)
+
+
+def test_absolute_positions_closed_forms():
+    B, W, D = 2, 9, 10
+    x = np.random.default_rng(27).standard_normal((B, W, D))
+    for pos0 in (0, 5):
+        y = orc.add_positions(x, pos0)
+        U = y - x
+        t = np.arange(pos0, pos0 + W, dtype=np.float64)
+        # frequency 1 in column 0 (sin) and column D/2 (cos); the slowest pair
+        # has frequency 10000^(-(D-2)/D)
+        np.testing.assert_allclose(U[:, :, 0], np.broadcast_to(np.sin(t), (B, W)), atol=1e-13)
+        np.testing.assert_allclose(U[:, :, D // 2], np.broadcast_to(np.cos(t), (B, W)), atol=1e-13)
+        f = 10000.0 ** (-(D - 2) / D)
+        np.testing.assert_allclose(U[:, :, D // 2 - 1], np.broadcast_to(np.sin(t * f), (B, W)), atol=1e-13)
+        np.testing.assert_allclose(U[:, :, D - 1], np.broadcast_to(np.cos(t * f), (B, W)), atol=1e-13)
+
+
 def test_bad_arguments_are_rejected():
     p, h, mem, R = _attn_case()
     with pytest.raises(ValueError):
