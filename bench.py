@@ -16,6 +16,8 @@ keys and values (txl_rel_attn_fwd_cached), reported under "kv_cache". Then
 "sliding_window" compares segment-recurrent evaluation with vanilla evaluation,
 which re-encodes a window of the last M + W tokens from scratch for every new
 token, on the long-memory attention workload and on the 16-layer stack.
+"encodings" times the same step with the encodings the pages compare against
+(Shaw et al.'s clipped embeddings, absolute positions).
 """
 from __future__ import annotations
 
@@ -90,6 +92,33 @@ def time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, steps, warmup):
     return {"value": B * W * steps / elapsed, "unit": "tokens/s", "ms_per_step": elapsed * 1e3 / steps,
             "step": "txl_rel_attn_fwd_cached, one steady segment (m = M)",
             "cache_bytes": 2 * B * M * D * 2}
+
+
+def time_encodings(tb, torch, segs, params, B, M, W, D, H, out, steps, warmup):
+    """The same steady segment step with Shaw et al.'s encoding (clip 64, tables
+    N(0, 0.02)) and with absolute positions (added to each segment's rows)."""
+    bf = torch.bfloat16
+    dev = out.device
+    dh = D // H
+    g = torch.Generator().manual_seed(99)
+    aK = (torch.randn(65, dh, generator=g) * 0.02).to(dev).to(bf)
+    aV = (torch.randn(65, dh, generator=g) * 0.02).to(dev).to(bf)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_ATTN_VARIANT, bf, B, W, M, D, H), dtype=torch.uint8, device=dev)
+    hp = torch.empty(B, W, D, dtype=bf, device=dev)
+    res = {}
+    for name, variant in (("shaw_clip64", tb.POS_SHAW), ("absolute", tb.POS_ABSOLUTE)):
+        ring = tb.MemoryRing.empty(B, M, D, bf, dev)
+
+        def step(k):
+            h = segs[k % len(segs)]
+            if variant == tb.POS_ABSOLUTE:
+                h = tb.add_positions(h, 0, y=hp)
+            tb.attn_fwd_variant(h, ring, params, variant, H, aK=aK, aV=aV, clip=64, out=out, workspace=ws)
+            tb.mem_update(ring, h)
+
+        el = _timed(torch, step, steps, warmup + (M + W - 1) // W)
+        res[name] = {"value": B * W * steps / el, "unit": "tokens/s", "ms_per_step": el * 1e3 / steps}
+    return res
 
 
 def _timed(torch, fn, calls, warm=2):
@@ -299,6 +328,7 @@ def main():
     kv = time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, args.steps, args.warmup)
     kv["speedup_vs_row_memory"] = kv["value"] / rec["value"]
     rec["kv_cache"] = kv
+    rec["encodings"] = time_encodings(tb, torch, segs, params, B, M, W, D, H, out, args.steps, args.warmup)
     if not args.no_sliding_window:
         del ring, ws
         rec["sliding_window"] = sliding_window(tb, torch, syn, dev)

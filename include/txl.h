@@ -71,8 +71,17 @@ typedef enum {
     TXL_OP_REL_ATTN = 0,      /* txl_rel_attn_fwd */
     TXL_OP_LAYER = 1,         /* txl_layer_fwd */
     TXL_OP_STACK = 2,         /* txl_stack_fwd_segments */
-    TXL_OP_REL_ATTN_CACHED = 3 /* txl_rel_attn_fwd_cached */
+    TXL_OP_REL_ATTN_CACHED = 3, /* txl_rel_attn_fwd_cached */
+    TXL_OP_ATTN_VARIANT = 4   /* txl_attn_fwd_variant */
 } txl_op;
+
+/* Position encodings Transformer-XL is compared against ("Transformer-XL,
+ * explained.", "What it adds to earlier relative positions" and the ablations
+ * among its results). */
+typedef enum {
+    TXL_POS_SHAW = 1,         /* Shaw et al.: learned clipped-distance embeddings on keys and values */
+    TXL_POS_ABSOLUTE = 2      /* absolute positions in the rows, content-only attention */
+} txl_pos_variant;
 
 /* One layer's parameters, all device pointers of the call's dtype.
  * Attention (pages: W_q, W_k,E, W_k,R, W_v, W_o and the global biases u, v):
@@ -203,6 +212,35 @@ txl_status txl_stack_fwd_window(txl_dtype dtype, int B, int W, int D, int H, int
                                 const txl_layer_params *params, const void *R, int R_len,
                                 void *y, long long y_bstride,
                                 void *ws, size_t ws_bytes, void *stream);
+
+/* Attention + output projection of one segment over [mem; h] with an encoding
+ * other than Transformer-XL's (txl_pos_variant), for comparison. Reads Wq, WkE,
+ * Wv and Wo of p only (no u, v, WkR, R). Causal over [mem; h] as in
+ * txl_rel_attn_fwd; the memory is not updated (txl_mem_update).
+ *   TXL_POS_SHAW: score_ij = (q_i.k_j + q_i.aK[min(delta, clip)]) / sqrt(dh) and
+ *     o_i = sum_j p_ij (val_j + aV[min(delta, clip)]), delta = m + i - j: the
+ *     first two score terms only, with learned embeddings of the clipped
+ *     distance (the NumPy layer's clip to max_rel_dist) also on the values.
+ *     aK, aV device [clip+1][dh] of the call's dtype, the same for every head;
+ *     0 <= clip <= 128.
+ *   TXL_POS_ABSOLUTE: score_ij = q_i.k_j / sqrt(dh), o_i = sum_j p_ij val_j; the
+ *     positions are part of the rows (txl_add_positions on the model's input, so
+ *     that cached rows keep the positions of their own segment). aK, aV unused.
+ * Workspace: txl_workspace_bytes(TXL_OP_ATTN_VARIANT, ...). */
+txl_status txl_attn_fwd_variant(txl_dtype dtype, txl_pos_variant variant, int B, int W, int D, int H,
+                                const void *h, long long h_bstride,
+                                const txl_mem *mem, const txl_layer_params *p,
+                                const void *aK, const void *aV, int clip,
+                                void *out, long long out_bstride,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/* Absolute positions for the comparison model: y[b][t] = x[b][t] + U[pos0 + t]
+ * for t < W, U[p][k] = sin(p * 10000^(-2k/D)) and U[p][D/2 + k] = cos(...), the
+ * distance table's sinusoid at a position (the absolute model gives every
+ * segment positions 0 .. W-1, so pos0 = 0). x and y [B][W][D] with batch strides;
+ * y may equal x. D even, at most 1024. */
+txl_status txl_add_positions(txl_dtype dtype, int B, int W, int D, const void *x, long long x_bstride,
+                             int pos0, void *y, long long y_bstride, void *stream);
 
 /* Slots a key/value cache needs for memory length M and segments of up to W
  * rows: M + W rounded up to a multiple of 64. Returns 0 for M < 0 or W < 1. */

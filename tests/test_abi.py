@@ -145,6 +145,40 @@ def test_stack_window_rejects_bad_arguments():
     assert 0 < ws < L.txl_workspace_bytes(tb.OP_STACK, tb.TXL_FP32, 1, 4, 128, 16, 2, 32)
 
 
+def test_variants_reject_bad_arguments():
+    L = tb.lib()
+    p = _params()
+    def var(v=tb.POS_SHAW, clip=4, aK=FAKE, aV=FAKE, W=4, hs=64, mem=None, pp=p):
+        return L.txl_attn_fwd_variant(tb.TXL_FP32, v, 1, W, 16, 2, FAKE, hs, ctypes.byref(mem) if mem else None,
+                                      ctypes.byref(pp) if pp else None, aK, aV, clip, FAKE, 64, None, 0, None)
+    assert var(v=0) == tb.TXL_ERR_ARG
+    assert var(v=3) == tb.TXL_ERR_ARG
+    assert var(clip=-1) == tb.TXL_ERR_UNSUPPORTED
+    assert var(clip=129) == tb.TXL_ERR_UNSUPPORTED
+    assert var(aK=None) == tb.TXL_ERR_ARG
+    assert var(aV=FAKE + 2) == tb.TXL_ERR_ARG
+    assert var(hs=10) == tb.TXL_ERR_ARG
+    assert var(pp=None) == tb.TXL_ERR_ARG
+    q = _params()
+    q.Wv = None
+    assert var(pp=q) == tb.TXL_ERR_ARG
+    q = _params()
+    q.WkR = None; q.u = None; q.v = None                 # not read by the variants
+    assert var(pp=q) == tb.TXL_ERR_WORKSPACE
+    assert var(v=tb.POS_ABSOLUTE, aK=None, aV=None) == tb.TXL_ERR_WORKSPACE
+    assert var(mem=tb._Mem(FAKE, 4, 5, 0)) == tb.TXL_ERR_ARG
+    # workspace: the attention layout plus one float per query
+    a = L.txl_workspace_bytes(tb.OP_REL_ATTN, tb.TXL_BF16, 16, 512, 512, 512, 8, 0)
+    v = L.txl_workspace_bytes(tb.OP_ATTN_VARIANT, tb.TXL_BF16, 16, 512, 512, 512, 8, 0)
+    assert v == a + 16 * 8 * 512 * 4
+    pos = lambda D=16, xs=64, ys=64, pos0=0: L.txl_add_positions(tb.TXL_FP32, 1, 4, D, FAKE, xs, pos0, FAKE, ys, None)
+    assert pos(D=15, xs=60, ys=60) == tb.TXL_ERR_ARG
+    assert pos(pos0=-1) == tb.TXL_ERR_ARG
+    assert pos(xs=63) == tb.TXL_ERR_ARG
+    assert L.txl_add_positions(tb.TXL_FP32, 1, 4, 1026, FAKE, 4104, 0, FAKE, 4104, None) == tb.TXL_ERR_UNSUPPORTED
+    assert L.txl_add_positions(7, 1, 4, 16, FAKE, 64, 0, FAKE, 64, None) == tb.TXL_ERR_UNSUPPORTED
+
+
 def test_kv_cache_capacity_and_workspace():
     L = tb.lib()
     assert L.txl_kv_cache_capacity(512, 512) == 1024

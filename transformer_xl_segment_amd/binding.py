@@ -23,7 +23,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "txl.h")
 
 TXL_OK, TXL_ERR_ARG, TXL_ERR_UNSUPPORTED, TXL_ERR_WORKSPACE, TXL_ERR_HIP = range(5)
 TXL_FP32, TXL_BF16 = 0, 1
-OP_REL_ATTN, OP_LAYER, OP_STACK, OP_REL_ATTN_CACHED = 0, 1, 2, 3
+OP_REL_ATTN, OP_LAYER, OP_STACK, OP_REL_ATTN_CACHED, OP_ATTN_VARIANT = 0, 1, 2, 3, 4
+POS_SHAW, POS_ABSOLUTE = 1, 2
 
 _PARAM_FIELDS = ("Wq", "WkE", "WkR", "Wv", "Wo", "u", "v", "ln1_g", "ln1_b", "W1", "b1",
                  "W2", "b2", "ln2_g", "ln2_b")
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.txl_mem_update.argtypes = [i, i, i, Mp, vp, ll, i, vp]
         L.txl_layer_fwd.argtypes = [i, i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_stack_fwd_segments.argtypes = [i, i, i, i, i, i, i, i, vp, Mp, P, vp, i, vp, vp, sz, vp]
+        L.txl_attn_fwd_variant.argtypes = [i, i, i, i, i, i, vp, ll, Mp, P, vp, vp, i, vp, ll, vp, sz, vp]
+        L.txl_add_positions.argtypes = [i, i, i, i, vp, ll, i, vp, ll, vp]
         L.txl_stack_fwd_window.argtypes = [i, i, i, i, i, i, i, vp, ll, P, vp, i, vp, ll, vp, sz, vp]
         KVp = ctypes.POINTER(_KV)
         L.txl_kv_cache_capacity.argtypes = [i, i]
@@ -77,7 +80,8 @@ def lib() -> ctypes.CDLL:
         L.txl_profile_begin.argtypes = [i]
         L.txl_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_mem_update", "txl_layer_fwd",
-                  "txl_stack_fwd_segments", "txl_stack_fwd_window", "txl_kv_cache_capacity", "txl_kv_cache_append",
+                  "txl_stack_fwd_segments", "txl_stack_fwd_window", "txl_kv_cache_capacity",
+                  "txl_attn_fwd_variant", "txl_add_positions", "txl_kv_cache_append",
                   "txl_rel_attn_fwd_cached", "txl_profile_begin", "txl_profile_end"):
             getattr(L, f).restype = i
         L.txl_status_string.argtypes = [i]
@@ -265,6 +269,42 @@ def rel_attn_fwd_cached(h: torch.Tensor, cache: KVCache, params: LayerParams, R:
            "txl_rel_attn_fwd_cached")
     cache._update_from(cs)
     return out
+
+
+def attn_fwd_variant(h: torch.Tensor, mem: Optional[MemoryRing], params: LayerParams, variant: int, H: int,
+                     aK: Optional[torch.Tensor] = None, aV: Optional[torch.Tensor] = None, clip: int = 0,
+                     out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Attention + output projection with Shaw et al.'s (POS_SHAW, tables aK, aV
+    [clip+1, dh]) or absolute-position (POS_ABSOLUTE) encoding."""
+    B, W, D = h.shape
+    hs = _rows_view(h, "h")
+    if out is None:
+        out = torch.empty(B, W, D, dtype=h.dtype, device=h.device)
+    os_ = _rows_view(out, "out")
+    M = mem.M if mem is not None else 0
+    ws = _workspace(workspace_bytes(OP_ATTN_VARIANT, h.dtype, B, W, M, D, H), h.device, workspace)
+    ms = mem._struct() if mem is not None else None
+    ps = params._struct()
+    aK = aK.contiguous() if aK is not None else None
+    aV = aV.contiguous() if aV is not None else None
+    _check(lib().txl_attn_fwd_variant(dtype_code(h.dtype), variant, B, W, D, H, h.data_ptr(), hs,
+                                      ctypes.byref(ms) if ms is not None else None, ctypes.byref(ps),
+                                      _ptr(aK), _ptr(aV), clip, out.data_ptr(), os_, ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream(h.device)),
+           "txl_attn_fwd_variant")
+    return out
+
+
+def add_positions(x: torch.Tensor, pos0: int = 0, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [B, W, D] plus the absolute sinusoid of positions pos0 .. pos0 + W - 1."""
+    B, W, D = x.shape
+    xs = _rows_view(x, "x")
+    if y is None:
+        y = torch.empty(B, W, D, dtype=x.dtype, device=x.device)
+    ys = _rows_view(y, "y")
+    _check(lib().txl_add_positions(dtype_code(x.dtype), B, W, D, x.data_ptr(), xs, pos0, y.data_ptr(), ys,
+                                   _stream(x.device)), "txl_add_positions")
+    return y
 
 
 def mem_update(mem: MemoryRing, h: torch.Tensor) -> None:

@@ -47,6 +47,7 @@ bool al4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 // ---------------------------------------------------------------------------
 struct Layout {
     size_t qu, qv, ke, vt, rk, o;      // attention operands and output
+    size_t lse;                        // encoding variants: per-query log-sum-exp
     size_t z, h1, f;                   // block: fp32 pre-LN sums, LN1 output, FFN hidden
     size_t hb0, hb1;                   // stack: inter-layer activations
     size_t total;
@@ -77,6 +78,7 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
     }
     L.rk = take((size_t)H * (L.Kp + 2 * ATTN_RPAD) * L.dp * es);
     L.o = take((size_t)B * W * D * es);
+    if (op == TXL_OP_ATTN_VARIANT) L.lse = take((size_t)B * H * L.Wp * 4);
     if (op == TXL_OP_LAYER || op == TXL_OP_STACK) {
         L.z = take((size_t)B * W * D * 4);
         L.h1 = take((size_t)B * W * D * es);
@@ -221,9 +223,18 @@ void kv_cache_advance(txl_kv_cache *c, int n) {
     c->len = len;
 }
 
+// An encoding other than Transformer-XL's: Shaw et al.'s clipped embeddings
+// (aK, aV, clip) or absolute positions (no distance term).
+struct Variant {
+    txl_pos_variant kind;
+    const void *aK, *aV;
+    int clip;
+};
+
 txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const void *h, long long h_bstride,
                              const txl_mem *mem, const txl_kv_cache *cache, const txl_layer_params *p,
-                             const void *R, char *ws, const Layout &L, hipStream_t s) {
+                             const void *R, char *ws, const Layout &L, hipStream_t s,
+                             const Variant *var = nullptr) {
     const bool bf = dt == TXL_BF16;
     const int dh = D / H, dp = L.dp;
     const int m = cache ? cache->len : mem ? mem->len : 0;
@@ -239,7 +250,8 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     q.a_mode = A_ROWS; q.a = h; q.a_ld = D; q.a_bstride = h_bstride;
     q.b_mode = B_HEADS; q.b0 = p->Wq; q.b_split = q.cols; q.b_ld = D;
     q.dh = dh; q.dhp = dp; q.heads = H;
-    q.epi = EPI_QUV; q.c0 = ws + L.qu; q.c1 = ws + L.qv; q.u = p->u; q.v = p->v;
+    q.epi = EPI_QUV; q.c0 = ws + L.qu; q.c1 = ws + L.qv;
+    q.u = var ? nullptr : p->u; q.v = var ? nullptr : p->v;        // the variants have no u, v
     q.qscale = (float)(1.4426950408889634 / sqrt((double)dh));
     // K_E and V: of the context [mem; h], or of the segment rows into the cache
     GemmProblem &kv = g.p[1];
@@ -264,9 +276,9 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     r.b_mode = B_HEADS; r.b0 = p->WkR; r.b_split = r.cols; r.b_ld = D;
     r.dh = dh; r.dhp = dp; r.heads = H;
     r.epi = EPI_HEADS; r.c0 = ws + L.rk;
-    g.count = 3;
+    g.count = var ? 2 : 3;                                           // the variants need no R W_kR^T
     int t = 0;
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < g.count; ++i) {
         GemmProblem &P = g.p[i];
         P.tiles_n = (P.cols + 127) / 128;
         P.tile_begin = t;
@@ -275,9 +287,16 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     }
     g.total_tiles = t;
     TXL_TRY(hip_check(launch_gemm(bf, g, s), "projection GEMM launch"));
+    if (var && var->kind == TXL_POS_SHAW)
+        TXL_TRY(hip_check(launch_shaw_rows(bf, ws + L.rk, var->aK, var->clip, K, Kp, dh, dp, s),
+                          "distance table launch"));
 
     AttnArgs a;
+    memset(&a, 0, sizeof(a));
     a.qu = ws + L.qu; a.qv = ws + L.qv; a.rk = ws + L.rk;
+    a.rk_hstride = var ? 0 : (long long)(Kp + 2 * ATTN_RPAD) * dp;   // Shaw: one table for all heads
+    a.dist = !(var && var->kind == TXL_POS_ABSOLUTE);
+    a.lse = var && var->kind == TXL_POS_SHAW ? (float *)(ws + L.lse) : nullptr;
     a.ke = cache ? cache->k : (const void *)(ws + L.ke);
     a.vt = cache ? cache->vt : (const void *)(ws + L.vt);
     a.o = ws + L.o; a.o_bstride = (long long)W * D;
@@ -285,6 +304,7 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     a.C = cache ? cache->C : Kp;
     a.khead = cache ? cache->head : 0;
     TXL_TRY(hip_check(attn_launch(bf, a, s), "attention launch"));
+    if (a.lse) TXL_TRY(hip_check(launch_shaw_values(bf, a, var->aV, var->clip, s), "value-term launch"));
     return TXL_OK;
 }
 
@@ -361,8 +381,10 @@ extern "C" {
 size_t txl_workspace_bytes(txl_op op, txl_dtype dtype, int B, int W, int M, int D, int H, int F) {
     if (B < 1 || W < 1 || D < 2 || H < 1 || D % H || M < 0) return 0;
     if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
-    if (op != TXL_OP_REL_ATTN && op != TXL_OP_LAYER && op != TXL_OP_STACK && op != TXL_OP_REL_ATTN_CACHED) return 0;
-    const bool attn_only = op == TXL_OP_REL_ATTN || op == TXL_OP_REL_ATTN_CACHED;
+    if (op != TXL_OP_REL_ATTN && op != TXL_OP_LAYER && op != TXL_OP_STACK && op != TXL_OP_REL_ATTN_CACHED &&
+        op != TXL_OP_ATTN_VARIANT)
+        return 0;
+    const bool attn_only = op == TXL_OP_REL_ATTN || op == TXL_OP_REL_ATTN_CACHED || op == TXL_OP_ATTN_VARIANT;
     if (!attn_only && F < 1) return 0;
     return plan(op, dtype, B, W, M + W, D, H, attn_only ? 0 : F).total;
 }
@@ -496,6 +518,55 @@ txl_status txl_stack_fwd_window(txl_dtype dtype, int B, int W, int D, int H, int
         hin_bs = hout_bs;
     }
     return TXL_OK;
+}
+
+txl_status txl_attn_fwd_variant(txl_dtype dtype, txl_pos_variant variant, int B, int W, int D, int H,
+                                const void *h, long long h_bstride, const txl_mem *mem, const txl_layer_params *p,
+                                const void *aK, const void *aV, int clip, void *out, long long out_bstride,
+                                void *ws, size_t ws_bytes, void *stream) {
+    TXL_TRY(check_shape(dtype, B, W, D, H));
+    if (variant != TXL_POS_SHAW && variant != TXL_POS_ABSOLUTE)
+        return fail(TXL_ERR_ARG, "unknown encoding variant %d", (int)variant);
+    TXL_TRY(check_rows(h, h_bstride, W, D, dtype, "h"));
+    TXL_TRY(check_rows(out, out_bstride, W, D, dtype, "out"));
+    TXL_TRY(check_mem(mem, W));
+    if (!p) return fail(TXL_ERR_ARG, "params is NULL");
+    {
+        const void *ptrs[] = {p->Wq, p->WkE, p->Wv, p->Wo};
+        const char *names[] = {"Wq", "WkE", "Wv", "Wo"};
+        for (int i = 0; i < 4; ++i) {
+            if (!ptrs[i]) return fail(TXL_ERR_ARG, "parameter %s is NULL", names[i]);
+            if (!al4(ptrs[i])) return fail(TXL_ERR_ARG, "parameter %s must be 4-byte aligned", names[i]);
+        }
+    }
+    if (variant == TXL_POS_SHAW) {
+        if (clip < 0 || clip > shaw_max_clip())
+            return fail(TXL_ERR_UNSUPPORTED, "clip=%d must be in [0, %d]", clip, shaw_max_clip());
+        if (!aK || !aV || !al4(aK) || !al4(aV)) return fail(TXL_ERR_ARG, "aK and aV must be non-NULL and 4-byte aligned");
+    }
+    const int m = mem ? mem->len : 0;
+    TXL_TRY(check_rows_budget(B, W, m));
+    const Layout L = plan(TXL_OP_ATTN_VARIANT, dtype, B, W, (mem ? mem->M : 0) + W, D, H, 0);
+    if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+    if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    const Variant var = {variant, aK, aV, clip};
+    TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, mem, nullptr, p, nullptr, w, L, s, &var));
+    GemmProblem wo = rows_problem(B, W, D, D, w + L.o, D, (long long)W * D, p->Wo, out, D, out_bstride);
+    return hip_check(launch_gemm(dtype == TXL_BF16, single(wo), s), "output projection launch");
+}
+
+txl_status txl_add_positions(txl_dtype dtype, int B, int W, int D, const void *x, long long x_bstride, int pos0,
+                             void *y, long long y_bstride, void *stream) {
+    if (dtype != TXL_FP32 && dtype != TXL_BF16) return fail(TXL_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (B < 1 || W < 1 || D < 2 || D % 2) return fail(TXL_ERR_ARG, "need B, W >= 1 and an even D >= 2");
+    if (D > 1024) return fail(TXL_ERR_UNSUPPORTED, "positions support D <= 1024 (got %d)", D);
+    if (pos0 < 0) return fail(TXL_ERR_ARG, "pos0=%d must be >= 0", pos0);
+    TXL_TRY(check_rows(x, x_bstride, W, D, dtype, "x"));
+    TXL_TRY(check_rows(y, y_bstride, W, D, dtype, "y"));
+    return hip_check(launch_add_positions(dtype == TXL_BF16, x, x_bstride, y, y_bstride, B, W, D, pos0,
+                                          (hipStream_t)stream), "position launch");
 }
 
 int txl_kv_cache_capacity(int M, int W) {

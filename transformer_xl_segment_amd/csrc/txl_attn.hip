@@ -54,7 +54,7 @@ constexpr int kQB = 128;          // queries per workgroup (32 per wave)
 constexpr int kKB = 64;           // keys per block
 constexpr int kGPitch = 100;      // floats per query row of the distance buffer
 
-template <typename T, int DP>
+template <typename T, int DP, bool DIST>
 struct AttnSmem {
     static constexpr int NO = (DP + 31) / 32;                  // 32-row blocks of O^T
     static constexpr int kPitchK = DP * (int)sizeof(T) + 16;   // bytes per key row
@@ -62,7 +62,7 @@ struct AttnSmem {
     // 8-byte pad (34 dwords) spreads 32 lanes over distinct bank pairs; fp32
     // rows are read 16 bytes per lane and take a 16-byte pad
     static constexpr int kPitchV = kKB * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
-    float g[kWaves][32 * kGPitch];
+    float g[DIST ? kWaves : 1][DIST ? 32 * kGPitch : 4];
     char k[kKB * kPitchK];
     char v[NO * 32 * kPitchV];
 };
@@ -117,12 +117,15 @@ __device__ __forceinline__ float psum(const Frag<float> &f, float acc) {
 // bf16: two workgroups per CU when their LDS fits in the CU's 160 KB (two
 // waves per SIMD hide each other's latency). fp32 operands double the fragment
 // registers, so fp32 runs one workgroup per CU with the full register file.
-template <typename T, int DP>
-constexpr int attn_wgs_per_cu() { return sizeof(T) == 2 && 2 * sizeof(AttnSmem<T, DP>) <= 160 * 1024 ? 2 : 1; }
+template <typename T, int DP, bool DIST>
+constexpr int attn_wgs_per_cu() { return sizeof(T) == 2 && 2 * sizeof(AttnSmem<T, DP, DIST>) <= 160 * 1024 ? 2 : 1; }
 
-template <typename T, int DP>
-__global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kernel(const AttnArgs A) {
-    typedef AttnSmem<T, DP> SM;
+// MODE 0: the full score; 1: also writes the log-sum-exp of every query (for
+// a correction applied afterwards); 2: no distance term (content attention).
+template <typename T, int DP, int MODE>
+__global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) rel_attn_kernel(const AttnArgs A) {
+    constexpr bool DIST = MODE != 2;
+    typedef AttnSmem<T, DP, DIST> SM;
     constexpr int NS = DP / 16;
     constexpr int NO = SM::NO;
     __shared__ SM sm;
@@ -149,7 +152,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
     const T *ke = (const T *)A.ke + ((long long)bh * A.C) * DP;
     const T *vt = (const T *)A.vt + ((long long)bh * DP) * A.C;
     // row 0 of rk = distance 0; ATTN_RPAD zero rows on either side
-    const T *rk = (const T *)A.rk + ((long long)h * (A.Kp + 2 * ATTN_RPAD) + ATTN_RPAD) * DP;
+    const T *rk = (const T *)A.rk + (long long)h * A.rk_hstride + (long long)ATTN_RPAD * DP;
 
     // zero the V^T rows past DP once (they pad the last 32-row block of O^T)
     for (int idx = tid; idx < (NO * 32 - DP) * (SM::kPitchV / 4); idx += 256)
@@ -183,7 +186,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
         }
     };
 
-    float *grow = sm.g[w] + fr * kGPitch;
+    float *grow = sm.g[DIST ? w : 0] + (DIST ? fr * kGPitch : 0);
     f32x16 oacc[NO];
 #pragma unroll
     for (int o = 0; o < NO; ++o) oacc[o] = zero16();
@@ -198,7 +201,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
     // by two), so no register tile is copied from one step to the next.
     f32x16 gtop = zero16(), gb[2][2];
     Frag<T> rnext[2][NS];
-    if (wave_has_queries) {
+    if (DIST && wave_has_queries) {
         const int c0 = m + iw;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -275,18 +278,23 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
         if (!wave_has_queries || j0 > last_key_wave) return;
 
         // ---- shift the distance term into place through LDS
+        f32x16 sacc[2];
+        if constexpr (!DIST) {
+            sacc[0] = zero16();
+            sacc[1] = zero16();
+        } else {
         write_gblock(grow, gb[P][0], 0, hf);
         write_gblock(grow, gb[P][1], 32, hf);
         if (P == 1 || kb > 0) write_gblock(grow, gb[Q][0], 64, hf);
         wave_lds_sync();
         // key b = 32*sb + crow(i) of query a needs band offset a - b + 63
-        f32x16 sacc[2];
         {
             const float *rb = grow + fr - 4 * hf;
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[sb][i] = rb[63 - 32 * sb - 8 * (i >> 2) - (i & 3)];
+        }
         }
         // ---- content term on top: S^T += K (q+u)^T
 #pragma unroll
@@ -324,10 +332,12 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
             m_run = m_new;
         }
         // ---- next distance chunk (MFMA) interleaved with exp / pack / row sum (VALU)
-        g_chunk(gb[Q], rnext);
-        // prefetch for block kb+2 only while that block is still visible to the
-        // wave; this keeps every distance read >= -94 (inside the zero padding)
-        if (j0 + 2 * kKB <= last_key_wave) r_chunk(rnext, m + iw - j0 - kKB - 127);
+        if constexpr (DIST) {
+            g_chunk(gb[Q], rnext);
+            // prefetch for block kb+2 only while that block is still visible to the
+            // wave; this keeps every distance read >= -94 (inside the zero padding)
+            if (j0 + 2 * kKB <= last_key_wave) r_chunk(rnext, m + iw - j0 - kKB - 127);
+        }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -365,6 +375,8 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP>())) rel_attn_kern
     const float inv = 1.f / l_tot;
     const int qi = iw + fr;
     if (qi >= A.W) return;
+    // log2 of the softmax denominator in the pre-scaled score units
+    if (MODE == 1 && hf == 0) A.lse[(long long)bh * A.Wp + qi] = m_run + log2f(l_tot);
     T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.D + h * A.dh;
 #pragma unroll
     for (int o = 0; o < NO; ++o)
@@ -381,7 +393,12 @@ template <typename T, int DP>
 hipError_t launch_dp(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const int nqb = (a.W + kQB - 1) / kQB;
     dim3 grid(a.B * a.H * nqb), block(256);
-    hipExtLaunchKernelGGL((rel_attn_kernel<T, DP>), grid, block, 0, s, start, stop, 0, a);
+    if (!a.dist)
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 2>), grid, block, 0, s, start, stop, 0, a);
+    else if (a.lse)
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 1>), grid, block, 0, s, start, stop, 0, a);
+    else
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 0>), grid, block, 0, s, start, stop, 0, a);
     return hipGetLastError();
 }
 

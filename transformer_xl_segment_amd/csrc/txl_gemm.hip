@@ -163,7 +163,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
             if (P.epi == EPI_KV && n >= P.b_split) { nn = n - P.b_split; second = true; }
             hh = nn / P.dhp;                           // the 8 columns share one head (dhp % 16 == 0)
             c = nn - hh * P.dhp;
-            if (P.epi == EPI_QUV)
+            if (P.epi == EPI_QUV && P.u)      // u, v null: both biases zero
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     if (c + i < P.dh) {

@@ -27,6 +27,7 @@ enum BColMode {
 enum EpiMode {
     EPI_ROWS = 0,    // dst = c0 + b*c_bstride + t*c_ld + n (+bias[n], relu, +residual), T or fp32
     EPI_QUV = 1,     // c0 = (acc + u) * qscale, c1 = (acc + v) * qscale, head-major [b][hh][t][c]
+                     // (u and v both null: no biases)
     EPI_KV = 2,      // n < b_split: c0 head-major [b][hh][slot][c]; else c1 transposed [b][hh][c][slot],
                      // slot = (kv_base + t) mod kv_slots
     EPI_HEADS = 3,   // c0 head-major [b][hh][t][c]
@@ -82,9 +83,13 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p);
 //   ke      [B][H][C][dp]   content keys; key j lives in slot (khead + j) mod C
 //   vt      [B][H][dp][C]   values, transposed, same slots (khead and C multiples
 //                           of 8, C >= Kp)
-//   rk      [H][ATTN_RPAD + Kp + ATTN_RPAD][dp]  distance keys; row ATTN_RPAD + d holds
+//   rk      [H][ATTN_RPAD + Kp + ATTN_RPAD][dp]  distance keys, head stride rk_hstride
+//           elements (0: one table shared by every head); row ATTN_RPAD + d holds
 //           distance d for 0 <= d < K and zeros elsewhere, so reads of distances in
 //           [-ATTN_RPAD, Kp + ATTN_RPAD) need no bounds checks
+//   dist    0: no distance term (content attention; rk unused)
+//   lse     optional [B][H][Wp] fp32: per query, log2 of the softmax denominator
+//           in the pre-scaled score units (max + log2(sum))
 //   o       [B][W][D]       output rows (heads concatenated), batch stride o_bstride
 // Rows past W (queries) hold zeros; key slots past K hold finite values (they
 // are masked).
@@ -95,6 +100,9 @@ struct AttnArgs {
     long long o_bstride;
     int B, H, W, Wp, m, K, Kp, dh, dp, D;
     int C, khead;
+    long long rk_hstride;
+    int dist;
+    float *lse;
 };
 // start / stop: optional events stamped at this kernel's own start and end.
 hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s, hipEvent_t start = nullptr,
@@ -104,6 +112,16 @@ int attn_dp(int dh);          // padded head width used by the attention kernel
 const int ATTN_QBLOCK = 128;  // queries per workgroup
 const int ATTN_KBLOCK = 64;   // keys per step
 const int ATTN_RPAD = 128;    // zero rows before and after the distance keys
+
+// Encoding variants (txl_variants.hip).
+int shaw_max_clip();
+// Shaw's distance keys: one table [ATTN_RPAD + Kp + ATTN_RPAD][dp], row ATTN_RPAD + d = aK[min(d, clip)]
+hipError_t launch_shaw_rows(bool is_bf16, void *rk, const void *aK, int clip, int K, int Kp, int dh, int dp,
+                            hipStream_t s);
+// Shaw's value term added to a.o, from a.qu, a.qv, a.ke, a.rk and a.lse of a finished attention launch
+hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aV, int clip, hipStream_t s);
+hipError_t launch_add_positions(bool is_bf16, const void *x, long long x_bstride, void *y, long long y_bstride,
+                                int B, int W, int D, int pos0, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Small kernels.
