@@ -59,9 +59,10 @@ def lib() -> ctypes.CDLL:
                                     + [_dp, ctypes.c_int, _dp, _dp, _ip])
         L.orc_attn_variant.argtypes = [ctypes.c_int] * 6 + [_dp] * 8 + [ctypes.c_int, _dp]
         L.orc_add_positions.argtypes = [ctypes.c_int] * 4 + [_dp, _dp]
+        L.orc_rel_attn_bwd.argtypes = [ctypes.c_int] * 5 + [_dp] * 13
         for f in ("orc_sinusoid_table", "orc_linear", "orc_layer_norm", "orc_rel_attn",
                   "orc_layer_fwd", "orc_mem_update", "orc_stack_fwd", "orc_attn_variant",
-                  "orc_add_positions"):
+                  "orc_add_positions", "orc_rel_attn_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -161,6 +162,22 @@ def attn_variant(mode: int, h: np.ndarray, mem: Optional[np.ndarray], p: Dict[st
     st = lib().orc_attn_variant(mode, B, W, D, H, m, _ptr(h), _ptr(memf), *[_ptr(a) for a in ps],
                                 _ptr(ak), _ptr(av), clip, _ptr(out))
     _check(st, "attn_variant")
+    return out
+
+
+def rel_attn_bwd(q: np.ndarray, k: np.ndarray, val: np.ndarray, r: np.ndarray, u: np.ndarray, v: np.ndarray,
+                 dO: np.ndarray, H: int) -> Dict[str, np.ndarray]:
+    """Gradients of relative attention (before W_o) w.r.t. its projected operands,
+    memory behind a stop-gradient. q, dO [B, W, D]; k, val [B, K, D] (memory rows
+    first, K = m + W); r [K, D]; u, v [D]. Returns dq, dk, dval, dr, du, dv."""
+    q, k, val, r, u, v, dO = (_f64(a) for a in (q, k, val, r, u, v, dO))
+    B, W, D = q.shape
+    K = k.shape[1]
+    out = {"dq": np.empty((B, W, D)), "dk": np.empty((B, K, D)), "dval": np.empty((B, K, D)),
+           "dr": np.empty((K, D)), "du": np.empty(D), "dv": np.empty(D)}
+    st = lib().orc_rel_attn_bwd(B, W, D, H, K - W, _ptr(q), _ptr(k), _ptr(val), _ptr(r), _ptr(u), _ptr(v),
+                                _ptr(dO), *[_ptr(out[n]) for n in ("dq", "dk", "dval", "dr", "du", "dv")])
+    _check(st, "rel_attn_bwd")
     return out
 
 

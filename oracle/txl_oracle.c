@@ -316,6 +316,110 @@ int orc_attn_variant(int mode, int B, int W, int D, int H, int m,
     return ORC_OK;
 }
 
+/*
+ * Gradients of relative attention with the memory behind a stop-gradient
+ * ([XL] step 2 and the SG(.) legend entry: the cached states are a fixed input
+ * and backpropagation stays inside the current segment). Inputs are the
+ * projected operands of one segment:
+ *   q    [B][W][D]   queries h W_q^T
+ *   k    [B][K][D]   content keys of [mem; h] (K = m + W, memory rows first)
+ *   val  [B][K][D]   values of [mem; h]
+ *   r    [K][D]      distance keys R W_kR^T for distances 0 .. K-1
+ *   u, v [D]
+ *   dO   [B][W][D]   gradient of the loss w.r.t. the attention output o
+ *                    (heads concatenated, before W_o)
+ * with score_ij = ((q_i + u).k_j + (q_i + v).r_{m+i-j}) / sqrt(dh), causal, and
+ * o_i = sum_j p_ij val_j. Outputs dq [B][W][D], dk, dval [B][K][D], dr [K][D],
+ * du, dv [D]: the gradients w.r.t. these operands. Rows j < m of dk and dval
+ * belong to the memory's projections (they reach W_kE and W_v); the memory
+ * rows themselves are inputs and get no gradient. Per query:
+ *   D_i = dO_i . o_i,  dP_ij = dO_i . val_j,  dS_ij = p_ij (dP_ij - D_i)
+ *   dq_i += dS_ij (k_j + r_delta) / sqrt(dh),  dk_j += dS_ij (q_i + u) / sqrt(dh)
+ *   dval_j += p_ij dO_i,  dr_delta += dS_ij (q_i + v) / sqrt(dh)
+ *   du += dS_ij k_j / sqrt(dh),  dv += dS_ij r_delta / sqrt(dh)
+ * (the softmax Jacobian applied to dP, then the product rule on each score term).
+ * Heads are independent and write disjoint columns, so OpenMP splits heads;
+ * within a head every sum runs in (b, i, j) order.
+ */
+int orc_rel_attn_bwd(int B, int W, int D, int H, int m,
+                     const double *q, const double *k, const double *val, const double *r,
+                     const double *u, const double *v, const double *dO,
+                     double *dq, double *dk, double *dval, double *dr, double *du, double *dv)
+{
+    if (B < 1 || W < 1 || D < 1 || H < 1 || D % H != 0 || m < 0) return ORC_ERR_ARG;
+    if (!q || !k || !val || !r || !u || !v || !dO || !dq || !dk || !dval || !dr || !du || !dv)
+        return ORC_ERR_ARG;
+    const int K = m + W;
+    const int dh = D / H;
+    const double c = 1.0 / sqrt((double)dh);
+    memset(dq, 0, sizeof(double) * (size_t)B * W * D);
+    memset(dk, 0, sizeof(double) * (size_t)B * K * D);
+    memset(dval, 0, sizeof(double) * (size_t)B * K * D);
+    memset(dr, 0, sizeof(double) * (size_t)K * D);
+    memset(du, 0, sizeof(double) * (size_t)D);
+    memset(dv, 0, sizeof(double) * (size_t)D);
+
+#pragma omp parallel for schedule(dynamic)
+    for (int hd = 0; hd < H; ++hd) {
+        const int c0 = hd * dh;
+        double *p = malloc(sizeof(double) * K);
+        double *ds = malloc(sizeof(double) * K);
+        for (int b = 0; b < B; ++b) {
+            for (int i = 0; i < W; ++i) {
+                const double *qi = q + ((size_t)b * W + i) * D + c0;
+                const double *gi = dO + ((size_t)b * W + i) * D + c0;
+                const int last = m + i;
+                /* forward probabilities of this query */
+                double smax = -INFINITY;
+                for (int j = 0; j <= last; ++j) {
+                    const double *kj = k + ((size_t)b * K + j) * D + c0;
+                    const double *rd = r + (size_t)(m + i - j) * D + c0;
+                    double sc = 0.0;
+                    for (int t = 0; t < dh; ++t) sc += (qi[t] + u[c0 + t]) * kj[t] + (qi[t] + v[c0 + t]) * rd[t];
+                    p[j] = sc * c;
+                    if (p[j] > smax) smax = p[j];
+                }
+                double den = 0.0;
+                for (int j = 0; j <= last; ++j) { p[j] = exp(p[j] - smax); den += p[j]; }
+                for (int j = 0; j <= last; ++j) p[j] /= den;
+                /* D_i = dO_i . o_i with o_i = sum_j p_ij val_j */
+                double Di = 0.0;
+                for (int t = 0; t < dh; ++t) {
+                    double o = 0.0;
+                    for (int j = 0; j <= last; ++j) o += p[j] * val[((size_t)b * K + j) * D + c0 + t];
+                    Di += gi[t] * o;
+                }
+                for (int j = 0; j <= last; ++j) {
+                    const double *vj = val + ((size_t)b * K + j) * D + c0;
+                    double dp = 0.0;
+                    for (int t = 0; t < dh; ++t) dp += gi[t] * vj[t];
+                    ds[j] = p[j] * (dp - Di);
+                }
+                for (int j = 0; j <= last; ++j) {
+                    const int delta = m + i - j;
+                    const double *kj = k + ((size_t)b * K + j) * D + c0;
+                    const double *rd = r + (size_t)delta * D + c0;
+                    double *dqi = dq + ((size_t)b * W + i) * D + c0;
+                    double *dkj = dk + ((size_t)b * K + j) * D + c0;
+                    double *dvj = dval + ((size_t)b * K + j) * D + c0;
+                    double *drd = dr + (size_t)delta * D + c0;
+                    for (int t = 0; t < dh; ++t) {
+                        dqi[t] += ds[j] * (kj[t] + rd[t]) * c;
+                        dkj[t] += ds[j] * (qi[t] + u[c0 + t]) * c;
+                        dvj[t] += p[j] * gi[t];
+                        drd[t] += ds[j] * (qi[t] + v[c0 + t]) * c;
+                        du[c0 + t] += ds[j] * kj[t] * c;
+                        dv[c0 + t] += ds[j] * rd[t] * c;
+                    }
+                }
+            }
+        }
+        free(p);
+        free(ds);
+    }
+    return ORC_OK;
+}
+
 /* Absolute positions of the ablation ([XL] results: absolute encodings with
  * recurrence): y[b][t] = x[b][t] + U[pos0 + t], U the sinusoid of orc_sinusoid_table
  * evaluated at the absolute position instead of a distance. */

@@ -502,6 +502,80 @@ def test_absolute_positions_closed_forms():
         np.testing.assert_allclose(U[:, :, D - 1], np.broadcast_to(np.cos(t * f), (B, W)), atol=1e-13)
 
 
+# --------------------------------------------------------------------------
+# Backward pass with the memory behind a stop-gradient.
+# --------------------------------------------------------------------------
+
+def _bwd_case(seed, B=2, W=3, m=2, D=8, H=2, scale=0.5):
+    rng = np.random.default_rng(seed)
+    p = {n: a.astype(np.float64) for n, a in _params(rng, D, scale=scale).items()}
+    p["Wo"] = np.eye(D)                      # the loss reads the attention output o itself
+    h = rng.standard_normal((B, W, D))
+    mem = rng.standard_normal((B, m, D)) if m > 0 else None
+    dO = rng.standard_normal((B, W, D))
+    return p, h, mem, _R(m + W, D), dO
+
+
+def _bwd_through_projections(p, h, mem, R, dO, H):
+    """Gradients of L = sum(dO * o) w.r.t. the weights, u, v and the segment rows,
+    from the backward oracle and the chain rule through the linear projections."""
+    m = 0 if mem is None else mem.shape[1]
+    ctx = h if mem is None else np.concatenate([mem, h], axis=1)
+    K = ctx.shape[1]
+    q, k, val, r = h @ p["Wq"].T, ctx @ p["WkE"].T, ctx @ p["Wv"].T, R[:K] @ p["WkR"].T
+    g = orc.rel_attn_bwd(q, k, val, r, p["u"], p["v"], dO, H)
+    return {
+        "Wq": np.einsum("bto,bti->oi", g["dq"], h),
+        "WkE": np.einsum("bjo,bji->oi", g["dk"], ctx),      # memory rows included
+        "Wv": np.einsum("bjo,bji->oi", g["dval"], ctx),
+        "WkR": g["dr"].T @ R[:K],
+        "u": g["du"], "v": g["dv"],
+        "h": g["dq"] @ p["Wq"] + g["dk"][:, m:] @ p["WkE"] + g["dval"][:, m:] @ p["Wv"],
+    }
+
+
+@pytest.mark.parametrize("m", [0, 2, 5])
+def test_backward_matches_finite_differences(m):
+    # central differences of the (separately pinned) forward oracle, in fp64;
+    # the memory is held fixed (stop-gradient), every other input is perturbed
+    H = 2
+    p, h, mem, R, dO = _bwd_case(31 + m, m=m)
+    grads = _bwd_through_projections(p, h, mem, R, dO, H)
+
+    def loss(pp, hh):
+        return float(np.sum(dO * orc.rel_attn(hh, mem, pp, R, H)))
+
+    eps = 1e-5
+    for name in ("Wq", "WkE", "Wv", "WkR", "u", "v", "h"):
+        base = h if name == "h" else p[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            if name == "h":
+                fd[idx] = (loss(p, plus) - loss(p, minus)) / (2 * eps)
+            else:
+                fd[idx] = (loss({**p, name: plus}, h) - loss({**p, name: minus}, h)) / (2 * eps)
+        np.testing.assert_allclose(grads[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_single_key_closed_form():
+    # the first query of a segment with no memory sees only itself: p = 1, so
+    # its score gradient vanishes (dq_0 = 0) and its value gets dO_0 exactly
+    B, W, D, H = 2, 4, 8, 2
+    rng = np.random.default_rng(33)
+    q, dO = rng.standard_normal((B, W, D)), rng.standard_normal((B, W, D))
+    k, val = rng.standard_normal((B, W, D)), rng.standard_normal((B, W, D))
+    r, u, v = rng.standard_normal((W, D)), rng.standard_normal(D), rng.standard_normal(D)
+    g = orc.rel_attn_bwd(q, k, val, r, u, v, dO, H)
+    assert np.all(g["dq"][:, 0] == 0.0)
+    # key W-1 is seen only by the last query (weight p), the first key by all
+    o_last = orc.rel_attn_bwd(q, k, val, r, u, v, np.zeros_like(dO), H)
+    assert all(np.all(o_last[n] == 0.0) for n in o_last)          # linear in dO
+    assert np.all(np.abs(g["dval"][:, 0]) > 0)
+
+
 def test_bad_arguments_are_rejected():
     p, h, mem, R = _attn_case()
     with pytest.raises(ValueError):
