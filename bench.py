@@ -17,7 +17,8 @@ keys and values (txl_rel_attn_fwd_cached), reported under "kv_cache". Then
 which re-encodes a window of the last M + W tokens from scratch for every new
 token, on the long-memory attention workload and on the 16-layer stack.
 "encodings" times the same step with the encodings the pages compare against
-(Shaw et al.'s clipped embeddings, absolute positions).
+(Shaw et al.'s clipped embeddings, absolute positions), and "backward" the
+attention backward (txl_rel_attn_bwd) at the same shape.
 """
 from __future__ import annotations
 
@@ -119,6 +120,29 @@ def time_encodings(tb, torch, segs, params, B, M, W, D, H, out, steps, warmup):
         el = _timed(torch, step, steps, warmup + (M + W - 1) // W)
         res[name] = {"value": B * W * steps / el, "unit": "tokens/s", "ms_per_step": el * 1e3 / steps}
     return res
+
+
+def bwd_flops(B, H, dh, W, m):
+    """Algorithmic flops of the attention backward: per causally visible pair,
+    the two score terms recomputed (4 dh), dP (2 dh), dq from both terms (4 dh),
+    dk, dval and dr (2 dh each)."""
+    pairs = W * m + W * (W + 1) // 2
+    return 16.0 * dh * H * B * pairs
+
+
+def time_backward(tb, torch, B, W, M, D, H, dev, steps):
+    bf = torch.bfloat16
+    g = torch.Generator().manual_seed(7)
+    K = M + W
+    mk = lambda *shape, s=0.5: (torch.randn(*shape, generator=g) * s).to(dev).to(bf)
+    q, k, val, r, u, v, dO = mk(B, W, D), mk(B, K, D), mk(B, K, D, s=1.0), mk(K, D), mk(D), mk(D), mk(B, W, D, s=1.0)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN_BWD, bf, B, W, M, D, H), dtype=torch.uint8, device=dev)
+    el = _timed(torch, lambda i: tb.rel_attn_bwd(q, k, val, r, u, v, dO, H, workspace=ws), steps)
+    ms = el * 1e3 / steps
+    fl = bwd_flops(B, H, D // H, W, M)
+    return {"ms_per_call": ms, "tokens_per_s": B * W / (ms * 1e-3), "algorithmic_tflops": fl / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, "workspace_bytes": ws.numel(),
+            "call": "txl_rel_attn_bwd, B=16, W=m=512, D=512, H=8 (all gradients of the projected operands)"}
 
 
 def _timed(torch, fn, calls, warm=2):
@@ -329,6 +353,7 @@ def main():
     kv["speedup_vs_row_memory"] = kv["value"] / rec["value"]
     rec["kv_cache"] = kv
     rec["encodings"] = time_encodings(tb, torch, segs, params, B, M, W, D, H, out, args.steps, args.warmup)
+    rec["backward"] = time_backward(tb, torch, B, W, M, D, H, dev, max(5, args.steps // 10))
     if not args.no_sliding_window:
         del ring, ws
         rec["sliding_window"] = sliding_window(tb, torch, syn, dev)

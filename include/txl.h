@@ -72,7 +72,8 @@ typedef enum {
     TXL_OP_LAYER = 1,         /* txl_layer_fwd */
     TXL_OP_STACK = 2,         /* txl_stack_fwd_segments */
     TXL_OP_REL_ATTN_CACHED = 3, /* txl_rel_attn_fwd_cached */
-    TXL_OP_ATTN_VARIANT = 4   /* txl_attn_fwd_variant */
+    TXL_OP_ATTN_VARIANT = 4,  /* txl_attn_fwd_variant */
+    TXL_OP_REL_ATTN_BWD = 5   /* txl_rel_attn_bwd (M = the memory length m) */
 } txl_op;
 
 /* Position encodings Transformer-XL is compared against ("Transformer-XL,
@@ -233,6 +234,29 @@ txl_status txl_attn_fwd_variant(txl_dtype dtype, txl_pos_variant variant, int B,
                                 const void *aK, const void *aV, int clip,
                                 void *out, long long out_bstride,
                                 void *ws, size_t ws_bytes, void *stream);
+
+/* Backward pass of the relative attention with the memory behind a
+ * stop-gradient ("Transformer-XL, explained.", method step 2 and the SG(.)
+ * legend entry: the cached states are a fixed input, backpropagation stays in
+ * the current segment). Inputs are the projected operands of one segment, in
+ * the call's dtype, rows contiguous:
+ *   q, dO  [B][W][D]   queries h W_q^T; gradient of the loss w.r.t. the attention
+ *                      output o (heads concatenated, before W_o)
+ *   k, val [B][K][D]   content keys and values of [mem; h], K = m + W, memory first
+ *   r      [K][D]      distance keys R W_kR^T for distances 0 .. K-1
+ *   u, v   [D]
+ * with score_ij = ((q_i+u).k_j + (q_i+v).r_{m+i-j}) / sqrt(dh), causal, and
+ * o_i = sum_j softmax_j(score_ij) val_j. Outputs, fp32, rows contiguous: dq
+ * [B][W][D], dk and dval [B][K][D], dr [K][D], du and dv [D], the gradients
+ * w.r.t. these operands. Rows j < m of dk and dval belong to the memory's
+ * projections (they reach W_kE and W_v); nothing is propagated into the memory
+ * rows themselves. m + W <= 4096, D/H <= 64. Workspace:
+ * txl_workspace_bytes(TXL_OP_REL_ATTN_BWD, dtype, B, W, m, D, H, 0). */
+txl_status txl_rel_attn_bwd(txl_dtype dtype, int B, int W, int D, int H, int m,
+                            const void *q, const void *k, const void *val, const void *r,
+                            const void *u, const void *v, const void *dO,
+                            float *dq, float *dk, float *dval, float *dr, float *du, float *dv,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /* Absolute positions for the comparison model: y[b][t] = x[b][t] + U[pos0 + t]
  * for t < W, U[p][k] = sin(p * 10000^(-2k/D)) and U[p][D/2 + k] = cos(...), the

@@ -179,6 +179,23 @@ def test_variants_reject_bad_arguments():
     assert L.txl_add_positions(7, 1, 4, 16, FAKE, 64, 0, FAKE, 64, None) == tb.TXL_ERR_UNSUPPORTED
 
 
+def test_backward_rejects_bad_arguments():
+    L = tb.lib()
+    def bwd(m=2, W=4, D=16, H=2, ins=None, outs=None, wsb=0):
+        ins = ins or [FAKE] * 7
+        outs = outs or [FAKE] * 6
+        return L.txl_rel_attn_bwd(tb.TXL_FP32, 1, W, D, H, m, *ins, *outs, None, wsb, None)
+    assert bwd(m=-1) == tb.TXL_ERR_ARG
+    assert bwd(m=4090, W=8) == tb.TXL_ERR_UNSUPPORTED              # m + W > 4096
+    assert bwd(D=130, H=1) == tb.TXL_ERR_UNSUPPORTED               # dh > 64
+    assert bwd(ins=[FAKE] * 6 + [None]) == tb.TXL_ERR_ARG          # dO
+    assert bwd(outs=[FAKE + 2] + [FAKE] * 5) == tb.TXL_ERR_ARG     # misaligned dq
+    assert bwd() == tb.TXL_ERR_WORKSPACE
+    ws = L.txl_workspace_bytes(tb.OP_REL_ATTN_BWD, tb.TXL_BF16, 2, 64, 64, 128, 2, 0)
+    assert ws > L.txl_workspace_bytes(tb.OP_REL_ATTN, tb.TXL_BF16, 2, 64, 64, 128, 2, 0)
+    assert L.txl_workspace_bytes(tb.OP_REL_ATTN_BWD, tb.TXL_BF16, 1, 64, 4096, 128, 2, 0) == 0
+
+
 def test_kv_cache_capacity_and_workspace():
     L = tb.lib()
     assert L.txl_kv_cache_capacity(512, 512) == 1024

@@ -23,7 +23,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "txl.h")
 
 TXL_OK, TXL_ERR_ARG, TXL_ERR_UNSUPPORTED, TXL_ERR_WORKSPACE, TXL_ERR_HIP = range(5)
 TXL_FP32, TXL_BF16 = 0, 1
-OP_REL_ATTN, OP_LAYER, OP_STACK, OP_REL_ATTN_CACHED, OP_ATTN_VARIANT = 0, 1, 2, 3, 4
+OP_REL_ATTN, OP_LAYER, OP_STACK, OP_REL_ATTN_CACHED, OP_ATTN_VARIANT, OP_REL_ATTN_BWD = 0, 1, 2, 3, 4, 5
 POS_SHAW, POS_ABSOLUTE = 1, 2
 
 _PARAM_FIELDS = ("Wq", "WkE", "WkR", "Wv", "Wo", "u", "v", "ln1_g", "ln1_b", "W1", "b1",
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.txl_stack_fwd_segments.argtypes = [i, i, i, i, i, i, i, i, vp, Mp, P, vp, i, vp, vp, sz, vp]
         L.txl_attn_fwd_variant.argtypes = [i, i, i, i, i, i, vp, ll, Mp, P, vp, vp, i, vp, ll, vp, sz, vp]
         L.txl_add_positions.argtypes = [i, i, i, i, vp, ll, i, vp, ll, vp]
+        L.txl_rel_attn_bwd.argtypes = [i, i, i, i, i, i] + [vp] * 7 + [vp] * 6 + [vp, sz, vp]
         L.txl_stack_fwd_window.argtypes = [i, i, i, i, i, i, i, vp, ll, P, vp, i, vp, ll, vp, sz, vp]
         KVp = ctypes.POINTER(_KV)
         L.txl_kv_cache_capacity.argtypes = [i, i]
@@ -81,7 +82,7 @@ def lib() -> ctypes.CDLL:
         L.txl_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_mem_update", "txl_layer_fwd",
                   "txl_stack_fwd_segments", "txl_stack_fwd_window", "txl_kv_cache_capacity",
-                  "txl_attn_fwd_variant", "txl_add_positions", "txl_kv_cache_append",
+                  "txl_attn_fwd_variant", "txl_add_positions", "txl_rel_attn_bwd", "txl_kv_cache_append",
                   "txl_rel_attn_fwd_cached", "txl_profile_begin", "txl_profile_end"):
             getattr(L, f).restype = i
         L.txl_status_string.argtypes = [i]
@@ -305,6 +306,27 @@ def add_positions(x: torch.Tensor, pos0: int = 0, y: Optional[torch.Tensor] = No
     _check(lib().txl_add_positions(dtype_code(x.dtype), B, W, D, x.data_ptr(), xs, pos0, y.data_ptr(), ys,
                                    _stream(x.device)), "txl_add_positions")
     return y
+
+
+def rel_attn_bwd(q: torch.Tensor, k: torch.Tensor, val: torch.Tensor, r: torch.Tensor, u: torch.Tensor,
+                 v: torch.Tensor, dO: torch.Tensor, H: int,
+                 workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Gradients (fp32) of relative attention w.r.t. its projected operands, the
+    memory behind a stop-gradient: q, dO [B, W, D]; k, val [B, K, D]; r [>=K, D]."""
+    B, W, D = q.shape
+    K = k.shape[1]
+    ins = [t.contiguous() for t in (q, k, val, r, u, v, dO)]
+    dev = q.device
+    f32 = torch.float32
+    out = {"dq": torch.empty(B, W, D, dtype=f32, device=dev), "dk": torch.empty(B, K, D, dtype=f32, device=dev),
+           "dval": torch.empty(B, K, D, dtype=f32, device=dev), "dr": torch.empty(K, D, dtype=f32, device=dev),
+           "du": torch.empty(D, dtype=f32, device=dev), "dv": torch.empty(D, dtype=f32, device=dev)}
+    ws = _workspace(workspace_bytes(OP_REL_ATTN_BWD, q.dtype, B, W, K - W, D, H), dev, workspace)
+    _check(lib().txl_rel_attn_bwd(dtype_code(q.dtype), B, W, D, H, K - W, *[t.data_ptr() for t in ins],
+                                  *[out[n].data_ptr() for n in ("dq", "dk", "dval", "dr", "du", "dv")],
+                                  ws.data_ptr(), ws.numel() * ws.element_size(), _stream(dev)),
+           "txl_rel_attn_bwd")
+    return out
 
 
 def mem_update(mem: MemoryRing, h: torch.Tensor) -> None:

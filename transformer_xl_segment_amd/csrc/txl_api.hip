@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -374,6 +375,46 @@ txl_status enqueue_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const vo
     return TXL_OK;
 }
 
+// Workspace of the backward pass (one region per operand, 256-byte aligned).
+struct BwdLayout {
+    size_t qu, qv, dOh, ke, vk, rk, ket, rkt, qut, dOt, qvt;   // T operands
+    size_t p, ds, dsd, pt, dst, dsdt;                          // T, per-(b, h) score matrices
+    size_t ac, bd, dpm, dq1, dq2, dkh, dvh, drh, part;         // fp32
+    size_t total;
+    BwdDims d;
+};
+
+BwdLayout plan_bwd(txl_dtype dt, int B, int W, int m, int D, int H) {
+    BwdLayout L;
+    memset(&L, 0, sizeof(L));
+    const size_t es = es_of(dt);
+    BwdDims &d = L.d;
+    d.B = B; d.H = H; d.W = W; d.m = m; d.K = m + W; d.D = D; d.dh = D / H;
+    d.dp = attn_dp(d.dh);
+    d.Wp = (int)round_up(W, 128);          // GEMM tiles never straddle two (b, h) entries
+    d.Kp = (int)round_up(d.K, 128);
+    const size_t G = (size_t)B * H;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = (size_t)round_up((long long)(off + bytes), 256);
+        return at;
+    };
+    const size_t qb = G * d.Wp * d.dp * es, kb = G * d.Kp * d.dp * es, sb = G * d.Wp * d.Kp;
+    L.qu = take(qb); L.qv = take(qb); L.dOh = take(qb);
+    L.ke = take(kb); L.vk = take(kb); L.rk = take(kb); L.ket = take(kb); L.rkt = take(kb);
+    L.qut = take(qb); L.dOt = take(qb); L.qvt = take(qb);
+    L.p = take(sb * es); L.ds = take(sb * es); L.dsd = take(sb * es);
+    L.pt = take(sb * es); L.dst = take(sb * es); L.dsdt = take(sb * es);
+    L.ac = take(sb * 4); L.bd = take(sb * 4); L.dpm = take(sb * 4);
+    L.dq1 = take(G * d.Wp * d.dp * 4); L.dq2 = take(G * d.Wp * d.dp * 4);
+    L.dkh = take(G * d.Kp * d.dp * 4); L.dvh = take(G * d.Kp * d.dp * 4);
+    L.drh = take((size_t)H * d.Kp * d.dp * 4);
+    L.part = take((size_t)2 * H * bwd_bias_chunks(d) * 64 * 4);
+    L.total = off;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -381,6 +422,7 @@ extern "C" {
 size_t txl_workspace_bytes(txl_op op, txl_dtype dtype, int B, int W, int M, int D, int H, int F) {
     if (B < 1 || W < 1 || D < 2 || H < 1 || D % H || M < 0) return 0;
     if (dtype != TXL_FP32 && dtype != TXL_BF16) return 0;
+    if (op == TXL_OP_REL_ATTN_BWD) return M + W > 4096 ? 0 : plan_bwd(dtype, B, W, M, D, H).total;
     if (op != TXL_OP_REL_ATTN && op != TXL_OP_LAYER && op != TXL_OP_STACK && op != TXL_OP_REL_ATTN_CACHED &&
         op != TXL_OP_ATTN_VARIANT)
         return 0;
@@ -567,6 +609,109 @@ txl_status txl_add_positions(txl_dtype dtype, int B, int W, int D, const void *x
     TXL_TRY(check_rows(y, y_bstride, W, D, dtype, "y"));
     return hip_check(launch_add_positions(dtype == TXL_BF16, x, x_bstride, y, y_bstride, B, W, D, pos0,
                                           (hipStream_t)stream), "position launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// C[e] = A[e] B[e]^T for batch entries e (A [rows][kdim] with row stride a_ld,
+// B [cols][kdim]), fp32 output [rows][cols] per entry.
+GemmProblem batched_problem(int entries, int rows, int cols, int kdim, const void *a, long long a_ld,
+                            const void *b, long long b_ld, void *c) {
+    GemmProblem p;
+    memset(&p, 0, sizeof(p));
+    p.rows = entries * rows; p.cols = cols; p.kdim = kdim;
+    p.seg_rows = rows; p.valid_rows = rows;
+    p.a_mode = A_ROWS; p.a = a; p.a_ld = a_ld; p.a_bstride = (long long)rows * a_ld;
+    p.b_mode = B_ROWS; p.b0 = b; p.b_split = cols; p.b_ld = b_ld; p.b_bstride = (long long)cols * b_ld;
+    p.dh = 1; p.dhp = 1; p.heads = 1;
+    p.epi = EPI_ROWS; p.c0 = c; p.c_ld = cols; p.c_bstride = (long long)rows * cols; p.out_f32 = 1;
+    return p;
+}
+
+GemmLaunch grouped(std::initializer_list<GemmProblem> ps) {
+    GemmLaunch g;
+    memset(&g, 0, sizeof(g));
+    int t = 0;
+    for (const GemmProblem &p0 : ps) {
+        GemmProblem &P = g.p[g.count++];
+        P = p0;
+        P.tiles_n = (P.cols + 127) / 128;
+        P.tile_begin = t;
+        P.tile_count = ((P.rows + 127) / 128) * P.tiles_n;
+        t += P.tile_count;
+    }
+    g.total_tiles = t;
+    return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+txl_status txl_rel_attn_bwd(txl_dtype dtype, int B, int W, int D, int H, int m, const void *q, const void *k,
+                            const void *val, const void *r, const void *u, const void *v, const void *dO,
+                            float *dq, float *dk, float *dval, float *dr, float *du, float *dv, void *ws,
+                            size_t ws_bytes, void *stream) {
+    TXL_TRY(check_shape(dtype, B, W, D, H));
+    if (m < 0) return fail(TXL_ERR_ARG, "m=%d must be >= 0", m);
+    if ((long long)m + W > 4096) return fail(TXL_ERR_UNSUPPORTED, "the backward supports m + W <= 4096");
+    const void *ins[] = {q, k, val, r, u, v, dO};
+    const char *in_names[] = {"q", "k", "val", "r", "u", "v", "dO"};
+    for (int i = 0; i < 7; ++i)
+        if (!ins[i] || !al4(ins[i])) return fail(TXL_ERR_ARG, "%s must be a non-NULL 4-byte aligned pointer", in_names[i]);
+    const void *outs[] = {dq, dk, dval, dr, du, dv};
+    const char *out_names[] = {"dq", "dk", "dval", "dr", "du", "dv"};
+    for (int i = 0; i < 6; ++i)
+        if (!outs[i] || !al4(outs[i])) return fail(TXL_ERR_ARG, "%s must be a non-NULL 4-byte aligned pointer", out_names[i]);
+    const BwdLayout L = plan_bwd(dtype, B, W, m, D, H);
+    const BwdDims &d = L.d;
+    if ((long long)B * H * d.Kp >= (1LL << 22)) return fail(TXL_ERR_UNSUPPORTED, "B * H * (m + W) too large");
+    if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+    if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
+    const bool bf = dtype == TXL_BF16;
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    const int G = B * H, Wp = d.Wp, Kp = d.Kp, dp = d.dp;
+    // head-major operands and their transposes
+    TXL_TRY(hip_check(launch_bwd_pack(bf, d, q, k, val, r, u, v, dO, w + L.qu, w + L.qv, w + L.dOh, w + L.ke,
+                                      w + L.vk, w + L.rk, s), "backward pack launch"));
+    const long long Gk = (long long)dp * Kp, Gq = (long long)dp * Wp;
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.ke, G, H, Kp, dp, dp, w + L.ket, Gk, Kp, H * Gk, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.rk, G, H, Kp, dp, dp, w + L.rkt, Gk, Kp, H * Gk, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.qu, G, H, Wp, dp, dp, w + L.qut, Gq, Wp, H * Gq, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.dOh, G, H, Wp, dp, dp, w + L.dOt, Gq, Wp, H * Gq, s), "transpose launch"));
+    // (q + v)^T of all batch rows of one head side by side: [H][dp][B * Wp]
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.qv, G, H, Wp, dp, dp, w + L.qvt, (long long)dp * B * Wp,
+                                       (long long)B * Wp, Wp, s), "transpose launch"));
+    // (q+u) K^T, (q+v) R^T (column = distance), dO V^T
+    TXL_TRY(hip_check(launch_gemm(bf, grouped({batched_problem(G, Wp, Kp, dp, w + L.qu, dp, w + L.ke, dp, w + L.ac),
+                                                batched_problem(G, Wp, Kp, dp, w + L.qv, dp, w + L.rk, dp, w + L.bd),
+                                                batched_problem(G, Wp, Kp, dp, w + L.dOh, dp, w + L.vk, dp, w + L.dpm)}),
+                                      s), "score GEMM launch"));
+    TXL_TRY(hip_check(launch_bwd_scores(bf, d, (const float *)(w + L.ac), (const float *)(w + L.bd),
+                                        (const float *)(w + L.dpm), w + L.p, w + L.ds, w + L.dsd, s),
+                      "score gradient launch"));
+    const long long Gs = (long long)Kp * Wp;
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.p, G, H, Wp, Kp, Kp, w + L.pt, Gs, Wp, H * Gs, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.ds, G, H, Wp, Kp, Kp, w + L.dst, Gs, Wp, H * Gs, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.dsd, G, H, Wp, Kp, Kp, w + L.dsdt, (long long)Kp * B * Wp,
+                                       (long long)B * Wp, Wp, s), "transpose launch"));
+    // dS K, dS_d R, dS^T (q+u); then P^T dO and, per head over all batch rows, dS_d^T (q+v)
+    TXL_TRY(hip_check(launch_gemm(bf, grouped({batched_problem(G, Wp, dp, Kp, w + L.ds, Kp, w + L.ket, Kp, w + L.dq1),
+                                                batched_problem(G, Wp, dp, Kp, w + L.dsd, Kp, w + L.rkt, Kp, w + L.dq2),
+                                                batched_problem(G, Kp, dp, Wp, w + L.dst, Wp, w + L.qut, Wp, w + L.dkh)}),
+                                      s), "gradient GEMM launch"));
+    TXL_TRY(hip_check(launch_gemm(bf, grouped({batched_problem(G, Kp, dp, Wp, w + L.pt, Wp, w + L.dOt, Wp, w + L.dvh),
+                                                batched_problem(H, Kp, dp, B * Wp, w + L.dsdt, (long long)B * Wp,
+                                                                w + L.qvt, (long long)B * Wp, w + L.drh)}),
+                                      s), "gradient GEMM launch"));
+    return hip_check(launch_bwd_unpack(d, (const float *)(w + L.dq1), (const float *)(w + L.dq2),
+                                       (const float *)(w + L.dkh), (const float *)(w + L.dvh),
+                                       (const float *)(w + L.drh), dq, dk, dval, dr, du, dv,
+                                       (float *)(w + L.part), s),
+                     "backward unpack launch");
 }
 
 int txl_kv_cache_capacity(int M, int W) {

@@ -61,9 +61,9 @@ __device__ __forceinline__ const char *a_row_ptr(const GemmProblem &P, int row, 
 }
 
 template <typename T>
-__device__ __forceinline__ const char *b_row_ptr(const GemmProblem &P, int n) {
+__device__ __forceinline__ const char *b_row_ptr(const GemmProblem &P, int n, int bidx) {
     if (n >= P.cols) return nullptr;
-    const void *w = P.b0;
+    const void *w = (const char *)P.b0 + (long long)bidx * P.b_bstride * (long long)sizeof(T);
     if (n >= P.b_split) { n -= P.b_split; w = P.b1; }
     int wrow = n;
     if (P.b_mode == B_HEADS) {
@@ -284,11 +284,12 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
 
     // Rows and chunk column this thread stages: rows tid/8 + 32c, chunk tid%8.
     const int ccol = tid & 7;
+    const int bidx = P.b_bstride ? m0 / P.seg_rows : 0;    // batch entry of every row of this tile
     const char *arow[kChunks], *brow[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         arow[c] = a_row_ptr<T>(P, m0 + (tid >> 3) + 32 * c, inv_seg);
-        brow[c] = b_row_ptr<T>(P, n0 + (tid >> 3) + 32 * c);
+        brow[c] = b_row_ptr<T>(P, n0 + (tid >> 3) + 32 * c, bidx);
     }
     const int nk = (P.kdim + BK - 1) / BK;
 
@@ -367,7 +368,7 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p) {
     if (p.kdim % epc) return false;
     if ((p.a_ld * es) % 16 || (p.a_bstride * es) % 16 || !aligned16(p.a)) return false;
     if (p.a_mode == A_CONTEXT && (!aligned16(p.ring) || (p.ring_bstride * es) % 16)) return false;
-    if ((p.b_ld * es) % 16 || !aligned16(p.b0) || (p.b1 && !aligned16(p.b1))) return false;
+    if ((p.b_ld * es) % 16 || (p.b_bstride * es) % 16 || !aligned16(p.b0) || (p.b1 && !aligned16(p.b1))) return false;
     if (p.epi == EPI_ROWS) {
         // eight-column vector stores of the output (and loads of the residual)
         const long long oes = p.out_f32 ? 4 : es;

@@ -63,6 +63,8 @@ struct GemmProblem {
     float qscale;
     int relu, out_f32;
     int kv_slots, kv_base;       // EPI_KV: slots per (b, hh) and slot of row t = 0 (multiples of 8)
+    long long b_bstride;         // B_ROWS: elements between the B operands of batch entries (0: one B;
+                                 // nonzero requires seg_rows % 128 == 0 so no tile straddles entries)
 };
 
 struct GemmLaunch {
@@ -122,6 +124,31 @@ hipError_t launch_shaw_rows(bool is_bf16, void *rk, const void *aK, int clip, in
 hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aV, int clip, hipStream_t s);
 hipError_t launch_add_positions(bool is_bf16, const void *x, long long x_bstride, void *y, long long y_bstride,
                                 int B, int W, int D, int pos0, hipStream_t s);
+
+// Backward of the relative attention (txl_backward.hip).
+struct BwdDims {
+    int B, H, W, Wp, m, K, Kp, dh, dp, D;
+};
+// q, dO [B][W][D] -> qu = q + u, qv = q + v, dOh  [G][Wp][dp]   (G = B*H, zero padding)
+// k, val [B][K][D] -> ke, vk [G][Kp][dp];  r [K][D] -> rk [G][Kp][dp] (one copy per batch row)
+hipError_t launch_bwd_pack(bool is_bf16, const BwdDims &d, const void *q, const void *k, const void *val,
+                           const void *r, const void *u, const void *v, const void *dO, void *qu, void *qv,
+                           void *dOh, void *ke, void *vk, void *rk, hipStream_t s);
+// dst[...] = src[g][row][col] transposed per batch entry g = b*H + h: element (g, row, col)
+// goes to dst + h*dst_hs + col*dst_cs + b*dst_bs + row (rows < nrow, cols < ncol)
+hipError_t launch_transpose(bool is_bf16, const void *src, int G, int H, int nrow, int ncol, long long src_ld,
+                            void *dst, long long dst_hs, long long dst_cs, long long dst_bs, hipStream_t s);
+// Per query row: scores from ac [G][Wp][Kp] and bd [G][Wp][Kp] (bd column = distance), softmax,
+// D = sum p dP, ds = p (dP - D) / sqrt(dh); writes p, ds and the distance-indexed dsd [G][Wp][Kp]
+hipError_t launch_bwd_scores(bool is_bf16, const BwdDims &d, const float *ac, const float *bd, const float *dp,
+                             void *p, void *ds, void *dsd, hipStream_t s);
+// dq = dq1 + dq2 (head-major fp32) -> [B][W][D]; du, dv = column sums of dq1, dq2;
+// dk, dval [G][Kp][dp] -> [B][K][D]; dr [H][Kp][dp] -> [K][D]
+// (part: scratch of 2 * H * bwd_bias_chunks(d) * 64 floats)
+int bwd_bias_chunks(const BwdDims &d);
+hipError_t launch_bwd_unpack(const BwdDims &d, const float *dq1, const float *dq2, const float *dkh,
+                             const float *dvh, const float *drh, float *dq, float *dk, float *dval, float *dr,
+                             float *du, float *dv, float *part, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Small kernels.
