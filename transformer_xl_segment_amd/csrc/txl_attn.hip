@@ -212,7 +212,10 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         r_chunk(rnext, c0 - 63);
         g_chunk(gb[0], rnext);
         r_chunk(rnext, c0 - 127);
-        // the band top of block 0 goes to LDS once; later blocks rewrite it
+        // the band of block 0; every later band is written at the end of the
+        // block before it, where it overlaps that block's P.V products
+        write_gblock(grow, gb[0][0], 0, hf);
+        write_gblock(grow, gb[0][1], 32, hf);
         write_gblock(grow, gtop, 64, hf);
     }
 
@@ -283,9 +286,6 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
             sacc[0] = zero16();
             sacc[1] = zero16();
         } else {
-        write_gblock(grow, gb[P][0], 0, hf);
-        write_gblock(grow, gb[P][1], 32, hf);
-        if (P == 1 || kb > 0) write_gblock(grow, gb[Q][0], 64, hf);
         wave_lds_sync();
         // key b = 32*sb + crow(i) of query a needs band offset a - b + 63
         {
@@ -359,6 +359,14 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
                 load_vt(fv, sm.v + (32 * o + fr) * SM::kPitchV, 16 * p + 4 * hf);
                 mma16(oacc[o], fv, fp4[p]);
             }
+        }
+        // ---- band of block kb+1: its chunk (computed above) and, on top, the
+        // low half of this block's chunk. This block's band reads are complete
+        // (the content-term MFMAs consumed them).
+        if constexpr (DIST) {
+            write_gblock(grow, gb[Q][0], 0, hf);
+            write_gblock(grow, gb[Q][1], 32, hf);
+            write_gblock(grow, gb[P][0], 64, hf);
         }
     };
 

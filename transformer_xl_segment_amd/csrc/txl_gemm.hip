@@ -15,6 +15,8 @@
 // Tiles are numbered so that tiles sharing rows of A are consecutive, and the
 // workgroup index is remapped so that consecutive tiles land on the same XCD
 // (workgroups are dealt round-robin over the 8 XCDs, each with its own L2).
+#include <type_traits>
+
 #include "txl_device.hpp"
 #include "txl_internal.hpp"
 
@@ -26,6 +28,7 @@ constexpr int kBM = 128, kBN = 128, kThreads = 256;
 constexpr int kRowBytes = 128;                       // bytes per row of one k-tile
 constexpr int kPitch = kRowBytes + 16;               // LDS bytes per row
 constexpr int kChunks = kBM * (kRowBytes / 16) / kThreads;   // 16-byte chunks per thread per operand (4)
+constexpr int kPrefetch = 2;                         // k-tiles of global loads in flight
 
 struct GemmSmem {
     char a[2][kBM * kPitch];
@@ -293,21 +296,25 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
     }
     const int nk = (P.kdim + BK - 1) / BK;
 
-    u32x4 ra[kChunks], rb[kChunks];
-#define TXL_GLOAD(kt_)                                                    \
+    // Global loads run kPre k-tiles ahead of the MFMAs (a ring of register
+    // sets): a k-tile's MFMAs take far less time than an L2 round trip.
+    constexpr int kPre = kPrefetch;
+    static_assert(kPre == 2 || kPre == 3, "the ring needs two or three register sets");
+    u32x4 ra[kPre][kChunks], rb[kPre][kChunks];
+#define TXL_GLOAD(set_, kt_)                                              \
     do {                                                                  \
         const int k_ = (kt_) * BK + ccol * EPC;                           \
         _Pragma("unroll") for (int c = 0; c < kChunks; ++c) {             \
-            ra[c] = load_chunk<T, VEC>(arow[c], k_, P.kdim);              \
-            rb[c] = load_chunk<T, VEC>(brow[c], k_, P.kdim);              \
+            ra[set_][c] = load_chunk<T, VEC>(arow[c], k_, P.kdim);        \
+            rb[set_][c] = load_chunk<T, VEC>(brow[c], k_, P.kdim);        \
         }                                                                 \
     } while (0)
-#define TXL_SSTORE(buf_)                                                  \
+#define TXL_SSTORE(set_, buf_)                                            \
     do {                                                                  \
         _Pragma("unroll") for (int c = 0; c < kChunks; ++c) {             \
             const int r_ = (tid >> 3) + 32 * c;                           \
-            *reinterpret_cast<u32x4 *>(&sm.a[buf_][r_ * kPitch + ccol * 16]) = ra[c]; \
-            *reinterpret_cast<u32x4 *>(&sm.b[buf_][r_ * kPitch + ccol * 16]) = rb[c]; \
+            *reinterpret_cast<u32x4 *>(&sm.a[buf_][r_ * kPitch + ccol * 16]) = ra[set_][c]; \
+            *reinterpret_cast<u32x4 *>(&sm.b[buf_][r_ * kPitch + ccol * 16]) = rb[set_][c]; \
         }                                                                 \
     } while (0)
 
@@ -317,13 +324,8 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
-    TXL_GLOAD(0);
-    TXL_SSTORE(0);
-    __syncthreads();
     const int fr = lane & 31, fh = lane >> 5;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) TXL_GLOAD(kt + 1);
+    auto mma_tile = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             Frag<T> fa[2], fb[2];
@@ -337,21 +339,48 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) mma16(acc[i][j], fa[i], fb[j]);
+                for (int j = 0; j < 2; ++j) mma16(acc[i][j], fb[j], fa[i]);   // C^T block: lane = row of C
         }
-        if (kt + 1 < nk) TXL_SSTORE(buf ^ 1);
+    };
+    // k-tile kt lives in register set kt % kPre and LDS buffer kt & 1; the loop
+    // is unrolled by kPre so every set index is a compile-time constant, and
+    // each unrolled step issues the same loads in the same order
+    auto step = [&](auto phase, int kt) {
+        constexpr int S = decltype(phase)::value;
+        constexpr int S1 = (S + 1) % kPre;
+        mma_tile(kt & 1);
+        if (kt + 1 < nk) TXL_SSTORE(S1, (kt + 1) & 1);
+        if (kt + kPre < nk) TXL_GLOAD(S, kt + kPre);
         __syncthreads();
+    };
+
+    TXL_GLOAD(0, 0);
+    if (1 < nk) TXL_GLOAD(1, 1);
+    if constexpr (kPre > 2) {
+        if (2 < nk) TXL_GLOAD(2, 2);
+    }
+    TXL_SSTORE(0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += kPre) {
+        step(std::integral_constant<int, 0>(), kt);
+        if (kt + 1 < nk) step(std::integral_constant<int, 1>(), kt + 1);
+        if constexpr (kPre > 2) {
+            if (kt + 2 < nk) step(std::integral_constant<int, 2>(), kt + 2);
+        }
     }
 
-    // stage the C tile in LDS (the k-loop ended with a barrier), then write it out
+    // stage the C tile in LDS (the k-loop ended with a barrier), then write it out.
+    // The blocks were computed transposed, so lane fr holds row fr of the block and
+    // each group of four registers four consecutive columns: one 16-byte store each.
     float *cs = reinterpret_cast<float *>(&sm);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                cs[(wm * 64 + i * 32 + crow(r, lane)) * kCPitch + wn * 64 + j * 32 + fr] = acc[i][j][r];
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<f32x4 *>(&cs[(wm * 64 + i * 32 + fr) * kCPitch + wn * 64 + j * 32 + crow(4 * q, lane)]) =
+                    f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     __syncthreads();
     epilogue<T, VEC>(P, cs, m0, n0, tid, inv_seg);
 #undef TXL_GLOAD
