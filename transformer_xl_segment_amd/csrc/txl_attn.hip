@@ -35,9 +35,12 @@
 // of the probabilities is taken with packed bf16 dot products over the very
 // values the P.V product consumes.
 //
-// Softmax uses a lazy maximum: the running maximum only moves (and the output
-// accumulators are only rescaled) when a block's maximum exceeds it by more
-// than 8 in log2 units, which keeps every exp2 below 2^8.
+// Softmax uses a lazy maximum: the scores are taken relative to a running base
+// m_run (subtracted as the band values are read, so the exponentials need no
+// subtraction of their own); the base only moves (and the output accumulators
+// are only rescaled) when a block's maximum exceeds it by more than 8 in log2
+// units (which keeps every exp2 below 2^8); it starts at the first block's
+// maximum.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -190,7 +193,8 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     f32x16 oacc[NO];
 #pragma unroll
     for (int o = 0; o < NO; ++o) oacc[o] = zero16();
-    float m_run = -INFINITY, l_run = 0.f;
+    // running maximum (the base the scores are taken relative to) and sum
+    float m_run = 0.f, l_run = 0.f;
 
     // Band of key block kb: distances cw-63 .. cw+31 with cw = m + iw - 64*kb.
     // gb[kb & 1] holds the chunk cw-63 .. cw (two 32-distance blocks); the band's
@@ -283,8 +287,8 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         // ---- shift the distance term into place through LDS
         f32x16 sacc[2];
         if constexpr (!DIST) {
-            sacc[0] = zero16();
-            sacc[1] = zero16();
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sacc[0][i] = sacc[1][i] = -m_run;
         } else {
         wave_lds_sync();
         // key b = 32*sb + crow(i) of query a needs band offset a - b + 63
@@ -293,7 +297,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 #pragma unroll
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[sb][i] = rb[63 - 32 * sb - 8 * (i >> 2) - (i & 3)];
+                for (int i = 0; i < 16; ++i) sacc[sb][i] = rb[63 - 32 * sb - 8 * (i >> 2) - (i & 3)] - m_run;
         }
         }
         // ---- content term on top: S^T += K (q+u)^T
@@ -314,22 +318,29 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
                 for (int i = 0; i < 16; ++i)
                     if (32 * sb + crow(i, lane) > lim) sacc[sb][i] = -INFINITY;
         }
-        // ---- online softmax (log2 domain): maximum and lazy rescale
+        // ---- online softmax (log2 domain; the scores are held relative to m_run)
         float mx = sacc[0][0];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[sb][i]);
-        mx = fmaxf(mx, swap_half(mx));
-        const float m_new = fmaxf(m_run, mx);
-        if (__any(m_new > m_run + 8.f)) {
-            const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        mx = half_max(mx);
+        // lazy re-base: to the first block's maximum, then whenever a block
+        // maximum exceeds the base by more than 8
+        const bool rebase = mx > 8.f || (l_run == 0.f && mx > -INFINITY);
+        if (__any(rebase)) {
+            const float shift = rebase ? mx : 0.f;
+            const float alpha = __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
             for (int o = 0; o < NO; ++o)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[o][i] *= alpha;
             l_run *= alpha;
-            m_run = m_new;
+            m_run += shift;
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sacc[sb][i] -= shift;
         }
         // ---- next distance chunk (MFMA) interleaved with exp / pack / row sum (VALU)
         if constexpr (DIST) {
@@ -341,15 +352,15 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sacc[sb][i] = __builtin_amdgcn_exp2f(sacc[sb][i] - m_run);
+            for (int i = 0; i < 16; ++i) sacc[sb][i] = __builtin_amdgcn_exp2f(sacc[sb][i]);
         Frag<T> fp4[4];
-        float lsum = 0.f;
+        float lsum[2] = {0.f, 0.f};          // two independent chains
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             p_frag(fp4[p], sacc[p >> 1], 8 * (p & 1));
-            lsum = psum(fp4[p], lsum);       // sums exactly the values P.V uses
+            lsum[p & 1] = psum(fp4[p], lsum[p & 1]);   // sums exactly the values P.V uses
         }
-        l_run += lsum;
+        l_run += lsum[0] + lsum[1];
         // ---- O^T += V^T P^T, 16 keys per MFMA
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -379,7 +390,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 #undef TXL_KV_SSTORE
 
     if (!wave_has_queries) return;
-    const float l_tot = l_run + swap_half(l_run);
+    const float l_tot = half_sum(l_run);
     const float inv = 1.f / l_tot;
     const int qi = iw + fr;
     if (qi >= A.W) return;

@@ -80,6 +80,16 @@ __device__ __forceinline__ f32x16 zero16() {
 __device__ __forceinline__ int crow(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 // Exchange with the lane 32 positions away (the other half of the wave).
+// Maximum and sum of x over the two lanes l and l ^ 32 (v_permlane32_swap: no LDS trip).
+__device__ __forceinline__ float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float swap_half(float x) {
     int l = threadIdx.x & 63;
     return __int_as_float(__builtin_amdgcn_ds_bpermute(((l ^ 32) << 2), __float_as_int(x)));
