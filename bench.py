@@ -46,7 +46,10 @@ def attn_flops(B, H, dh, W, m):
 
 
 def proj_flops(B, W, m, D):
-    return 4.0 * B * W * D * D + 4.0 * B * (m + W) * D * D + 2.0 * (m + W) * D * D + 2.0 * B * W * D * D
+    """Flops of the projections of one segment: q (one product serves q+u and
+    q+v), k_E and v over the m + W context rows, r over the m + W distances
+    (shared by the batch), and the output projection."""
+    return 2.0 * B * W * D * D + 4.0 * B * (m + W) * D * D + 2.0 * (m + W) * D * D + 2.0 * B * W * D * D
 
 
 def attn_bytes(B, W, m, D, es):
@@ -68,6 +71,74 @@ def traffic_for(kernel_src: str, path: str):
     if rec.get("kernel_sha256") != digest:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def time_fwd_only(tb, torch, segs, ring, params, R, H, out, ws, steps):
+    """txl_rel_attn_fwd alone (projections, attention kernel, output projection)
+    on the full memory, without the memory update."""
+    B, W = out.shape[0], out.shape[1]
+    el = _timed(torch, lambda k: tb.rel_attn_fwd(segs[k % len(segs)], ring, params, R, H, out=out, workspace=ws),
+                steps)
+    return {"ms_per_call": el * 1e3 / steps, "tokens_per_s": B * W * steps / el,
+            "call": "txl_rel_attn_fwd at m = M (fused projections + attention kernel + W_o)"}
+
+
+def time_schedule(tb, torch, segs, params, R, B, M, D, H, out, ws, reps):
+    """The workload's whole schedule: its S segments from an empty memory, each
+    txl_rel_attn_fwd + txl_mem_update, so the early segments see m < M."""
+    ring = tb.MemoryRing.empty(B, M, D, out.dtype, out.device)
+    W = out.shape[1]
+
+    def sched(k):
+        ring.len, ring.head = 0, 0           # an empty memory: the stale rows are never read
+        for h in segs:
+            tb.rel_attn_fwd(h, ring, params, R, H, out=out, workspace=ws)
+            tb.mem_update(ring, h)
+
+    el = _timed(torch, sched, reps, 1)
+    S = len(segs)
+    return {"segments": S, "ms_per_schedule": el * 1e3 / reps, "tokens_per_s": B * W * S * reps / el,
+            "memory_lengths": [min(M, k * W) for k in range(S)]}
+
+
+def longmem_warm(tb, torch, syn, dev, steps):
+    """The long-memory workload with its memory already full (m = 1600 for every
+    segment): attention-kernel MFMA fraction and its HBM rate."""
+    bf = torch.bfloat16
+    wl = syn.WORKLOADS["longmem_m1600_bf16"]
+    B, D, H, W, M = wl.B, wl.D, wl.H, wl.W, wl.M
+    dh = D // H
+    prob = syn.draw_problem(wl)
+    params = tb.LayerParams.from_numpy(prob.params[0], bf, dev)
+    R = tb.sinusoid_table(M + W, D, bf, dev)
+    x = torch.from_numpy(prob.x).to(dev).to(bf)
+    segs = [x[:, k * W:(k + 1) * W] for k in range(wl.S)]
+    warm = torch.from_numpy(prob.warm_mem).to(dev).to(bf)
+    ring = tb.MemoryRing.empty(B, M, D, bf, dev)
+    tb.mem_update(ring, warm)
+    out = torch.empty(B, W, D, dtype=bf, device=dev)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN, bf, B, W, M, D, H), dtype=torch.uint8, device=dev)
+
+    def step(k):
+        tb.rel_attn_fwd(segs[k % wl.S], ring, params, R, H, out=out, workspace=ws)
+        tb.mem_update(ring, segs[k % wl.S])
+
+    for k in range(3):
+        step(k)
+    torch.cuda.synchronize()
+    tb.profile_begin(steps)
+    el = _timed(torch, step, steps, 0)
+    attn_ms, n = tb.profile_end()
+    lm = sorted(tb.profile_times(n))
+    m = ring.len
+    fl, by = attn_flops(B, H, dh, W, m), attn_bytes(B, W, m, D, 2)
+    avg = attn_ms * 1e-3 / n
+    return {"workload": wl.name, "B": B, "W": W, "m": m, "D": D, "H": H,
+            "tokens_per_s": B * W * steps / el, "ms_per_step": el * 1e3 / steps,
+            "attn_avg_launch_us": avg * 1e6, "attn_median_launch_us": float(np.median(lm)) * 1e3,
+            "attn_min_launch_us": lm[0] * 1e3,
+            "attn_tflops": fl / avg / 1e12, "attn_frac_bf16_peak": fl / avg / 1e12 / BF16_PEAK_TFLOPS,
+            "attn_compulsory_gbs": by / avg / 1e9, "attn_frac_hbm_peak": by / avg / 1e9 / HBM_PEAK_GBS}
 
 
 def time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, steps, warmup):
@@ -234,13 +305,28 @@ def sliding_window(tb, torch, syn, dev):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(prob, R64, H):
     """The oracle on the steady segments of the workload (m = 512, all batch
     rows): segments 1 .. S-1 with the previous segment as the memory, repeated
-    until about 10 s of host time have been spent."""
+    until about 10 s of host time have been spent. Then the oracle on one thread
+    for the two small workloads (their whole schedules) and for one batch row of
+    one steady segment of this workload."""
     from oracle import oracle as orc
+    from transformer_xl_segment_amd import synthetic as syn
     wl = prob.wl
-    W = wl.W
+    W, D = wl.W, wl.D
+    threads = orc.num_threads()
     t0 = time.perf_counter()
     segs = 0
     while True:
@@ -252,10 +338,39 @@ def cpu_baseline(prob, R64, H):
         dt = time.perf_counter() - t0
         if dt >= 10.0 or segs >= 4 * (wl.S - 1):
             break
-    tokens = segs * prob.x.shape[0] * W
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": orc.num_threads(), "kind": "oracle",
-            "sample": f"{segs} steady segments of {WORKLOAD} (all {prob.x.shape[0]} batch rows each, m={W}), "
-                      f"{dt:.1f} s wall"}
+    Bx = prob.x.shape[0]
+    tokens = segs * Bx * W
+    seg_flops = attn_flops(Bx, H, D // H, W, W) + proj_flops(Bx, W, W, D)
+
+    single = {}
+    orc.set_num_threads(1)
+    try:
+        for name in ("tiny_attn_fp32", "layer_ffn_fp32"):
+            w = syn.WORKLOADS[name]
+            p = syn.draw_problem(w)
+            Rw = orc.sinusoid_table(w.M + w.W, w.D)
+            t1 = time.perf_counter()
+            orc.stack_fwd(p.x, p.params, Rw, w.H, w.W, w.M, w.op == "layer")
+            d1 = time.perf_counter() - t1
+            single[name] = {"tokens_per_s": p.x.shape[0] * p.x.shape[1] / d1, "sample": "whole schedule",
+                            "seconds": d1}
+        t = 1
+        h = prob.x[:1, t * W:(t + 1) * W].astype(np.float64)
+        mem = prob.x[:1, (t - 1) * W:t * W].astype(np.float64)
+        t1 = time.perf_counter()
+        orc.rel_attn(h, mem, prob.params[0], R64, H)
+        d1 = time.perf_counter() - t1
+        single[WORKLOAD] = {"tokens_per_s": W / d1, "sample": "batch row 0 of one steady segment",
+                            "seconds": d1,
+                            "gflops": (attn_flops(1, H, D // H, W, W) + proj_flops(1, W, W, D)) / d1 / 1e9}
+    finally:
+        orc.set_num_threads(threads)
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{segs} steady segments of {WORKLOAD} (all {Bx} batch rows each, m={W}), "
+                      f"{dt:.1f} s wall",
+            "gflops": seg_flops * segs / dt / 1e9, "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "omp_threads": threads, "cpu_model": cpu_model(),
+            "single_thread": single}
 
 
 def main():
@@ -266,6 +381,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sliding-window", action="store_true",
                     help="skip the comparison with vanilla sliding-window evaluation")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline step (for counter runs); implies the two --no-* flags")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times) before the "
                          "warm-up, as the reference point for HBM byte counters")
@@ -326,6 +443,7 @@ def main():
     elapsed = time.perf_counter() - t0
     attn_ms, launches = tb.profile_end()
     assert launches == args.steps
+    launch_ms = sorted(tb.profile_times(launches))
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = B * W * args.steps
@@ -352,11 +470,19 @@ def main():
         "roofline": {"kernel": "rel_attn_kernel", "bound": "mfma", "achieved": a_tflops,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": a_tflops / BF16_PEAK_TFLOPS,
                      "traffic": traffic, "avg_launch_us": a_avg_s * 1e6,
+                     "median_launch_us": float(np.median(launch_ms)) * 1e3, "min_launch_us": launch_ms[0] * 1e3,
+                     "frac_at_min_launch": a_flops / (launch_ms[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_launch": a_flops,
                      "compulsory_bytes_per_launch": attn_bytes(B, W, m, D, 2)},
         "attn_tokens_per_s": B * W / a_avg_s,
         "step_tflops": (a_flops + proj_flops(B, W, m, D)) / (ms_per_step * 1e-3) / 1e12,
     }
+    if args.headline_only:
+        print(json.dumps(rec), flush=True)
+        return
+    rec["rel_attn_fwd_only"] = time_fwd_only(tb, torch, segs, ring, params, R, H, out, ws, args.steps)
+    rec["schedule"] = time_schedule(tb, torch, segs, params, R, B, M, D, H, out, ws, max(3, args.steps // 8))
+    rec["longmem_warm"] = longmem_warm(tb, torch, syn, dev, max(10, args.steps // 4))
     kv = time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, args.steps, args.warmup)
     kv["speedup_vs_row_memory"] = kv["value"] / rec["value"]
     rec["kv_cache"] = kv

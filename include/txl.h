@@ -299,6 +299,11 @@ txl_status txl_rel_attn_fwd_cached(txl_dtype dtype, int B, int W, int D, int H,
  * number of timed launches. Not thread-safe; meant for benchmarks. */
 txl_status txl_profile_begin(int max_launches);
 txl_status txl_profile_end(double *total_ms, int *launches);
+/* Per-launch kernel times, in milliseconds and launch order, of the window the
+ * last txl_profile_end closed: copies min(capacity, launches) values into ms
+ * (host memory owned by the caller) and their count into *n. Fails while a
+ * window is open or if ms is NULL with capacity > 0. */
+txl_status txl_profile_times(double *ms, int capacity, int *n);
 
 /* Static description of a status code, and the calling thread's last error. */
 const char *txl_status_string(txl_status s);

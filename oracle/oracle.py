@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
             build()
         L = ctypes.CDLL(_LIB_PATH)
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]
+        L.orc_set_num_threads.restype = ctypes.c_int
         L.orc_sinusoid_table.argtypes = [ctypes.c_int, ctypes.c_int, _dp]
         L.orc_linear.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _dp, _dp, _dp]
         L.orc_layer_norm.argtypes = [ctypes.c_long, ctypes.c_int, _dp, _dp, _dp, _dp]
@@ -83,6 +85,11 @@ def _check(st: int, what: str) -> None:
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Thread count of the oracle's OpenMP loops from now on; returns the count in use."""
+    return int(lib().orc_set_num_threads(n))
 
 
 def sinusoid_table(R_len: int, D: int) -> np.ndarray:

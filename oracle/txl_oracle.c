@@ -55,6 +55,18 @@ int orc_num_threads(void)
 #endif
 }
 
+/* Set the thread count of the OpenMP loops (n >= 1); returns the count in use. */
+int orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /* Relative-encoding table ([XL] step 4 and the legend entry for R_{i-j}:
  * a sinusoidal encoding of the distance with no trained parameters). The
  * pages do not print the formula; the [sin | cos] half-split with base 10000

@@ -254,6 +254,9 @@ def test_sinusoid_and_profiler_reject_bad_arguments():
     assert L.txl_profile_begin(0) == tb.TXL_ERR_ARG
     ms, n = ctypes.c_double(), ctypes.c_int()
     assert L.txl_profile_end(ctypes.byref(ms), ctypes.byref(n)) == tb.TXL_ERR_ARG   # not active
+    assert L.txl_profile_times(None, 4, ctypes.byref(n)) == tb.TXL_ERR_ARG            # no buffer
+    assert L.txl_profile_times(None, -1, ctypes.byref(n)) == tb.TXL_ERR_ARG
+    assert L.txl_profile_times(None, 0, ctypes.byref(n)) == tb.TXL_OK and n.value == 0
 
 
 def test_binding_raises_when_library_missing(monkeypatch, tmp_path):

@@ -80,10 +80,11 @@ def lib() -> ctypes.CDLL:
         L.txl_rel_attn_fwd_cached.argtypes = [i, i, i, i, i, vp, ll, KVp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_profile_begin.argtypes = [i]
         L.txl_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+        L.txl_profile_times.argtypes = [ctypes.POINTER(ctypes.c_double), i, ctypes.POINTER(ctypes.c_int)]
         for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_mem_update", "txl_layer_fwd",
                   "txl_stack_fwd_segments", "txl_stack_fwd_window", "txl_kv_cache_capacity",
                   "txl_attn_fwd_variant", "txl_add_positions", "txl_rel_attn_bwd", "txl_kv_cache_append",
-                  "txl_rel_attn_fwd_cached", "txl_profile_begin", "txl_profile_end"):
+                  "txl_rel_attn_fwd_cached", "txl_profile_begin", "txl_profile_end", "txl_profile_times"):
             getattr(L, f).restype = i
         L.txl_status_string.argtypes = [i]
         L.txl_status_string.restype = ctypes.c_char_p
@@ -409,6 +410,14 @@ def profile_end():
     n = ctypes.c_int(0)
     _check(lib().txl_profile_end(ctypes.byref(ms), ctypes.byref(n)), "txl_profile_end")
     return ms.value, n.value
+
+
+def profile_times(capacity: int) -> List[float]:
+    """Per-launch attention-kernel milliseconds of the last closed profiling window."""
+    buf = (ctypes.c_double * max(capacity, 1))()
+    n = ctypes.c_int(0)
+    _check(lib().txl_profile_times(buf, capacity, ctypes.byref(n)), "txl_profile_times")
+    return [buf[i] for i in range(n.value)]
 
 
 def exported_names() -> List[str]:

@@ -100,6 +100,7 @@ struct Profiler {
     bool on = false;
     int used = 0;
     std::vector<hipEvent_t> start, stop;
+    std::vector<double> times;      // per-launch milliseconds of the last finished window
 } g_prof;
 
 hipError_t attn_launch(bool bf16, const AttnArgs &a, hipStream_t s) {
@@ -782,15 +783,26 @@ txl_status txl_profile_begin(int max_launches) {
 txl_status txl_profile_end(double *total_ms, int *launches) {
     if (!g_prof.on) return fail(TXL_ERR_ARG, "profiling is not active");
     g_prof.on = false;
+    g_prof.times.clear();
     double sum = 0.0;
     for (int i = 0; i < g_prof.used; ++i) {
         TXL_TRY(hip_check(hipEventSynchronize(g_prof.stop[i]), "hipEventSynchronize"));
         float ms = 0.f;
         TXL_TRY(hip_check(hipEventElapsedTime(&ms, g_prof.start[i], g_prof.stop[i]), "hipEventElapsedTime"));
+        g_prof.times.push_back(ms);
         sum += ms;
     }
     if (total_ms) *total_ms = sum;
     if (launches) *launches = g_prof.used;
+    return TXL_OK;
+}
+
+txl_status txl_profile_times(double *ms, int capacity, int *n) {
+    if (g_prof.on) return fail(TXL_ERR_ARG, "profiling is still active");
+    if (capacity < 0 || (capacity > 0 && !ms)) return fail(TXL_ERR_ARG, "ms must hold capacity >= 0 values");
+    const int k = std::min(capacity, (int)g_prof.times.size());
+    for (int i = 0; i < k; ++i) ms[i] = g_prof.times[i];
+    if (n) *n = k;
     return TXL_OK;
 }
 
