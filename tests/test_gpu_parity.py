@@ -62,6 +62,13 @@ ATTN_CASES = [
     ("dh64_two_qblocks", 2, 128, 2, 130, 70, 3),
     ("dh41_odd", 2, 82, 2, 29, 45, 3),
     ("dh64_wide_mem", 1, 64, 1, 20, 200, 4),
+    # few query blocks over many keys: the key range of each query block is
+    # split over several workgroups and merged (2, 4 and 4 parts; in the second
+    # case the first query block has 3 key blocks for 4 parts, so some parts
+    # are empty, and the queries of a wave see none of the last part's keys)
+    ("dh64_split_long_mem", 1, 64, 1, 20, 600, 3),
+    ("dh64_split_empty_parts", 1, 64, 1, 1024, 16, 2),
+    ("dh41_split", 2, 82, 2, 200, 900, 2),
 ]
 
 

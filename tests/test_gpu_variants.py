@@ -65,6 +65,7 @@ SHAW_CASES = [
     ("dh64_clip64_two_qblocks", 2, 128, 2, 130, 70, 3, 64),
     ("dh41_clip120_beyond_keys", 2, 82, 2, 29, 45, 3, 120),
     ("dh64_clip128_long_mem", 1, 64, 1, 40, 300, 2, 128),
+    ("dh64_clip64_key_split", 1, 64, 1, 40, 700, 2, 64),     # 3 key parts, merged log-sum-exp
 ]
 
 
@@ -84,6 +85,7 @@ ABS_CASES = [
     ("dh32_ragged", 2, 64, 2, 37, 50, 3),
     ("dh64_two_qblocks", 2, 128, 2, 130, 70, 3),
     ("dh41", 2, 82, 2, 29, 45, 3),
+    ("dh64_key_split", 1, 64, 1, 40, 700, 2),                 # 3 key parts
 ]
 
 

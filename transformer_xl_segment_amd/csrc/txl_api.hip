@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <initializer_list>
 #include <string>
 #include <vector>
@@ -49,6 +50,8 @@ bool al4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 struct Layout {
     size_t qu, qv, ke, vt, rk, o;      // attention operands and output
     size_t lse;                        // encoding variants: per-query log-sum-exp
+    size_t part_o, part_ml;            // key-split parts of the attention output
+    int nsplit;                        // most key splits any launch of this layout uses
     size_t z, h1, f;                   // block: fp32 pre-LN sums, LN1 output, FFN hidden
     size_t hb0, hb1;                   // stack: inter-layer activations
     size_t total;
@@ -80,6 +83,11 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
     L.rk = take((size_t)H * (L.Kp + 2 * ATTN_RPAD) * L.dp * es);
     L.o = take((size_t)B * W * D * es);
     if (op == TXL_OP_ATTN_VARIANT) L.lse = take((size_t)B * H * L.Wp * 4);
+    L.nsplit = attn_splits(B, H, W, Kmax);
+    if (L.nsplit > 1) {
+        L.part_o = take((size_t)L.nsplit * B * H * L.Wp * L.dp * 4);
+        L.part_ml = take((size_t)L.nsplit * B * H * L.Wp * 2 * 4);
+    }
     if (op == TXL_OP_LAYER || op == TXL_OP_STACK) {
         L.z = take((size_t)B * W * D * 4);
         L.h1 = take((size_t)B * W * D * es);
@@ -305,6 +313,14 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     a.B = B; a.H = H; a.W = W; a.Wp = L.Wp; a.m = m; a.K = K; a.Kp = Kp; a.dh = dh; a.dp = dp; a.D = D;
     a.C = cache ? cache->C : Kp;
     a.khead = cache ? cache->head : 0;
+    // key split (non-decreasing in K, so never more parts than the layout holds)
+    a.nsplit = std::min(attn_splits(B, H, W, K), L.nsplit);
+    if (a.nsplit > 1) {
+        a.part_o = (float *)(ws + L.part_o);
+        a.part_ml = (float *)(ws + L.part_ml);
+    } else {
+        a.nsplit = 1;
+    }
     TXL_TRY(hip_check(attn_launch(bf, a, s), "attention launch"));
     if (a.lse) TXL_TRY(hip_check(launch_shaw_values(bf, a, var->aV, var->clip, s), "value-term launch"));
     return TXL_OK;

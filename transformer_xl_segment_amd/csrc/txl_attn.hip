@@ -41,8 +41,16 @@
 // are only rescaled) when a block's maximum exceeds it by more than 8 in log2
 // units (which keeps every exp2 below 2^8); it starts at the first block's
 // maximum.
+//
+// Key split. When the query blocks alone give too few workgroups to fill the
+// chip (a short segment over a long memory), each query block is run by
+// nsplit workgroups over disjoint ranges of its key blocks. Each writes its
+// unnormalised output with its running base and sum; a second kernel rescales
+// the parts to their common maximum and divides by the total sum (the online
+// softmax's own merge rule, applied once across the parts).
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "txl_device.hpp"
@@ -56,6 +64,7 @@ constexpr int kWaves = 4;
 constexpr int kQB = 128;          // queries per workgroup (32 per wave)
 constexpr int kKB = 64;           // keys per block
 constexpr int kGPitch = 100;      // floats per query row of the distance buffer
+constexpr int kMaxSplit = 8;      // most key parts per query block
 
 template <typename T, int DP, bool DIST>
 struct AttnSmem {
@@ -135,8 +144,11 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 
     const int BH = A.B * A.H;
     const int nqb = (A.W + kQB - 1) / kQB;
-    const int rank = blockIdx.x / BH;
-    const int bh = blockIdx.x - rank * BH;
+    const int ns = A.nsplit;
+    const int rank = blockIdx.x / (BH * ns);
+    const int rem = blockIdx.x - rank * (BH * ns);
+    const int split = rem / BH;
+    const int bh = rem - split * BH;
     const int qblk = nqb - 1 - rank;                 // longest query blocks first
     const int b = bh / A.H, h = bh - b * A.H;
     const int i0 = qblk * kQB;
@@ -147,7 +159,10 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     const int iw = i0 + 32 * w;                      // first query of this wave
     const bool wave_has_queries = iw < A.W;
     const int jend = min(A.K, m + i0 + kQB);         // keys any query here can see
-    const int nkb = (jend + kKB - 1) / kKB;
+    const int nkb_all = (jend + kKB - 1) / kKB;
+    // this workgroup's key blocks [kb_lo, nkb)
+    const int kb_lo = (int)((long long)split * nkb_all / ns);
+    const int nkb = (int)((long long)(split + 1) * nkb_all / ns);
     const int last_key_wave = m + iw + 31;           // last key any query of the wave sees
 
     const T *qu = (const T *)A.qu + ((long long)bh * A.Wp) * DP;
@@ -188,40 +203,6 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
             for (int s = 0; s < NS; ++s) mma16(g[bb], f[bb][s], fqv[s]);
         }
     };
-
-    float *grow = sm.g[DIST ? w : 0] + (DIST ? fr * kGPitch : 0);
-    f32x16 oacc[NO];
-#pragma unroll
-    for (int o = 0; o < NO; ++o) oacc[o] = zero16();
-    // running maximum (the base the scores are taken relative to) and sum
-    float m_run = 0.f, l_run = 0.f;
-
-    // Band of key block kb: distances cw-63 .. cw+31 with cw = m + iw - 64*kb.
-    // gb[kb & 1] holds the chunk cw-63 .. cw (two 32-distance blocks); the band's
-    // top part cw+1 .. cw+31 is block 0 of the previous chunk, gb[(kb+1) & 1][0],
-    // or for kb = 0 the block gtop computed here (written to LDS before the
-    // loop). rnext holds r of the next chunk.
-    // The two chunk buffers alternate with the parity of kb (the loop is unrolled
-    // by two), so no register tile is copied from one step to the next.
-    f32x16 gtop = zero16(), gb[2][2];
-    Frag<T> rnext[2][NS];
-    if (DIST && wave_has_queries) {
-        const int c0 = m + iw;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            Frag<T> f;
-            load8(f, rk + (long long)(c0 + 1 + fr) * DP + 16 * s + 8 * hf);
-            mma16(gtop, f, fqv[s]);
-        }
-        r_chunk(rnext, c0 - 63);
-        g_chunk(gb[0], rnext);
-        r_chunk(rnext, c0 - 127);
-        // the band of block 0; every later band is written at the end of the
-        // block before it, where it overlaps that block's P.V products
-        write_gblock(grow, gb[0][0], 0, hf);
-        write_gblock(grow, gb[0][1], 32, hf);
-        write_gblock(grow, gtop, 64, hf);
-    }
 
     // cooperative K / V^T staging; key j lives in slot (khead + j) mod C, and a
     // 16-byte V^T chunk (8 bf16 or 4 fp32 keys) never straddles the wrap
@@ -272,6 +253,49 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
             }                                                                                      \
         }                                                                                          \
     } while (0)
+    // the first K / V tile is requested before the distance prologue, whose
+    // loads and products then cover its latency
+    if (kb_lo < nkb) TXL_KV_GLOAD(kb_lo);
+
+    float *grow = sm.g[DIST ? w : 0] + (DIST ? fr * kGPitch : 0);
+    f32x16 oacc[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) oacc[o] = zero16();
+    // running maximum (the base the scores are taken relative to) and sum
+    float m_run = 0.f, l_run = 0.f;
+
+    // Band of key block kb: distances cw-63 .. cw+31 with cw = m + iw - 64*kb.
+    // gb[kb & 1] holds the chunk cw-63 .. cw (two 32-distance blocks); the band's
+    // top part cw+1 .. cw+31 is block 0 of the previous chunk, gb[(kb+1) & 1][0],
+    // or for kb = 0 the block gtop computed here (written to LDS before the
+    // loop). rnext holds r of the next chunk.
+    // The two chunk buffers alternate with the parity of kb (the loop is unrolled
+    // by two), so no register tile is copied from one step to the next.
+    f32x16 gtop = zero16(), gb[2][2];
+    Frag<T> rnext[2][NS];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) rnext[bb][s] = Frag<T>{};
+    if (DIST && wave_has_queries && kb_lo < nkb && kb_lo * kKB <= last_key_wave) {
+        const int c0 = m + iw - kb_lo * kKB;         // >= -31: block kb_lo is visible
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            Frag<T> f;
+            load8(f, rk + (long long)(c0 + 1 + fr) * DP + 16 * s + 8 * hf);
+            mma16(gtop, f, fqv[s]);
+        }
+        r_chunk(rnext, c0 - 63);
+        g_chunk(gb[0], rnext);
+        // the next chunk only while its block is visible (keeps the reads >= -94)
+        if ((kb_lo + 1) * kKB <= last_key_wave) r_chunk(rnext, c0 - 127);
+        // the band of block 0; every later band is written at the end of the
+        // block before it, where it overlaps that block's P.V products
+        write_gblock(grow, gb[0][0], 0, hf);
+        write_gblock(grow, gb[0][1], 32, hf);
+        write_gblock(grow, gtop, 64, hf);
+    }
+
 
     // One key block; P is the parity of kb (compile time), so gb[P] / gb[Q] are
     // fixed register tiles.
@@ -381,8 +405,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         }
     };
 
-    TXL_KV_GLOAD(0);
-    for (int kb = 0; kb < nkb; kb += 2) {
+    for (int kb = kb_lo; kb < nkb; kb += 2) {
         step(std::integral_constant<int, 0>(), kb);
         if (kb + 1 < nkb) step(std::integral_constant<int, 1>(), kb + 1);
     }
@@ -391,9 +414,27 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 
     if (!wave_has_queries) return;
     const float l_tot = half_sum(l_run);
-    const float inv = 1.f / l_tot;
     const int qi = iw + fr;
     if (qi >= A.W) return;
+    if (ns > 1) {
+        // one part of a split query block: unnormalised output, base and sum
+        // (a zero sum marks a part in which this query sees no key)
+        const long long row = ((long long)split * BH + bh) * A.Wp + qi;
+        float *po = A.part_o + row * DP;
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int d = 32 * o + crow(4 * q, lane);
+                if (d < DP)
+                    *reinterpret_cast<f32x4 *>(po + d) =
+                        f32x4{oacc[o][4 * q], oacc[o][4 * q + 1], oacc[o][4 * q + 2], oacc[o][4 * q + 3]};
+            }
+        if (hf == 0)
+            *reinterpret_cast<float2 *>(A.part_ml + 2 * row) = float2{l_tot > 0.f ? m_run : -INFINITY, l_tot};
+        return;
+    }
+    const float inv = 1.f / l_tot;
     // log2 of the softmax denominator in the pre-scaled score units
     if (MODE == 1 && hf == 0) A.lse[(long long)bh * A.Wp + qi] = m_run + log2f(l_tot);
     T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.D + h * A.dh;
@@ -406,18 +447,84 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         }
 }
 
-// start/stop (may be null) are stamped by the kernel's own dispatch, so they
-// bracket exactly this kernel on its stream.
+// Merge of the key-split parts: one thread per (batch-head, query, group of 8
+// output columns). With bases m_s and sums l_s, the output is
+// sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s for M = max_s m_s, and the
+// log-sum-exp (log2 units) M + log2 of the denominator.
+template <typename T, int DP>
+__global__ void __launch_bounds__(256) attn_merge_kernel(const AttnArgs A) {
+    constexpr int G = DP / 8;
+    const int BH = A.B * A.H;
+    const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long long)BH * A.W * G) return;
+    const int g = (int)(idx % G);
+    const long long r = idx / G;
+    const int qi = (int)(r % A.W);
+    const int bh = (int)(r / A.W);
+    const long long stride = (long long)BH * A.Wp;          // rows per part
+    const long long row0 = (long long)bh * A.Wp + qi;
+    // every part's (base, sum) and output columns in one round of loads
+    float2 ml[kMaxSplit];
+    f32x4 lo[kMaxSplit], hi[kMaxSplit];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+        if (sp < A.nsplit) {
+            const long long row = row0 + sp * stride;
+            ml[sp] = *reinterpret_cast<const float2 *>(A.part_ml + 2 * row);
+            lo[sp] = *reinterpret_cast<const f32x4 *>(A.part_o + row * DP + 8 * g);
+            hi[sp] = *reinterpret_cast<const f32x4 *>(A.part_o + row * DP + 8 * g + 4);
+        } else {
+            ml[sp] = float2{-INFINITY, 0.f};
+            lo[sp] = hi[sp] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) M = fmaxf(M, ml[sp].x);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float L = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplit; ++sp) {
+        // a part with a zero sum (no visible key) has base -inf and weight 0
+        const float wgt = ml[sp].y > 0.f ? __builtin_amdgcn_exp2f(ml[sp].x - M) : 0.f;
+        L += wgt * ml[sp].y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i] += wgt * lo[sp][i];
+            acc[4 + i] += wgt * hi[sp][i];
+        }
+    }
+    const float inv = 1.f / L;
+    const int b = bh / A.H, h = bh - b * A.H;
+    T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.D + h * A.dh;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int d = 8 * g + i;
+        if (d < A.dh) orow[d] = from_f32<T>(acc[i] * inv);
+    }
+    if (A.lse && g == 0) A.lse[row0] = M + log2f(L);
+}
+
+// start/stop (may be null) are stamped by the kernels' own dispatches, so they
+// bracket exactly this launch (attention, and the merge of a key split) on its
+// stream.
 template <typename T, int DP>
 hipError_t launch_dp(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     const int nqb = (a.W + kQB - 1) / kQB;
-    dim3 grid(a.B * a.H * nqb), block(256);
+    dim3 grid(a.B * a.H * nqb * a.nsplit), block(256);
+    const bool merge = a.nsplit > 1;
+    hipEvent_t stop1 = merge ? nullptr : stop;
     if (!a.dist)
-        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 2>), grid, block, 0, s, start, stop, 0, a);
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 2>), grid, block, 0, s, start, stop1, 0, a);
     else if (a.lse)
-        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 1>), grid, block, 0, s, start, stop, 0, a);
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 1>), grid, block, 0, s, start, stop1, 0, a);
     else
-        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 0>), grid, block, 0, s, start, stop, 0, a);
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 0>), grid, block, 0, s, start, stop1, 0, a);
+    if (merge) {
+        const long long threads = (long long)a.B * a.H * a.W * (DP / 8);
+        dim3 mgrid((unsigned)((threads + 255) / 256));
+        hipExtLaunchKernelGGL((attn_merge_kernel<T, DP>), mgrid, block, 0, s, nullptr, stop, 0, a);
+    }
     return hipGetLastError();
 }
 
@@ -435,9 +542,19 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent
 }  // namespace
 
 int attn_dp(int dh) { return (dh + 15) / 16 * 16; }
+
+int attn_splits(int B, int H, int W, int K) {
+    const long long wgs = (long long)B * H * ((W + kQB - 1) / kQB);
+    if (wgs >= 512) return 1;                     // two workgroups per CU already
+    const int nkb = (K + kKB - 1) / kKB;          // key blocks of the last query block
+    const int want = (int)((512 + wgs - 1) / wgs);
+    return std::max(1, std::min(want, std::min(kMaxSplit, nkb / 4)));   // parts of >= 4 key blocks
+}
 bool rel_attn_supported(int dh) { return dh >= 1 && dh <= 64; }
 
-hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &args, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
+    AttnArgs a = args;
+    if (a.nsplit < 1 || !a.part_o || !a.part_ml) a.nsplit = 1;
     return is_bf16 ? launch_t<bf16>(a, s, start, stop) : launch_t<float>(a, s, start, stop);
 }
 

@@ -105,11 +105,20 @@ struct AttnArgs {
     long long rk_hstride;
     int dist;
     float *lse;
+    // key split: nsplit > 1 runs nsplit workgroups per query block over disjoint
+    // key ranges; each writes its unnormalised output (part_o, [split][bh][Wp][dp]
+    // fp32) and (running base, sum) pair (part_ml, [split][bh][Wp][2]), and a
+    // second kernel merges them
+    int nsplit;
+    float *part_o, *part_ml;
 };
 // start / stop: optional events stamped at this kernel's own start and end.
 hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &a, hipStream_t s, hipEvent_t start = nullptr,
                            hipEvent_t stop = nullptr);
 bool rel_attn_supported(int dh);
+// key splits for a launch over K keys: more than one only when the query blocks
+// alone cannot fill the chip; non-decreasing in K
+int attn_splits(int B, int H, int W, int K);
 int attn_dp(int dh);          // padded head width used by the attention kernel
 const int ATTN_QBLOCK = 128;  // queries per workgroup
 const int ATTN_KBLOCK = 64;   // keys per step
