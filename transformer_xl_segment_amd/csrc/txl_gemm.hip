@@ -5,9 +5,10 @@
 // layer uses: y = x W^T). Both operands are therefore contiguous along the
 // reduction axis and load straight into MFMA fragments without a transpose.
 //
-// Work split: a 256-thread workgroup computes a 128 x 128 tile of C; each of
-// its four waves owns a 64 x 64 quarter as 2 x 2 blocks of 32 x 32 MFMA
-// output. The reduction runs in k-tiles of 128 bytes per row (64 bf16 or 32
+// Work split: a 256-thread workgroup computes a BM x 128 tile of C (BM = 128,
+// or 64 when 128-row tiles would leave fewer than two workgroups per CU); each
+// of its four waves owns a (BM/2) x 64 part as (BM/64) x 2 blocks of 32 x 32
+// MFMA output. The reduction runs in k-tiles of 128 bytes per row (64 bf16 or 32
 // fp32 values), double-buffered in LDS with 16 bytes of padding per row so
 // that the fragment reads of 32 rows hit distinct banks. Global loads of the
 // next k-tile are issued before the MFMAs of the current one.
@@ -24,17 +25,18 @@ namespace txl {
 
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kThreads = 256;
+constexpr int kBN = 128, kThreads = 256;
 constexpr int kRowBytes = 128;                       // bytes per row of one k-tile
 constexpr int kPitch = kRowBytes + 16;               // LDS bytes per row
-constexpr int kChunks = kBM * (kRowBytes / 16) / kThreads;   // 16-byte chunks per thread per operand (4)
 constexpr int kPrefetch = 2;                         // k-tiles of global loads in flight
 
+template <int BM>
 struct GemmSmem {
-    char a[2][kBM * kPitch];
+    char a[2][BM * kPitch];
     char b[2][kBN * kPitch];
 };
-static_assert(sizeof(GemmSmem) >= 128 * 132 * 4, "C tile staging must fit in the operand buffers");
+static_assert(sizeof(GemmSmem<128>) >= 128 * 132 * 4, "C tile staging must fit in the operand buffers");
+static_assert(sizeof(GemmSmem<64>) >= 64 * 132 * 4, "C tile staging must fit in the operand buffers");
 
 // Fast floor(x / d) for 0 <= x < 2^22 with a float reciprocal and one fix-up.
 __device__ __forceinline__ int fdiv(int x, int d, float inv) {
@@ -132,7 +134,7 @@ __device__ __forceinline__ void load8f(float (&x)[8], const T *src) {
     }
 }
 
-// Write the 128 x 128 C tile staged in LDS (cs). Row-major destinations: a
+// Write the BM x 128 C tile staged in LDS (cs). Row-major destinations: a
 // thread owns eight consecutive columns and walks every 32nd row of the tile
 // (rows advance incrementally, no division). The transposed value output: a
 // wave covers 64 consecutive columns of one 8-row group, each lane writing
@@ -143,7 +145,7 @@ __device__ __forceinline__ int kv_slot(const GemmProblem &P, int t) {
     return s >= P.kv_slots ? s - P.kv_slots : s;
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int BM>
 __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, int m0, int n0, int tid,
                                          float inv_seg) {
     const bool trans = P.epi == EPI_KV && n0 >= P.b_split;
@@ -178,7 +180,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
         int row = m0 + rl;
         int b = fdiv(row, P.seg_rows, inv_seg);
         int t = row - b * P.seg_rows;
-        for (; rl < 128; rl += 16) {
+        for (; rl < BM; rl += 16) {
             if (row >= P.rows) break;
             float x[8];
             const f32x4 lo = *reinterpret_cast<const f32x4 *>(cs + rl * kCPitch + 8 * cg);
@@ -241,7 +243,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
     } else {
         // V^T [b][hh][c][slot]: rows of the tile are consecutive t (seg_rows % 8 == 0)
         const int lane = tid & 63, wv = tid >> 6;
-        for (int task = wv; task < 32; task += 4) {      // task = (row group rg, column half ch)
+        for (int task = wv; task < BM / 4; task += 4) {  // task = (row group rg, column half ch)
             const int rg = task >> 1, ch = task & 1;
             const int nl = 64 * ch + lane;
             const int n = n0 + nl;
@@ -260,9 +262,12 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
     }
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int BM>
 __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
-    __shared__ GemmSmem sm;
+    constexpr int MI = BM / 64;                                     // 32-row blocks per wave
+    constexpr int kChA = BM * (kRowBytes / 16) / kThreads;          // 16-byte chunks per thread, A
+    constexpr int kChB = kBN * (kRowBytes / 16) / kThreads;         // ... B
+    __shared__ GemmSmem<BM> sm;
     // XCD-aware remap: deal consecutive tiles to the same XCD.
     const int total = g.total_tiles;
     const int gid = blockIdx.x;
@@ -276,7 +281,7 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
     else P = g.p[0];
     const int lt = tile - P.tile_begin;
     const int tm = lt / P.tiles_n, tn = lt - tm * P.tiles_n;
-    const int m0 = tm * kBM, n0 = tn * kBN;
+    const int m0 = tm * BM, n0 = tn * kBN;
     const float inv_seg = 1.0f / (float)P.seg_rows;
 
     const int tid = threadIdx.x;
@@ -288,39 +293,38 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
     // Rows and chunk column this thread stages: rows tid/8 + 32c, chunk tid%8.
     const int ccol = tid & 7;
     const int bidx = P.b_bstride ? m0 / P.seg_rows : 0;    // batch entry of every row of this tile
-    const char *arow[kChunks], *brow[kChunks];
+    const char *arow[kChA], *brow[kChB];
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        arow[c] = a_row_ptr<T>(P, m0 + (tid >> 3) + 32 * c, inv_seg);
-        brow[c] = b_row_ptr<T>(P, n0 + (tid >> 3) + 32 * c, bidx);
-    }
+    for (int c = 0; c < kChA; ++c) arow[c] = a_row_ptr<T>(P, m0 + (tid >> 3) + 32 * c, inv_seg);
+#pragma unroll
+    for (int c = 0; c < kChB; ++c) brow[c] = b_row_ptr<T>(P, n0 + (tid >> 3) + 32 * c, bidx);
     const int nk = (P.kdim + BK - 1) / BK;
 
     // Global loads run kPre k-tiles ahead of the MFMAs (a ring of register
     // sets): a k-tile's MFMAs take far less time than an L2 round trip.
     constexpr int kPre = kPrefetch;
     static_assert(kPre == 2 || kPre == 3, "the ring needs two or three register sets");
-    u32x4 ra[kPre][kChunks], rb[kPre][kChunks];
+    u32x4 ra[kPre][kChA], rb[kPre][kChB];
 #define TXL_GLOAD(set_, kt_)                                              \
     do {                                                                  \
         const int k_ = (kt_) * BK + ccol * EPC;                           \
-        _Pragma("unroll") for (int c = 0; c < kChunks; ++c) {             \
-            ra[set_][c] = load_chunk<T, VEC>(arow[c], k_, P.kdim);        \
+        _Pragma("unroll") for (int c = 0; c < kChB; ++c) {                \
+            if (c < kChA) ra[set_][c] = load_chunk<T, VEC>(arow[c], k_, P.kdim); \
             rb[set_][c] = load_chunk<T, VEC>(brow[c], k_, P.kdim);        \
         }                                                                 \
     } while (0)
 #define TXL_SSTORE(set_, buf_)                                            \
     do {                                                                  \
-        _Pragma("unroll") for (int c = 0; c < kChunks; ++c) {             \
+        _Pragma("unroll") for (int c = 0; c < kChB; ++c) {                \
             const int r_ = (tid >> 3) + 32 * c;                           \
-            *reinterpret_cast<u32x4 *>(&sm.a[buf_][r_ * kPitch + ccol * 16]) = ra[set_][c]; \
+            if (c < kChA) *reinterpret_cast<u32x4 *>(&sm.a[buf_][r_ * kPitch + ccol * 16]) = ra[set_][c]; \
             *reinterpret_cast<u32x4 *>(&sm.b[buf_][r_ * kPitch + ccol * 16]) = rb[set_][c]; \
         }                                                                 \
     } while (0)
 
-    f32x16 acc[2][2];
+    f32x16 acc[MI][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
 
@@ -328,16 +332,16 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
     auto mma_tile = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            Frag<T> fa[2], fb[2];
+            Frag<T> fa[MI], fb[2];
             const int koff = (ks * 16 + fh * 8) * (int)sizeof(T);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                load8(fa[i], reinterpret_cast<const T *>(&sm.a[buf][(wm * 64 + i * 32 + fr) * kPitch + koff]));
+            for (int i = 0; i < MI; ++i)
+                load8(fa[i], reinterpret_cast<const T *>(&sm.a[buf][(wm * (BM / 2) + i * 32 + fr) * kPitch + koff]));
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 load8(fb[j], reinterpret_cast<const T *>(&sm.b[buf][(wn * 64 + j * 32 + fr) * kPitch + koff]));
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) mma16(acc[i][j], fb[j], fa[i]);   // C^T block: lane = row of C
         }
@@ -374,15 +378,15 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
     // each group of four registers four consecutive columns: one 16-byte store each.
     float *cs = reinterpret_cast<float *>(&sm);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                *reinterpret_cast<f32x4 *>(&cs[(wm * 64 + i * 32 + fr) * kCPitch + wn * 64 + j * 32 + crow(4 * q, lane)]) =
+                *reinterpret_cast<f32x4 *>(&cs[(wm * (BM / 2) + i * 32 + fr) * kCPitch + wn * 64 + j * 32 + crow(4 * q, lane)]) =
                     f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     __syncthreads();
-    epilogue<T, VEC>(P, cs, m0, n0, tid, inv_seg);
+    epilogue<T, VEC, BM>(P, cs, m0, n0, tid, inv_seg);
 #undef TXL_GLOAD
 #undef TXL_SSTORE
 }
@@ -407,17 +411,39 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p) {
     return true;
 }
 
+template <int BM>
+void launch_bm(bool is_bf16, bool vec, const GemmLaunch &g, hipStream_t s) {
+    dim3 grid(g.total_tiles), block(kThreads);
+    if (is_bf16) {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<bf16, true, BM>), grid, block, 0, s, g);
+        else hipLaunchKernelGGL((gemm_kernel<bf16, false, BM>), grid, block, 0, s, g);
+    } else {
+        if (vec) hipLaunchKernelGGL((gemm_kernel<float, true, BM>), grid, block, 0, s, g);
+        else hipLaunchKernelGGL((gemm_kernel<float, false, BM>), grid, block, 0, s, g);
+    }
+}
+
+// Launches with fewer 128-row tiles than two per CU (one wave per SIMD) take
+// 64-row tiles instead: twice the workgroups, each half the work.
+constexpr int kSmallGrid = 512;
+
 hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s) {
     if (g.total_tiles <= 0) return hipSuccess;
     bool vec = true;
     for (int i = 0; i < g.count; ++i) vec = vec && gemm_vec_ok(is_bf16, g.p[i]);
-    dim3 grid(g.total_tiles), block(kThreads);
-    if (is_bf16) {
-        if (vec) hipLaunchKernelGGL((gemm_kernel<bf16, true>), grid, block, 0, s, g);
-        else hipLaunchKernelGGL((gemm_kernel<bf16, false>), grid, block, 0, s, g);
+    if (g.total_tiles >= kSmallGrid) {
+        launch_bm<128>(is_bf16, vec, g, s);
     } else {
-        if (vec) hipLaunchKernelGGL((gemm_kernel<float, true>), grid, block, 0, s, g);
-        else hipLaunchKernelGGL((gemm_kernel<float, false>), grid, block, 0, s, g);
+        GemmLaunch g64 = g;
+        int t = 0;
+        for (int i = 0; i < g64.count; ++i) {
+            GemmProblem &P = g64.p[i];
+            P.tile_begin = t;
+            P.tile_count = ((P.rows + 63) / 64) * P.tiles_n;
+            t += P.tile_count;
+        }
+        g64.total_tiles = t;
+        launch_bm<64>(is_bf16, vec, g64, s);
     }
     return hipGetLastError();
 }
