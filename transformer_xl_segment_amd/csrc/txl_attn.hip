@@ -369,9 +369,11 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         // ---- next distance chunk (MFMA) interleaved with exp / pack / row sum (VALU)
         if constexpr (DIST) {
             g_chunk(gb[Q], rnext);
-            // prefetch for block kb+2 only while that block is still visible to the
-            // wave; this keeps every distance read >= -94 (inside the zero padding)
-            if (j0 + 2 * kKB <= last_key_wave) r_chunk(rnext, m + iw - j0 - kKB - 127);
+            // prefetch for block kb+2; once that block is past the wave's keys the
+            // distance is clamped into the zero padding (>= -94). Unconditional,
+            // so that the chunk's MFMAs share one basic block with the
+            // exponentials below and the scheduler can interleave them.
+            r_chunk(rnext, max(m + iw - j0 - kKB - 127, -94));
         }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)

@@ -391,6 +391,166 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
 #undef TXL_SSTORE
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS variant for 16-byte aligned operands. k-tiles are 64 bytes
+// per row (A rows, then B rows, four 16-byte chunks each) and travel from
+// global memory to LDS with global_load_lds (no register round trip and no
+// LDS store instructions): each wave instruction fills 1 KB of LDS, 16 rows,
+// lane l at byte 16 l, so each lane fetches the global chunk that belongs at
+// its position. Chunk c of row r sits at position c ^ ((r >> 2) & 3) of the
+// row: the 16-byte fragment reads of 16 consecutive rows then hit 16 distinct
+// bank groups. Three LDS buffers: the loads of k-tile kt+2 go into the buffer
+// of k-tile kt-1, so one barrier per k-tile orders them after every wave's
+// reads of that buffer.
+// ---------------------------------------------------------------------------
+constexpr int kLRow = 64;                                 // bytes per row of one k-tile
+
+template <int BM>
+struct GemmLdsSmem {
+    char buf[3][(BM + kBN) * kLRow];
+};
+static_assert(sizeof(GemmLdsSmem<64>) >= 64 * 132 * 4, "C staging must fit in the operand buffers");
+
+// Source of lanes whose chunk lies past kdim or in a row without data.
+__device__ __align__(16) unsigned int g_zero_chunk[4];
+
+typedef __attribute__((address_space(3))) void *lds_ptr;
+
+// s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4
+// and lgkmcnt 11:8 left at their maxima): this wave's direct-to-LDS loads have
+// written LDS.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+template <typename T, int BM>
+__global__ void __launch_bounds__(kThreads, 3) gemm_lds_kernel(const GemmLaunch g) {
+    constexpr int MI = BM / 64;                          // 32-row blocks per wave
+    constexpr int ROWS = BM + kBN;                       // rows per k-tile (A, then B)
+    constexpr int NI = ROWS / 16 / 4;                    // load instructions per wave per k-tile
+    constexpr int BK = kLRow / (int)sizeof(T);           // elements per row of a k-tile
+    constexpr int EPC = 16 / (int)sizeof(T);             // elements per chunk
+    static_assert(ROWS % 64 == 0, "whole load instructions per wave");
+    __shared__ GemmLdsSmem<BM> sm;
+
+    const int total = g.total_tiles;
+    const int gid = blockIdx.x;
+    const int full = total - (total & 7);
+    const int tile = gid < full ? (gid & 7) * (full >> 3) + (gid >> 3) : gid;
+    GemmProblem P;
+    if (g.count > 2 && tile >= g.p[2].tile_begin) P = g.p[2];
+    else if (g.count > 1 && tile >= g.p[1].tile_begin) P = g.p[1];
+    else P = g.p[0];
+    const int lt = tile - P.tile_begin;
+    const int tm = lt / P.tiles_n, tn = lt - tm * P.tiles_n;
+    const int m0 = tm * BM, n0 = tn * kBN;
+    const float inv_seg = 1.0f / (float)P.seg_rows;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int bidx = P.b_bstride ? m0 / P.seg_rows : 0;
+
+    // instruction j of this wave fills rows 16 (wave + 4 j) .. +16 of a k-tile;
+    // this lane's row and the global chunk it fetches
+    const char *src[NI];
+    int cel[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        const int row = 16 * (wave + 4 * j) + (lane >> 2);
+        cel[j] = ((lane & 3) ^ ((row >> 2) & 3)) * EPC;
+        src[j] = row < BM ? a_row_ptr<T>(P, m0 + row, inv_seg) : b_row_ptr<T>(P, n0 + row - BM, bidx);
+    }
+    const int nk = (P.kdim + BK - 1) / BK;
+    const char *zero = reinterpret_cast<const char *>(g_zero_chunk);
+    // k-tiles whose chunk at element offset cel[j] is still inside kdim (kdim is a
+    // multiple of the chunk width on this path)
+    int kin[NI];
+#pragma unroll
+    for (int j = 0; j < NI; ++j) {
+        kin[j] = src[j] ? (P.kdim - cel[j] + BK - 1) / BK : 0;
+        if (!src[j]) src[j] = zero;
+    }
+    auto issue = [&](int kt, int b) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const char *p = kt < kin[j] ? src[j] + ((long long)kt * BK + cel[j]) * (long long)sizeof(T) : zero;
+            __builtin_amdgcn_global_load_lds(p, (lds_ptr)(sm.buf[b] + 1024 * (wave + 4 * j)), 16, 0, 0);
+        }
+    };
+
+    f32x16 acc[MI][2];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+
+    const int fr = lane & 31, fh = lane >> 5;
+    const int sw = (fr >> 2) & 3;                        // this lane's row swizzle
+    auto frag = [&](Frag<T> &f, const char *bufp, int row, int e0) {
+        // elements e0 .. e0+7 of a k-tile row (one chunk for bf16, two for fp32)
+        const char *r = bufp + row * kLRow;
+        if constexpr (sizeof(T) == 2) {
+            f.v = *reinterpret_cast<const bf16x8 *>(r + (((e0 / EPC) ^ sw) << 4));
+        } else {
+            f.lo = *reinterpret_cast<const f32x4 *>(r + (((e0 / EPC) ^ sw) << 4));
+            f.hi = *reinterpret_cast<const f32x4 *>(r + (((e0 / EPC + 1) ^ sw) << 4));
+        }
+    };
+    auto mma_tile = [&](const char *bufp) {
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            Frag<T> fa[MI], fb[2];
+            const int e0 = ks * 16 + fh * 8;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) frag(fa[i], bufp, wm * (BM / 2) + i * 32 + fr, e0);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) frag(fb[j], bufp, BM + wn * 64 + j * 32 + fr, e0);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) mma16(acc[i][j], fb[j], fa[i]);   // C^T block: lane = row of C
+        }
+    };
+
+    // Each wave completes all of its loads in flight before the barrier of a
+    // k-tile (the compiler cannot tell the three buffers apart and would wait
+    // for them before the fragment reads anyway): k-tile kt+2 is requested
+    // right after the barrier of k-tile kt and complete at the barrier of
+    // k-tile kt+1, one k-tile of products later.
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    int b = 0;                                           // buffer of k-tile kt
+    for (int kt = 0; kt < nk; ++kt) {
+        // every wave's chunks of k-tile kt are in LDS, and every wave is done
+        // reading the buffer of k-tile kt-1, which k-tile kt+2 now fills
+        wait_loads();
+        __syncthreads();
+        if (kt + 2 < nk) issue(kt + 2, b == 0 ? 2 : b - 1);
+        mma_tile(sm.buf[b]);
+        b = b == 2 ? 0 : b + 1;
+    }
+    __syncthreads();                                     // all reads done before C staging
+
+    // C staged 64 rows at a time (the waves whose rows fall in that half)
+    float *cs = reinterpret_cast<float *>(&sm);
+#pragma unroll
+    for (int half = 0; half < BM / 64; ++half) {
+        if ((wm * (BM / 2)) / 64 == half) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<f32x4 *>(&cs[(wm * (BM / 2) + i * 32 + fr - 64 * half) * kCPitch + wn * 64 +
+                                                       j * 32 + crow(4 * q, lane)]) =
+                            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+        __syncthreads();
+        epilogue<T, true, 64>(P, cs, m0 + 64 * half, n0, tid, inv_seg);
+        if (half + 1 < BM / 64) __syncthreads();
+    }
+}
+
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
@@ -415,10 +575,10 @@ template <int BM>
 void launch_bm(bool is_bf16, bool vec, const GemmLaunch &g, hipStream_t s) {
     dim3 grid(g.total_tiles), block(kThreads);
     if (is_bf16) {
-        if (vec) hipLaunchKernelGGL((gemm_kernel<bf16, true, BM>), grid, block, 0, s, g);
+        if (vec) hipLaunchKernelGGL((gemm_lds_kernel<bf16, BM>), grid, block, 0, s, g);
         else hipLaunchKernelGGL((gemm_kernel<bf16, false, BM>), grid, block, 0, s, g);
     } else {
-        if (vec) hipLaunchKernelGGL((gemm_kernel<float, true, BM>), grid, block, 0, s, g);
+        if (vec) hipLaunchKernelGGL((gemm_lds_kernel<float, BM>), grid, block, 0, s, g);
         else hipLaunchKernelGGL((gemm_kernel<float, false, BM>), grid, block, 0, s, g);
     }
 }
