@@ -149,7 +149,12 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     const int rem = blockIdx.x - rank * (BH * ns);
     const int split = rem / BH;
     const int bh = rem - split * BH;
-    const int qblk = nqb - 1 - rank;                 // longest query blocks first
+    // the first half of the ranks takes the query blocks longest first, the
+    // second half shortest first: workgroup g and g + (grid / 2), which the
+    // dispatcher tends to place on the same CU, then carry complementary key
+    // ranges (the first and last query blocks, the second and second-to-last)
+    const int hq = (nqb + 1) / 2;
+    const int qblk = rank < hq ? nqb - 1 - rank : rank - hq;
     const int b = bh / A.H, h = bh - b * A.H;
     const int i0 = qblk * kQB;
 
@@ -379,6 +384,15 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) sacc[sb][i] = __builtin_amdgcn_exp2f(sacc[sb][i]);
+        // ---- band of block kb+1: its chunk (computed above) and, on top, the
+        // low half of this block's chunk. This block's band reads are complete
+        // (the content-term MFMAs consumed them); written here, the stores
+        // drain while the P.V products run.
+        if constexpr (DIST) {
+            write_gblock(grow, gb[Q][0], 0, hf);
+            write_gblock(grow, gb[Q][1], 32, hf);
+            write_gblock(grow, gb[P][0], 64, hf);
+        }
         Frag<T> fp4[4];
         float lsum[2] = {0.f, 0.f};          // two independent chains
 #pragma unroll
@@ -396,14 +410,6 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
                 load_vt(fv, sm.v + (32 * o + fr) * SM::kPitchV, 16 * p + 4 * hf);
                 mma16(oacc[o], fv, fp4[p]);
             }
-        }
-        // ---- band of block kb+1: its chunk (computed above) and, on top, the
-        // low half of this block's chunk. This block's band reads are complete
-        // (the content-term MFMAs consumed them).
-        if constexpr (DIST) {
-            write_gblock(grow, gb[Q][0], 0, hf);
-            write_gblock(grow, gb[Q][1], 32, hf);
-            write_gblock(grow, gb[P][0], 64, hf);
         }
     };
 
