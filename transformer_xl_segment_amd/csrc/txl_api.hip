@@ -80,7 +80,7 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
         L.ke = take(k_bytes);
         L.vt = take(k_bytes);
     }
-    L.rk = take((size_t)H * (L.Kp + 2 * ATTN_RPAD) * L.dp * es);
+    L.rk = take((size_t)H * rk_table_rows(L.Kp) * L.dp * es);
     L.o = take((size_t)B * W * D * es);
     if (op == TXL_OP_ATTN_VARIANT) L.lse = take((size_t)B * H * L.Wp * 4);
     L.nsplit = attn_splits(B, H, W, Kmax);
@@ -285,7 +285,8 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     r.a_mode = A_ROWS; r.a = R; r.a_ld = D; r.a_bstride = 0;
     r.b_mode = B_HEADS; r.b0 = p->WkR; r.b_split = r.cols; r.b_ld = D;
     r.dh = dh; r.dhp = dp; r.heads = H;
-    r.epi = EPI_HEADS; r.c0 = ws + L.rk;
+    r.epi = EPI_RFRAG; r.c0 = ws + L.rk;
+    r.frag_off = rk_frag_off(m); r.frag_hstride = (long long)rk_table_rows(Kp) * dp;
     g.count = var ? 2 : 3;                                           // the variants need no R W_kR^T
     int t = 0;
     for (int i = 0; i < g.count; ++i) {
@@ -298,13 +299,13 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     g.total_tiles = t;
     TXL_TRY(hip_check(launch_gemm(bf, g, s), "projection GEMM launch"));
     if (var && var->kind == TXL_POS_SHAW)
-        TXL_TRY(hip_check(launch_shaw_rows(bf, ws + L.rk, var->aK, var->clip, K, Kp, dh, dp, s),
+        TXL_TRY(hip_check(launch_shaw_rows(bf, ws + L.rk, var->aK, var->clip, K, Kp, dh, dp, rk_frag_off(m), s),
                           "distance table launch"));
 
     AttnArgs a;
     memset(&a, 0, sizeof(a));
     a.qu = ws + L.qu; a.qv = ws + L.qv; a.rk = ws + L.rk;
-    a.rk_hstride = var ? 0 : (long long)(Kp + 2 * ATTN_RPAD) * dp;   // Shaw: one table for all heads
+    a.rk_hstride = var ? 0 : (long long)rk_table_rows(Kp) * dp;      // Shaw: one table for all heads
     a.dist = !(var && var->kind == TXL_POS_ABSOLUTE);
     a.lse = var && var->kind == TXL_POS_SHAW ? (float *)(ws + L.lse) : nullptr;
     a.ke = cache ? cache->k : (const void *)(ws + L.ke);
@@ -322,7 +323,7 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
         a.nsplit = 1;
     }
     TXL_TRY(hip_check(attn_launch(bf, a, s), "attention launch"));
-    if (a.lse) TXL_TRY(hip_check(launch_shaw_values(bf, a, var->aV, var->clip, s), "value-term launch"));
+    if (a.lse) TXL_TRY(hip_check(launch_shaw_values(bf, a, var->aK, var->aV, var->clip, s), "value-term launch"));
     return TXL_OK;
 }
 

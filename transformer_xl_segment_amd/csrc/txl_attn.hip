@@ -174,8 +174,14 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     const T *qv = (const T *)A.qv + ((long long)bh * A.Wp) * DP;
     const T *ke = (const T *)A.ke + ((long long)bh * A.C) * DP;
     const T *vt = (const T *)A.vt + ((long long)bh * DP) * A.C;
-    // row 0 of rk = distance 0; ATTN_RPAD zero rows on either side
-    const T *rk = (const T *)A.rk + (long long)h * A.rk_hstride + (long long)ATTN_RPAD * DP;
+    // this head's distance-key table (rk_elem layout): ATTN_RPAD zero rows on
+    // either side of distances 0 .. K-1, in 32-row blocks starting at rows
+    // congruent to roff = (m + 1) mod 32, the residue of every distance window
+    // loaded below, so that each fragment load is one contiguous 1 KB
+    const T *rtab = (const T *)A.rk + (long long)h * A.rk_hstride;
+    const int roff = rk_frag_off(m);
+    // lowest window start congruent to m + 1 at or above distance -94
+    const int dlow = -94 + ((roff - (ATTN_RPAD - 94)) & 31);
 
     // zero the V^T rows past DP once (they pad the last 32-row block of O^T)
     for (int idx = tid; idx < (NO * 32 - DP) * (SM::kPitchV / 4); idx += 256)
@@ -191,14 +197,19 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         }
     }
 
-    // r fragments of one 64-distance chunk: distances d0 + 32*bb + fr.
+    // r fragments of 32 distances d0 + fr (d0 congruent to m + 1 mod 32): the
+    // block of table row d0 + ATTN_RPAD, column group 2s + hf, row fr.
     // Every distance a wave touches lies in [-ATTN_RPAD, Kp + ATTN_RPAD).
+    auto r_frag = [&](Frag<T> &f, int d0, int s) {
+        const long long blk = (d0 + ATTN_RPAD - roff) / 32 + 1;
+        load8(f, rtab + blk * 32 * DP + (2 * s + hf) * 256 + fr * 8);
+    };
+    // r fragments of one 64-distance chunk: distances d0 + 32*bb + fr.
     auto r_chunk = [&](Frag<T> (&f)[2][NS], int d0) {
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
-                load8(f[bb][s], rk + (long long)(d0 + 32 * bb + fr) * DP + 16 * s + 8 * hf);
+            for (int s = 0; s < NS; ++s) r_frag(f[bb][s], d0 + 32 * bb, s);
     };
     auto g_chunk = [&](f32x16 (&g)[2], const Frag<T> (&f)[2][NS]) {
 #pragma unroll
@@ -287,7 +298,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             Frag<T> f;
-            load8(f, rk + (long long)(c0 + 1 + fr) * DP + 16 * s + 8 * hf);
+            r_frag(f, c0 + 1, s);
             mma16(gtop, f, fqv[s]);
         }
         r_chunk(rnext, c0 - 63);
@@ -375,10 +386,11 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         if constexpr (DIST) {
             g_chunk(gb[Q], rnext);
             // prefetch for block kb+2; once that block is past the wave's keys the
-            // distance is clamped into the zero padding (>= -94). Unconditional,
+            // window is clamped into the zero padding (to dlow >= -94, keeping its
+            // residue mod 32). Unconditional,
             // so that the chunk's MFMAs share one basic block with the
             // exponentials below and the scheduler can interleave them.
-            r_chunk(rnext, max(m + iw - j0 - kKB - 127, -94));
+            r_chunk(rnext, max(m + iw - j0 - kKB - 127, dlow));
         }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)

@@ -232,6 +232,9 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
                         ((T *)P.c1)[(bh * P.dhp + c + i) * P.kv_slots + slot] = from_f32<T>(x[i]);
                 } else if (P.epi == EPI_KV) {
                     store8<T, true>((T *)P.c0 + (bh * P.kv_slots + kv_slot(P, t)) * P.dhp + c, x);
+                } else if (P.epi == EPI_RFRAG) {
+                    // eight consecutive columns of a row stay contiguous (c % 8 == 0)
+                    store8<T, true>((T *)P.c0 + hh * P.frag_hstride + rk_elem(t, c, P.frag_off, P.dhp), x);
                 } else {
                     store8<T, true>((T *)P.c0 + (bh * P.seg_rows + t) * P.dhp + c, x);
                 }

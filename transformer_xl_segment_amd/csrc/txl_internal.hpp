@@ -31,6 +31,8 @@ enum EpiMode {
     EPI_KV = 2,      // n < b_split: c0 head-major [b][hh][slot][c]; else c1 transposed [b][hh][c][slot],
                      // slot = (kv_base + t) mod kv_slots
     EPI_HEADS = 3,   // c0 head-major [b][hh][t][c]
+    EPI_RFRAG = 4,   // c0 distance-key table of head hh (hh * frag_hstride), row t, column c in the
+                     // fragment-major order of rk_elem (rows offset by frag_off)
 };
 
 struct GemmProblem {
@@ -63,6 +65,8 @@ struct GemmProblem {
     float qscale;
     int relu, out_f32;
     int kv_slots, kv_base;       // EPI_KV: slots per (b, hh) and slot of row t = 0 (multiples of 8)
+    int frag_off;                // EPI_RFRAG: row offset of the 32-row blocks
+    long long frag_hstride;      // EPI_RFRAG: elements per head
     long long b_bstride;         // B_ROWS: elements between the B operands of batch entries (0: one B;
                                  // nonzero requires seg_rows % 128 == 0 so no tile straddles entries)
 };
@@ -124,13 +128,31 @@ const int ATTN_QBLOCK = 128;  // queries per workgroup
 const int ATTN_KBLOCK = 64;   // keys per step
 const int ATTN_RPAD = 128;    // zero rows before and after the distance keys
 
+// Distance-key table of one head, [ATTN_RPAD + Kp + ATTN_RPAD] rows of dp columns
+// (row ATTN_RPAD + d holds distance d), stored in the order the attention
+// kernel's MFMA fragments read it: 32-row blocks whose first row is congruent
+// to off (mod 32), each block as dp/8 column groups of 32 rows x 8 columns, so
+// that one 16-byte fragment load of a wave (32 rows, 8 columns each, for both
+// halves of a column group of 16) is 1 KB contiguous. The table takes
+// rk_table_rows(Kp) rows' worth of elements (one more block than the rows).
+__host__ __device__ inline int rk_table_rows(int Kp) { return Kp + 2 * ATTN_RPAD + 32; }
+__host__ __device__ inline long long rk_elem(int row, int col, int off, int dp) {
+    const int t = (row - off + 32) >> 5;            // block of this row (row >= 0, 0 <= off < 32)
+    const int r = row - (32 * t + off - 32);        // row within the block
+    return (long long)t * 32 * dp + (col >> 3) * 256 + r * 8 + (col & 7);
+}
+// the row offset a launch with m memory keys uses: every window of distances
+// the attention kernel loads starts at a distance congruent to m + 1 (mod 32)
+__host__ __device__ inline int rk_frag_off(int m) { return (m + 1) & 31; }
+
 // Encoding variants (txl_variants.hip).
 int shaw_max_clip();
-// Shaw's distance keys: one table [ATTN_RPAD + Kp + ATTN_RPAD][dp], row ATTN_RPAD + d = aK[min(d, clip)]
+// Shaw's distance keys: one table in the rk_elem layout (row offset off), row ATTN_RPAD + d = aK[min(d, clip)]
 hipError_t launch_shaw_rows(bool is_bf16, void *rk, const void *aK, int clip, int K, int Kp, int dh, int dp,
-                            hipStream_t s);
-// Shaw's value term added to a.o, from a.qu, a.qv, a.ke, a.rk and a.lse of a finished attention launch
-hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aV, int clip, hipStream_t s);
+                            int off, hipStream_t s);
+// Shaw's value term added to a.o, from a.qu, a.qv, a.ke, a.lse of a finished attention launch and aK
+hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aK, const void *aV, int clip,
+                              hipStream_t s);
 hipError_t launch_add_positions(bool is_bf16, const void *x, long long x_bstride, void *y, long long y_bstride,
                                 int B, int W, int D, int pos0, hipStream_t s);
 

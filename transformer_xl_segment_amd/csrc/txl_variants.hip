@@ -19,11 +19,12 @@ namespace txl {
 
 namespace {
 
-// Distance keys of Shaw's encoding in the attention kernel's layout: one table
-// [ATTN_RPAD + Kp + ATTN_RPAD][dp] shared by all heads; row ATTN_RPAD + d is
-// aK[min(d, clip)] for 0 <= d < K, zeros elsewhere and in columns >= dh.
+// Distance keys of Shaw's encoding in the attention kernel's table layout
+// (rk_elem with row offset off): one table shared by all heads; row
+// ATTN_RPAD + d is aK[min(d, clip)] for 0 <= d < K, zeros elsewhere and in
+// columns >= dh.
 template <typename T>
-__global__ void shaw_rows_kernel(T *rk, const T *aK, int clip, int K, int rows, int dh, int dp) {
+__global__ void shaw_rows_kernel(T *rk, const T *aK, int clip, int K, int rows, int dh, int dp, int off) {
     const long long n = (long long)rows * dp;
     for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < n;
          idx += (long long)gridDim.x * blockDim.x) {
@@ -31,7 +32,7 @@ __global__ void shaw_rows_kernel(T *rk, const T *aK, int clip, int K, int rows, 
         const int d = r - ATTN_RPAD;
         T v = from_f32<T>(0.f);
         if (d >= 0 && d < K && c < dh) v = aK[(long long)(d < clip ? d : clip) * dh + c];
-        rk[idx] = v;
+        rk[rk_elem(r, c, off, dp)] = v;
     }
 }
 
@@ -73,7 +74,7 @@ template <> __device__ __forceinline__ float dot_dw<bf16>(uint32_t x, const floa
 }
 
 template <typename T, int DP>
-__global__ void __launch_bounds__(256) shaw_values_kernel(const T *qu, const T *qv, const T *ke, const T *rk,
+__global__ void __launch_bounds__(256) shaw_values_kernel(const T *qu, const T *qv, const T *ke, const T *aK,
                                                           const float *lse, const T *aV, T *o, int H, int W,
                                                           int Wp, int m, int Kp, int dh, int D, int clip) {
     typedef ShawSmem<T, DP> SM;
@@ -95,11 +96,12 @@ __global__ void __launch_bounds__(256) shaw_values_kernel(const T *qu, const T *
         const int r = idx / RD, u = idx - r * RD;
         sm.k[r * PD + u] = kg[idx];
     }
-    const uint32_t *ag = reinterpret_cast<const uint32_t *>(rk + (long long)ATTN_RPAD * DP);
+    // aK rows 0 .. clip-1, zero past column dh
+    T *akl = reinterpret_cast<T *>(sm.ak);
 #pragma unroll 8
-    for (int idx = threadIdx.x; idx < clip * RD; idx += 256) {
-        const int r = idx / RD, u = idx - r * RD;
-        sm.ak[r * PD + u] = ag[idx];
+    for (int idx = threadIdx.x; idx < clip * DP; idx += 256) {
+        const int r = idx / DP, c = idx - r * DP;
+        akl[r * PD * EPD + c] = c < dh ? aK[(long long)r * dh + c] : from_f32<T>(0.f);
     }
     // rows d = w, w + 4, ... of the value differences (columns >= dh are never read)
     const float tail = lane < dh ? to_f32(aV[(long long)clip * dh + lane]) : 0.f;
@@ -190,40 +192,41 @@ int grid_for(long long n) {
 int shaw_max_clip() { return kShawMaxClip; }
 
 hipError_t launch_shaw_rows(bool is_bf16, void *rk, const void *aK, int clip, int K, int Kp, int dh, int dp,
-                            hipStream_t s) {
+                            int off, hipStream_t s) {
     const int rows = Kp + 2 * ATTN_RPAD;
     const int g = grid_for((long long)rows * dp);
     if (is_bf16)
         hipLaunchKernelGGL(shaw_rows_kernel<bf16>, dim3(g), dim3(256), 0, s, (bf16 *)rk, (const bf16 *)aK, clip, K,
-                           rows, dh, dp);
+                           rows, dh, dp, off);
     else
         hipLaunchKernelGGL(shaw_rows_kernel<float>, dim3(g), dim3(256), 0, s, (float *)rk, (const float *)aK, clip,
-                           K, rows, dh, dp);
+                           K, rows, dh, dp, off);
     return hipGetLastError();
 }
 
 template <typename T, int DP>
-void launch_shaw_values_t(const AttnArgs &a, const void *aV, int clip, hipStream_t s) {
+void launch_shaw_values_t(const AttnArgs &a, const void *aK, const void *aV, int clip, hipStream_t s) {
     const int nqb = (a.W + kShawQueries - 1) / kShawQueries;
     hipLaunchKernelGGL((shaw_values_kernel<T, DP>), dim3(a.B * a.H * nqb), dim3(256), 0, s, (const T *)a.qu,
-                       (const T *)a.qv, (const T *)a.ke, (const T *)a.rk, (const float *)a.lse, (const T *)aV,
+                       (const T *)a.qv, (const T *)a.ke, (const T *)aK, (const float *)a.lse, (const T *)aV,
                        (T *)a.o, a.H, a.W, a.Wp, a.m, a.Kp, a.dh, a.D, clip);
 }
 
 template <typename T>
-hipError_t launch_shaw_values_dp(const AttnArgs &a, const void *aV, int clip, hipStream_t s) {
+hipError_t launch_shaw_values_dp(const AttnArgs &a, const void *aK, const void *aV, int clip, hipStream_t s) {
     switch (a.dp) {
-        case 16: launch_shaw_values_t<T, 16>(a, aV, clip, s); break;
-        case 32: launch_shaw_values_t<T, 32>(a, aV, clip, s); break;
-        case 48: launch_shaw_values_t<T, 48>(a, aV, clip, s); break;
-        case 64: launch_shaw_values_t<T, 64>(a, aV, clip, s); break;
+        case 16: launch_shaw_values_t<T, 16>(a, aK, aV, clip, s); break;
+        case 32: launch_shaw_values_t<T, 32>(a, aK, aV, clip, s); break;
+        case 48: launch_shaw_values_t<T, 48>(a, aK, aV, clip, s); break;
+        case 64: launch_shaw_values_t<T, 64>(a, aK, aV, clip, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aV, int clip, hipStream_t s) {
-    return is_bf16 ? launch_shaw_values_dp<bf16>(a, aV, clip, s) : launch_shaw_values_dp<float>(a, aV, clip, s);
+hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aK, const void *aV, int clip,
+                              hipStream_t s) {
+    return is_bf16 ? launch_shaw_values_dp<bf16>(a, aK, aV, clip, s) : launch_shaw_values_dp<float>(a, aK, aV, clip, s);
 }
 
 hipError_t launch_add_positions(bool is_bf16, const void *x, long long x_bstride, void *y, long long y_bstride,
