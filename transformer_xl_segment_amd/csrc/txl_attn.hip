@@ -458,13 +458,34 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     // log2 of the softmax denominator in the pre-scaled score units
     if (MODE == 1 && hf == 0) A.lse[(long long)bh * A.Wp + qi] = m_run + log2f(l_tot);
     T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.D + h * A.dh;
+    // each group of four registers holds four consecutive columns: one store
+    // per group when the row offsets keep those stores aligned
+    const bool vec4 = A.dh % 4 == 0 && A.D % 4 == 0 && A.o_bstride % 4 == 0 &&
+                      ((uintptr_t)A.o % (4 * sizeof(T))) == 0;
+    if (vec4) {
 #pragma unroll
-    for (int o = 0; o < NO; ++o)
+        for (int o = 0; o < NO; ++o)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int d = 32 * o + crow(i, lane);
-            if (d < A.dh) orow[d] = from_f32<T>(oacc[o][i] * inv);
-        }
+            for (int q = 0; q < 4; ++q) {
+                const int d = 32 * o + crow(4 * q, lane);
+                if (d < A.dh) {
+                    const float x0 = oacc[o][4 * q] * inv, x1 = oacc[o][4 * q + 1] * inv;
+                    const float x2 = oacc[o][4 * q + 2] * inv, x3 = oacc[o][4 * q + 3] * inv;
+                    if constexpr (sizeof(T) == 2)
+                        *reinterpret_cast<bf16x4 *>(orow + d) = bf16x4{(bf16)x0, (bf16)x1, (bf16)x2, (bf16)x3};
+                    else
+                        *reinterpret_cast<f32x4 *>(orow + d) = f32x4{x0, x1, x2, x3};
+                }
+            }
+    } else {
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int d = 32 * o + crow(i, lane);
+                if (d < A.dh) orow[d] = from_f32<T>(oacc[o][i] * inv);
+            }
+    }
 }
 
 // Merge of the key-split parts: one thread per (batch-head, query, group of 8

@@ -5,6 +5,8 @@
 // operands allow) so each wave moves whole cache lines.
 #include <math.h>
 
+#include <type_traits>
+
 #include "txl_device.hpp"
 #include "txl_internal.hpp"
 
@@ -13,23 +15,40 @@ namespace txl {
 namespace {
 
 // Memory update (segment-recurrence simulator: mem = last M rows of [mem; h]).
-// One workgroup row-strip per (batch, row); 16-byte or 4-byte words per lane.
+// The B * n rows to copy are one sequence of words (16 bytes, or 4 when a row
+// or a base is not 16-byte aligned); a 256-thread workgroup moves kRingUnroll
+// consecutive runs of 256 words, all loads issued before the stores.
+constexpr int kRingUnroll = 4;
+
 template <bool VEC>
-__global__ void ring_write_kernel(char *ring, int M, long long row_bytes, int pos0, const char *src,
-                                  long long src_bstride_bytes, int src_row0, int n, int B) {
-    const int r = blockIdx.x;            // r = b * n + t
-    const int b = r / n, t = r - b * n;
-    int pr = pos0 + t;
-    if (pr >= M) pr -= M;
-    char *dst = ring + ((long long)b * M + pr) * row_bytes;
-    const char *s = src + (long long)b * src_bstride_bytes + (long long)(src_row0 + t) * row_bytes;
-    if (VEC) {
-        for (long long o = threadIdx.x * 16LL; o < row_bytes; o += blockDim.x * 16LL)
-            *reinterpret_cast<u32x4 *>(dst + o) = *reinterpret_cast<const u32x4 *>(s + o);
-    } else {
-        for (long long o = threadIdx.x * 4LL; o < row_bytes; o += blockDim.x * 4LL)
-            *reinterpret_cast<uint32_t *>(dst + o) = *reinterpret_cast<const uint32_t *>(s + o);
+__global__ void __launch_bounds__(256) ring_write_kernel(char *ring, int M, long long row_bytes, int pos0,
+                                                         const char *src, long long src_bstride_bytes,
+                                                         int src_row0, int n, int B) {
+    typedef typename std::conditional<VEC, u32x4, uint32_t>::type Word;
+    constexpr int WB = (int)sizeof(Word);
+    const long long row_words = row_bytes / WB;
+    const long long total = (long long)B * n * row_words;
+    const long long base = (long long)blockIdx.x * 256 * kRingUnroll + threadIdx.x;
+    Word v[kRingUnroll];
+    char *dst[kRingUnroll];
+#pragma unroll
+    for (int u = 0; u < kRingUnroll; ++u) {
+        const long long w = base + 256LL * u;
+        dst[u] = nullptr;
+        if (w < total) {
+            const long long r = w / row_words;                 // r = b * n + t
+            const long long o = (w - r * row_words) * WB;
+            const int b = (int)(r / n), t = (int)(r - (long long)b * n);
+            int pr = pos0 + t;
+            if (pr >= M) pr -= M;
+            v[u] = *reinterpret_cast<const Word *>(src + (long long)b * src_bstride_bytes +
+                                                   (long long)(src_row0 + t) * row_bytes + o);
+            dst[u] = ring + ((long long)b * M + pr) * row_bytes + o;
+        }
     }
+#pragma unroll
+    for (int u = 0; u < kRingUnroll; ++u)
+        if (dst[u]) *reinterpret_cast<Word *>(dst[u]) = v[u];
 }
 
 // LayerNorm of the NumPy layer on "Implementing Transformer-XL":
@@ -98,7 +117,10 @@ hipError_t launch_ring_write(bool is_bf16, void *ring, int M, int D, int pos0, c
     const long long row_bytes = D * es;
     const bool vec = (row_bytes % 16 == 0) && (((uintptr_t)ring | (uintptr_t)src) % 16 == 0) &&
                      ((src_bstride * es) % 16 == 0);
-    dim3 grid(B * n), block(row_bytes >= 2048 ? 128 : 64);
+    const long long words = (long long)B * n * (row_bytes / (vec ? 16 : 4));
+    const long long per_block = 256LL * kRingUnroll;
+    dim3 grid((unsigned)((words + per_block - 1) / per_block)), block(256);
+    if (grid.x == 0) return hipSuccess;
     if (vec)
         hipLaunchKernelGGL(ring_write_kernel<true>, grid, block, 0, s, (char *)ring, M, row_bytes, pos0,
                            (const char *)src, src_bstride * es, src_row0, n, B);
