@@ -141,6 +141,63 @@ def longmem_warm(tb, torch, syn, dev, steps):
             "attn_compulsory_gbs": by / avg / 1e9, "attn_frac_hbm_peak": by / avg / 1e9 / HBM_PEAK_GBS}
 
 
+def time_mem_update(tb, torch, segs, B, M, D, dev, calls):
+    """txl_mem_update alone on the headline shape (W = M rows of D moved per
+    batch row: read from the segment, written into the ring), HIP events on the
+    stream around the calls."""
+    ring = tb.MemoryRing.empty(B, M, D, torch.bfloat16, dev)
+    for k in range(3):
+        tb.mem_update(ring, segs[k % len(segs)])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for k in range(calls):
+        tb.mem_update(ring, segs[k % len(segs)])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    W = segs[0].shape[1]
+    nbytes = 2.0 * 2 * B * min(W, M) * D
+    return {"us_per_call": us, "bytes_per_call": nbytes, "gbs": nbytes / (us * 1e-6) / 1e9,
+            "frac_hbm_peak": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+def stack_flops(wl, m):
+    """Algorithmic flops of one layer on one segment with m memory rows: attention,
+    projections (q, k_E and v over m + W rows, r, W_o) and the FFN."""
+    B, W, D, H, F = wl.B, wl.W, wl.D, wl.H, wl.F
+    return attn_flops(B, H, D // H, W, m) + proj_flops(B, W, m, D) + 4.0 * B * W * D * F
+
+
+def time_stack16(tb, torch, syn, dev, reps):
+    """The 16-layer bf16 stack's whole 8-segment schedule from empty memories
+    (txl_stack_fwd_segments), with its algorithmic TFLOP/s."""
+    bf = torch.bfloat16
+    wl = syn.WORKLOADS["stack16_bf16"]
+    B, D, H, W, M, F = wl.B, wl.D, wl.H, wl.W, wl.M, wl.F
+    prob = syn.draw_problem(wl)
+    x = torch.from_numpy(prob.x).to(dev).to(bf)
+    lp = [tb.LayerParams.from_numpy(p, bf, dev) for p in prob.params]
+    R = tb.sinusoid_table(M + W, D, bf, dev)
+    y = torch.empty_like(x)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_STACK, bf, B, W, M, D, H, F), dtype=torch.uint8, device=dev)
+
+    mems = [tb.MemoryRing.empty(B, M, D, bf, dev) for _ in lp]
+
+    def run(k):
+        for r in mems:
+            r.len, r.head = 0, 0            # empty memories: the stale rows are never read
+        tb.stack_fwd_segments(x, mems, lp, R, H, W, F, y=y, workspace=ws)
+
+    el = _timed(torch, run, reps, 1)
+    flops = sum(stack_flops(wl, m) for m in wl.mem_schedule()) * len(lp)
+    T = x.shape[1]
+    return {"workload": wl.name, "layers": len(lp), "segments": wl.S, "ms_per_schedule": el * 1e3 / reps,
+            "tokens_per_s": B * T * reps / el, "algorithmic_tflops": flops * reps / el / 1e12,
+            "frac_of_bf16_peak": flops * reps / el / 1e12 / BF16_PEAK_TFLOPS,
+            "memory_lengths": wl.mem_schedule()}
+
+
 def time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, steps, warmup):
     """The same segment stream through txl_rel_attn_fwd_cached: the memory is
     held as projected keys and values, so each segment projects W rows, not M + W."""
@@ -381,6 +438,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sliding-window", action="store_true",
                     help="skip the comparison with vanilla sliding-window evaluation")
+    ap.add_argument("--stack16-only", action="store_true",
+                    help="time only the 16-layer bf16 stack's schedule (for counter runs of its kernels)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline step (for counter runs); implies the two --no-* flags")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -400,6 +459,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.stack16_only:
+        print(json.dumps({"stack16": time_stack16(tb, torch, syn, dev, 2)}), flush=True)
+        return
     wl = syn.WORKLOADS[WORKLOAD]
     B, D, H, W, M = wl.B, wl.D, wl.H, wl.W, wl.M
     dh = D // H
@@ -413,14 +483,6 @@ def main():
     ws = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN, bf, B, W, M, D, H), dtype=torch.uint8, device=dev)
     segs = [x[:, t * W:(t + 1) * W] for t in range(wl.S)]
 
-    if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * (1 << 20) // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     def step(k):
         h = segs[k % len(segs)]
@@ -483,6 +545,8 @@ def main():
     rec["rel_attn_fwd_only"] = time_fwd_only(tb, torch, segs, ring, params, R, H, out, ws, args.steps)
     rec["schedule"] = time_schedule(tb, torch, segs, params, R, B, M, D, H, out, ws, max(3, args.steps // 8))
     rec["longmem_warm"] = longmem_warm(tb, torch, syn, dev, max(10, args.steps // 4))
+    rec["mem_update"] = time_mem_update(tb, torch, segs, B, M, D, dev, max(20, args.steps // 2))
+    rec["stack16"] = time_stack16(tb, torch, syn, dev, 2)
     kv = time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, args.steps, args.warmup)
     kv["speedup_vs_row_memory"] = kv["value"] / rec["value"]
     rec["kv_cache"] = kv

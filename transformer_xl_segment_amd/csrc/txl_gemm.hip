@@ -80,6 +80,9 @@ __device__ __forceinline__ const char *b_row_ptr(const GemmProblem &P, int n, in
 }
 
 // Load one 16-byte chunk (elements [k, k + 16/sizeof(T))) of a row, zero past kdim.
+// Without VEC the rows are only 4-byte aligned (d_model 410): a chunk wholly
+// inside kdim is still one 16-byte load (dword alignment suffices for global
+// memory), the tail chunk goes by dwords.
 template <typename T, bool VEC>
 __device__ __forceinline__ u32x4 load_chunk(const char *row, int k, int kdim) {
     u32x4 z = {0u, 0u, 0u, 0u};
@@ -88,10 +91,14 @@ __device__ __forceinline__ u32x4 load_chunk(const char *row, int k, int kdim) {
         if (k < kdim) z = *reinterpret_cast<const u32x4 *>(row + (long long)k * sizeof(T));
     } else {
         constexpr int per = 4 / sizeof(T);   // elements per dword
+        if (k + 4 * per <= kdim) {
+            __builtin_memcpy(&z, __builtin_assume_aligned(row + (long long)k * sizeof(T), 4), 16);
+        } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            int kk = k + q * per;
-            if (kk < kdim) z[q] = *reinterpret_cast<const uint32_t *>(row + (long long)kk * sizeof(T));
+            for (int q = 0; q < 4; ++q) {
+                int kk = k + q * per;
+                if (kk < kdim) z[q] = *reinterpret_cast<const uint32_t *>(row + (long long)kk * sizeof(T));
+            }
         }
     }
     return z;
@@ -117,8 +124,17 @@ __device__ __forceinline__ void store8(T *dst, const float (&x)[8]) {
             *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
         }
     } else {
+        // dword-aligned destination: one wide store of the packed values
+        if constexpr (sizeof(T) == 2) {
+            bf16x8 v;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dst[i] = from_f32<T>(x[i]);
+            for (int i = 0; i < 8; ++i) v[i] = (bf16)x[i];
+            __builtin_memcpy(__builtin_assume_aligned(dst, 4), &v, 16);
+        } else {
+            const f32x4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+            __builtin_memcpy(__builtin_assume_aligned(dst, 4), &lo, 16);
+            __builtin_memcpy(__builtin_assume_aligned((T *)dst + 4, 4), &hi, 16);
+        }
     }
 }
 
@@ -126,6 +142,11 @@ template <typename T, bool VEC>
 __device__ __forceinline__ void load8f(float (&x)[8], const T *src) {
     if (VEC && sizeof(T) == 2) {
         const bf16x8 v = *reinterpret_cast<const bf16x8 *>(src);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = to_f32(((const T *)&v)[i]);
+    } else if constexpr (sizeof(T) == 2) {
+        bf16x8 v;
+        __builtin_memcpy(&v, __builtin_assume_aligned(src, 4), 16);
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = to_f32(((const T *)&v)[i]);
     } else {
