@@ -395,9 +395,9 @@ txl_status enqueue_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const vo
 
 // Workspace of the backward pass (one region per operand, 256-byte aligned).
 struct BwdLayout {
-    size_t qu, qv, dOh, ke, vk, rk, ket, rkt, qut, dOt, qvt;   // T operands
-    size_t p, ds, dsd, pt, dst, dsdt;                          // T, per-(b, h) score matrices
-    size_t ac, bd, dpm, dq1, dq2, dkh, dvh, drh, part;         // fp32
+    size_t qu, qv, dOh, ke, vk, ket, vt, tmp, qut, dOt, qvt, rk, rt, o;   // T operands
+    size_t pt, dst, dsd;                                                // T, per-(b, h) matrices
+    size_t lse, dq1, dq2, dkh, dvh, drh, part;                           // fp32
     size_t total;
     BwdDims d;
 };
@@ -410,6 +410,7 @@ BwdLayout plan_bwd(txl_dtype dt, int B, int W, int m, int D, int H) {
     d.B = B; d.H = H; d.W = W; d.m = m; d.K = m + W; d.D = D; d.dh = D / H;
     d.dp = attn_dp(d.dh);
     d.Wp = (int)round_up(W, 128);          // GEMM tiles never straddle two (b, h) entries
+    d.W8 = (int)round_up(W, 8);            // reduction length of the dval, dk and dr GEMMs
     d.Kp = (int)round_up(d.K, 128);
     const size_t G = (size_t)B * H;
     size_t off = 0;
@@ -418,16 +419,18 @@ BwdLayout plan_bwd(txl_dtype dt, int B, int W, int m, int D, int H) {
         off = (size_t)round_up((long long)(off + bytes), 256);
         return at;
     };
-    const size_t qb = G * d.Wp * d.dp * es, kb = G * d.Kp * d.dp * es, sb = G * d.Wp * d.Kp;
-    L.qu = take(qb); L.qv = take(qb); L.dOh = take(qb);
-    L.ke = take(kb); L.vk = take(kb); L.rk = take(kb); L.ket = take(kb); L.rkt = take(kb);
-    L.qut = take(qb); L.dOt = take(qb); L.qvt = take(qb);
-    L.p = take(sb * es); L.ds = take(sb * es); L.dsd = take(sb * es);
-    L.pt = take(sb * es); L.dst = take(sb * es); L.dsdt = take(sb * es);
-    L.ac = take(sb * 4); L.bd = take(sb * 4); L.dpm = take(sb * 4);
+    const size_t qb = G * d.Wp * d.dp * es, kb = G * d.Kp * d.dp * es, sb = G * d.Kp * d.Wp * es;
+    L.qu = take(qb); L.qv = take(qb); L.dOh = take(qb); L.tmp = take(qb); L.qut = take(qb); L.dOt = take(qb);
+    L.qvt = take(qb);
+    L.ke = take(kb); L.vk = take(kb); L.ket = take(kb); L.vt = take(kb);
+    L.rk = take((size_t)H * rk_table_rows(d.Kp) * d.dp * es);
+    L.rt = take((size_t)H * d.dp * attn_bwd_rt_ld(d.Kp) * es);
+    L.o = take((size_t)B * W * D * es);
+    L.pt = take(sb); L.dst = take(sb); L.dsd = take(sb);
+    L.lse = take(G * d.Wp * 4);
     L.dq1 = take(G * d.Wp * d.dp * 4); L.dq2 = take(G * d.Wp * d.dp * 4);
     L.dkh = take(G * d.Kp * d.dp * 4); L.dvh = take(G * d.Kp * d.dp * 4);
-    L.drh = take((size_t)H * d.Kp * d.dp * 4);
+    L.drh = take(G * d.Kp * d.dp * 4);
     L.part = take((size_t)2 * H * bwd_bias_chunks(d) * 64 * 4);
     L.total = off;
     return L;
@@ -691,39 +694,45 @@ txl_status txl_rel_attn_bwd(txl_dtype dtype, int B, int W, int D, int H, int m, 
     const bool bf = dtype == TXL_BF16;
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
-    const int G = B * H, Wp = d.Wp, Kp = d.Kp, dp = d.dp;
-    // head-major operands and their transposes
-    TXL_TRY(hip_check(launch_bwd_pack(bf, d, q, k, val, r, u, v, dO, w + L.qu, w + L.qv, w + L.dOh, w + L.ke,
-                                      w + L.vk, w + L.rk, s), "backward pack launch"));
+    const int G = B * H, Wp = d.Wp, Kp = d.Kp, dp = d.dp, W8 = d.W8;
+    // head-major operands: (q + u), (q + v) pre-scaled for exp2 scores as in the forward
+    const float lam = (float)(1.4426950408889634 / sqrt((double)d.dh));
+    TXL_TRY(hip_check(launch_bwd_pack(bf, d, q, k, val, r, u, v, dO, lam, w + L.qu, w + L.qv, w + L.dOh, w + L.ke,
+                                      w + L.vk, w + L.rk, w + L.rt, s), "backward pack launch"));
+    // transposed operands: K^T and V^T for the attention kernels; (q + u)^T, (q + v)^T and dO^T
+    // per (b, h) for the GEMMs
     const long long Gk = (long long)dp * Kp, Gq = (long long)dp * Wp;
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.ke, G, H, Kp, dp, dp, w + L.ket, Gk, Kp, H * Gk, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.rk, G, H, Kp, dp, dp, w + L.rkt, Gk, Kp, H * Gk, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.qu, G, H, Wp, dp, dp, w + L.qut, Gq, Wp, H * Gq, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.dOh, G, H, Wp, dp, dp, w + L.dOt, Gq, Wp, H * Gq, s), "transpose launch"));
-    // (q + v)^T of all batch rows of one head side by side: [H][dp][B * Wp]
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.qv, G, H, Wp, dp, dp, w + L.qvt, (long long)dp * B * Wp,
-                                       (long long)B * Wp, Wp, s), "transpose launch"));
-    // (q+u) K^T, (q+v) R^T (column = distance), dO V^T
-    TXL_TRY(hip_check(launch_gemm(bf, grouped({batched_problem(G, Wp, Kp, dp, w + L.qu, dp, w + L.ke, dp, w + L.ac),
-                                                batched_problem(G, Wp, Kp, dp, w + L.qv, dp, w + L.rk, dp, w + L.bd),
-                                                batched_problem(G, Wp, Kp, dp, w + L.dOh, dp, w + L.vk, dp, w + L.dpm)}),
-                                      s), "score GEMM launch"));
-    TXL_TRY(hip_check(launch_bwd_scores(bf, d, (const float *)(w + L.ac), (const float *)(w + L.bd),
-                                        (const float *)(w + L.dpm), w + L.p, w + L.ds, w + L.dsd, s),
-                      "score gradient launch"));
-    const long long Gs = (long long)Kp * Wp;
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.p, G, H, Wp, Kp, Kp, w + L.pt, Gs, Wp, H * Gs, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.ds, G, H, Wp, Kp, Kp, w + L.dst, Gs, Wp, H * Gs, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.dsd, G, H, Wp, Kp, Kp, w + L.dsdt, (long long)Kp * B * Wp,
-                                       (long long)B * Wp, Wp, s), "transpose launch"));
-    // dS K, dS_d R, dS^T (q+u); then P^T dO and, per head over all batch rows, dS_d^T (q+v)
-    TXL_TRY(hip_check(launch_gemm(bf, grouped({batched_problem(G, Wp, dp, Kp, w + L.ds, Kp, w + L.ket, Kp, w + L.dq1),
-                                                batched_problem(G, Wp, dp, Kp, w + L.dsd, Kp, w + L.rkt, Kp, w + L.dq2),
-                                                batched_problem(G, Kp, dp, Wp, w + L.dst, Wp, w + L.qut, Wp, w + L.dkh)}),
-                                      s), "gradient GEMM launch"));
-    TXL_TRY(hip_check(launch_gemm(bf, grouped({batched_problem(G, Kp, dp, Wp, w + L.pt, Wp, w + L.dOt, Wp, w + L.dvh),
-                                                batched_problem(H, Kp, dp, B * Wp, w + L.dsdt, (long long)B * Wp,
-                                                                w + L.qvt, (long long)B * Wp, w + L.drh)}),
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.ke, Gk, G, H, Kp, dp, dp, w + L.ket, Gk, Kp, H * Gk, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.vk, Gk, G, H, Kp, dp, dp, w + L.vt, Gk, Kp, H * Gk, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.dOh, Gq, G, H, Wp, dp, dp, w + L.dOt, Gq, Wp, H * Gq, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_heads(bf, d, q, (long long)W * D, W, Wp, u, 1.f, w + L.tmp, s), "backward pack launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.tmp, Gq, G, H, Wp, dp, dp, w + L.qut, Gq, Wp, H * Gq, s), "transpose launch"));
+    TXL_TRY(hip_check(launch_heads(bf, d, q, (long long)W * D, W, Wp, v, 1.f, w + L.tmp, s), "backward pack launch"));
+    TXL_TRY(hip_check(launch_transpose(bf, w + L.tmp, Gq, G, H, Wp, dp, dp, w + L.qvt, Gq, Wp, H * Gq, s), "transpose launch"));
+    // forward once more for its output and log-sum-exp
+    AttnArgs fa;
+    memset(&fa, 0, sizeof(fa));
+    fa.qu = w + L.qu; fa.qv = w + L.qv; fa.ke = w + L.ke; fa.vt = w + L.vt; fa.rk = w + L.rk;
+    fa.o = w + L.o; fa.o_bstride = (long long)W * D;
+    fa.B = B; fa.H = H; fa.W = W; fa.Wp = Wp; fa.m = m; fa.K = d.K; fa.Kp = Kp; fa.dh = d.dh; fa.dp = dp; fa.D = D;
+    fa.C = Kp; fa.khead = 0; fa.rk_hstride = (long long)rk_table_rows(Kp) * dp; fa.dist = 1;
+    fa.lse = (float *)(w + L.lse); fa.nsplit = 1;
+    TXL_TRY(hip_check(launch_rel_attn(bf, fa, s), "attention launch"));
+    // fused query side: dq's two parts, p and dS key-major, dS by distance
+    AttnBwdArgs ba;
+    memset(&ba, 0, sizeof(ba));
+    ba.qu = w + L.qu; ba.qv = w + L.qv; ba.dO = w + L.dOh; ba.ke = w + L.ke; ba.vk = w + L.vk; ba.kt = w + L.ket;
+    ba.rk = w + L.rk; ba.rt = w + L.rt; ba.o = w + L.o; ba.lse = (const float *)(w + L.lse);
+    ba.dq1 = (float *)(w + L.dq1); ba.dq2 = (float *)(w + L.dq2);
+    ba.pt = w + L.pt; ba.dst = w + L.dst; ba.dsd = w + L.dsd;
+    ba.B = B; ba.H = H; ba.W = W; ba.Wp = Wp; ba.m = m; ba.K = d.K; ba.Kp = Kp; ba.dh = d.dh; ba.dp = dp;
+    ba.D = D; ba.rk_hstride = fa.rk_hstride; ba.rt_ld = attn_bwd_rt_ld(Kp); ba.rt_off = attn_bwd_rt_off(m);
+    ba.c = (float)(1.0 / sqrt((double)d.dh));
+    TXL_TRY(hip_check(launch_rel_attn_bwd(bf, ba, s), "attention backward launch"));
+    // dval = P^T dO, dk = dS^T (q+u) and dr's part dS_d^T (q+v) per (b, h), reduced over W8 queries
+    TXL_TRY(hip_check(launch_gemm(bf, grouped({batched_problem(G, Kp, dp, W8, w + L.pt, Wp, w + L.dOt, Wp, w + L.dvh),
+                                                batched_problem(G, Kp, dp, W8, w + L.dst, Wp, w + L.qut, Wp, w + L.dkh),
+                                                batched_problem(G, Kp, dp, W8, w + L.dsd, Wp, w + L.qvt, Wp, w + L.drh)}),
                                       s), "gradient GEMM launch"));
     return hip_check(launch_bwd_unpack(d, (const float *)(w + L.dq1), (const float *)(w + L.dq2),
                                        (const float *)(w + L.dkh), (const float *)(w + L.dvh),

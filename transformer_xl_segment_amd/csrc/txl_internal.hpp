@@ -156,25 +156,54 @@ hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aK, c
 hipError_t launch_add_positions(bool is_bf16, const void *x, long long x_bstride, void *y, long long y_bstride,
                                 int B, int W, int D, int pos0, hipStream_t s);
 
-// Backward of the relative attention (txl_backward.hip).
-struct BwdDims {
+// Backward of the relative attention: fused query side (txl_attn_bwd.hip).
+//   qu, qv, dO [B][H][Wp][dp]  (q + u), (q + v) pre-scaled as for the forward; dO unscaled
+//   ke, vk     [B][H][Kp][dp]  content keys and values;  kt [B][H][dp][Kp]  keys transposed
+//   rk         distance-key table in the rk_elem layout (row offset rk_frag_off(m)), head stride rk_hstride
+//   rt         [H][dp][rt_ld]  distance keys transposed: distance d at column d + rt_off
+//              (attn_bwd_rt_off(m), attn_bwd_rt_ld(Kp)), zero outside 0 <= d < K
+//   o          [B][W][D]  forward output;  lse [B][H][Wp]  its log-sum-exp (log2 units)
+// Writes dq1, dq2 [B][H][Wp][dp] fp32 (the content and distance parts of dq, rows < W),
+// pt, dst [B][H][Kp][Wp] (p and c p (dP - D), key-major) and dsd [B][H][Kp][Wp] (the
+// latter re-indexed by distance d = m + i - j); columns < W8 (W rounded up to 8) hold
+// data, zero where no key is visible (in particular past W); c = 1/sqrt(dh).
+struct AttnBwdArgs {
+    const void *qu, *qv, *dO, *ke, *vk, *kt, *rk, *rt, *o;
+    const float *lse;
+    float *dq1, *dq2;
+    void *pt, *dst, *dsd;
     int B, H, W, Wp, m, K, Kp, dh, dp, D;
+    long long rk_hstride;
+    int rt_ld, rt_off;
+    float c;
 };
-// q, dO [B][W][D] -> qu = q + u, qv = q + v, dOh  [G][Wp][dp]   (G = B*H, zero padding)
-// k, val [B][K][D] -> ke, vk [G][Kp][dp];  r [K][D] -> rk [G][Kp][dp] (one copy per batch row)
+hipError_t launch_rel_attn_bwd(bool is_bf16, const AttnBwdArgs &a, hipStream_t s);
+int attn_bwd_rt_off(int m);
+int attn_bwd_rt_ld(int Kp);
+
+// Operand packing and reductions of the backward (txl_backward.hip).
+struct BwdDims {
+    int B, H, W, Wp, W8, m, K, Kp, dh, dp, D;
+};
+// q, dO [B][W][D] -> qu = (q + u) * qscale, qv = (q + v) * qscale, dOh  [G][Wp][dp]   (G = B*H, zero
+// padding); k, val [B][K][D] -> ke, vk [G][Kp][dp]; r [K][D] -> rk (the attention kernels' distance-key
+// table, rk_elem layout with row offset rk_frag_off(m), rk_table_rows(Kp)*dp per head) and rt
+// ([H][dp][attn_bwd_rt_ld(Kp)], distance d at column d + attn_bwd_rt_off(m))
 hipError_t launch_bwd_pack(bool is_bf16, const BwdDims &d, const void *q, const void *k, const void *val,
-                           const void *r, const void *u, const void *v, const void *dO, void *qu, void *qv,
-                           void *dOh, void *ke, void *vk, void *rk, hipStream_t s);
-// dst[...] = src[g][row][col] transposed per batch entry g = b*H + h: element (g, row, col)
-// goes to dst + h*dst_hs + col*dst_cs + b*dst_bs + row (rows < nrow, cols < ncol)
-hipError_t launch_transpose(bool is_bf16, const void *src, int G, int H, int nrow, int ncol, long long src_ld,
-                            void *dst, long long dst_hs, long long dst_cs, long long dst_bs, hipStream_t s);
-// Per query row: scores from ac [G][Wp][Kp] and bd [G][Wp][Kp] (bd column = distance), softmax,
-// D = sum p dP, ds = p (dP - D) / sqrt(dh); writes p, ds and the distance-indexed dsd [G][Wp][Kp]
-hipError_t launch_bwd_scores(bool is_bf16, const BwdDims &d, const float *ac, const float *bd, const float *dp,
-                             void *p, void *ds, void *dsd, hipStream_t s);
+                           const void *r, const void *u, const void *v, const void *dO, float qscale, void *qu,
+                           void *qv, void *dOh, void *ke, void *vk, void *rk, void *rt, hipStream_t s);
+// dst[(b*H + h)][t][c] = (src[b][t][h*dh + c] + bias[h*dh + c]) * scale, t < nrows, c < dh (bias may be
+// null); zero up to nrows_p rows and dp columns
+hipError_t launch_heads(bool is_bf16, const BwdDims &d, const void *src, long long src_bs, int nrows, int nrows_p,
+                        const void *bias, float scale, void *dst, hipStream_t s);
+// dst[...] = src[g][row][col] transposed per batch entry g = b*H + h: element (g, row, col) at
+// src + g*src_gs + row*src_ld + col goes to dst + h*dst_hs + col*dst_cs + b*dst_bs + row
+// (rows < nrow, cols < ncol)
+hipError_t launch_transpose(bool is_bf16, const void *src, long long src_gs, int G, int H, int nrow, int ncol,
+                            long long src_ld, void *dst, long long dst_hs, long long dst_cs, long long dst_bs,
+                            hipStream_t s);
 // dq = dq1 + dq2 (head-major fp32) -> [B][W][D]; du, dv = column sums of dq1, dq2;
-// dk, dval [G][Kp][dp] -> [B][K][D]; dr [H][Kp][dp] -> [K][D]
+// dk, dval [G][Kp][dp] -> [B][K][D]; dr [G][Kp][dp] summed over the batch -> [K][D]
 // (part: scratch of 2 * H * bwd_bias_chunks(d) * 64 floats)
 int bwd_bias_chunks(const BwdDims &d);
 hipError_t launch_bwd_unpack(const BwdDims &d, const float *dq1, const float *dq2, const float *dkh,
