@@ -395,9 +395,9 @@ txl_status enqueue_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const vo
 
 // Workspace of the backward pass (one region per operand, 256-byte aligned).
 struct BwdLayout {
-    size_t qu, qv, dOh, ke, vk, ket, vt, tmp, qut, dOt, qvt, rk, rt, o;   // T operands
-    size_t pt, dst, dsd;                                                // T, per-(b, h) matrices
-    size_t lse, dq1, dq2, dkh, dvh, drh, part;                           // fp32
+    size_t qu, qv, dOh, qut, qvt, dOt, ke, vk, ket, vt, rk, rt, o;   // T operands
+    size_t pt, dst, dsd;                                            // T, per-(b, h) matrices
+    size_t lse, drh, part;                                          // fp32
     size_t total;
     BwdDims d;
 };
@@ -420,18 +420,15 @@ BwdLayout plan_bwd(txl_dtype dt, int B, int W, int m, int D, int H) {
         return at;
     };
     const size_t qb = G * d.Wp * d.dp * es, kb = G * d.Kp * d.dp * es, sb = G * d.Kp * d.Wp * es;
-    L.qu = take(qb); L.qv = take(qb); L.dOh = take(qb); L.tmp = take(qb); L.qut = take(qb); L.dOt = take(qb);
-    L.qvt = take(qb);
+    L.qu = take(qb); L.qv = take(qb); L.dOh = take(qb); L.qut = take(qb); L.qvt = take(qb); L.dOt = take(qb);
     L.ke = take(kb); L.vk = take(kb); L.ket = take(kb); L.vt = take(kb);
     L.rk = take((size_t)H * rk_table_rows(d.Kp) * d.dp * es);
     L.rt = take((size_t)H * d.dp * attn_bwd_rt_ld(d.Kp) * es);
     L.o = take((size_t)B * W * D * es);
     L.pt = take(sb); L.dst = take(sb); L.dsd = take(sb);
     L.lse = take(G * d.Wp * 4);
-    L.dq1 = take(G * d.Wp * d.dp * 4); L.dq2 = take(G * d.Wp * d.dp * 4);
-    L.dkh = take(G * d.Kp * d.dp * 4); L.dvh = take(G * d.Kp * d.dp * 4);
     L.drh = take(G * d.Kp * d.dp * 4);
-    L.part = take((size_t)2 * H * bwd_bias_chunks(d) * 64 * 4);
+    L.part = take((size_t)2 * H * bwd_parts(d) * 64 * 4);
     L.total = off;
     return L;
 }
@@ -695,20 +692,14 @@ txl_status txl_rel_attn_bwd(txl_dtype dtype, int B, int W, int D, int H, int m, 
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
     const int G = B * H, Wp = d.Wp, Kp = d.Kp, dp = d.dp, W8 = d.W8;
-    // head-major operands: (q + u), (q + v) pre-scaled for exp2 scores as in the forward
+    // packed operands: (q + u), (q + v) pre-scaled for exp2 scores as in the forward, and the
+    // transposed copies the attention kernels and the GEMMs take
     const float lam = (float)(1.4426950408889634 / sqrt((double)d.dh));
-    TXL_TRY(hip_check(launch_bwd_pack(bf, d, q, k, val, r, u, v, dO, lam, w + L.qu, w + L.qv, w + L.dOh, w + L.ke,
-                                      w + L.vk, w + L.rk, w + L.rt, s), "backward pack launch"));
-    // transposed operands: K^T and V^T for the attention kernels; (q + u)^T, (q + v)^T and dO^T
-    // per (b, h) for the GEMMs
-    const long long Gk = (long long)dp * Kp, Gq = (long long)dp * Wp;
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.ke, Gk, G, H, Kp, dp, dp, w + L.ket, Gk, Kp, H * Gk, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.vk, Gk, G, H, Kp, dp, dp, w + L.vt, Gk, Kp, H * Gk, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.dOh, Gq, G, H, Wp, dp, dp, w + L.dOt, Gq, Wp, H * Gq, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_heads(bf, d, q, (long long)W * D, W, Wp, u, 1.f, w + L.tmp, s), "backward pack launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.tmp, Gq, G, H, Wp, dp, dp, w + L.qut, Gq, Wp, H * Gq, s), "transpose launch"));
-    TXL_TRY(hip_check(launch_heads(bf, d, q, (long long)W * D, W, Wp, v, 1.f, w + L.tmp, s), "backward pack launch"));
-    TXL_TRY(hip_check(launch_transpose(bf, w + L.tmp, Gq, G, H, Wp, dp, dp, w + L.qvt, Gq, Wp, H * Gq, s), "transpose launch"));
+    BwdPack pk;
+    pk.qu = w + L.qu; pk.qv = w + L.qv; pk.dOh = w + L.dOh; pk.qut = w + L.qut; pk.qvt = w + L.qvt;
+    pk.dOt = w + L.dOt; pk.ke = w + L.ke; pk.vk = w + L.vk; pk.ket = w + L.ket; pk.vt = w + L.vt;
+    pk.rk = w + L.rk; pk.rt = w + L.rt;
+    TXL_TRY(hip_check(launch_bwd_pack(bf, d, pk, q, k, val, r, u, v, dO, lam, s), "backward pack launch"));
     // forward once more for its output and log-sum-exp
     AttnArgs fa;
     memset(&fa, 0, sizeof(fa));
@@ -718,27 +709,29 @@ txl_status txl_rel_attn_bwd(txl_dtype dtype, int B, int W, int D, int H, int m, 
     fa.C = Kp; fa.khead = 0; fa.rk_hstride = (long long)rk_table_rows(Kp) * dp; fa.dist = 1;
     fa.lse = (float *)(w + L.lse); fa.nsplit = 1;
     TXL_TRY(hip_check(launch_rel_attn(bf, fa, s), "attention launch"));
-    // fused query side: dq's two parts, p and dS key-major, dS by distance
+    // fused query side: dq, du / dv partials, p and dS key-major, dS by distance
     AttnBwdArgs ba;
     memset(&ba, 0, sizeof(ba));
     ba.qu = w + L.qu; ba.qv = w + L.qv; ba.dO = w + L.dOh; ba.ke = w + L.ke; ba.vk = w + L.vk; ba.kt = w + L.ket;
     ba.rk = w + L.rk; ba.rt = w + L.rt; ba.o = w + L.o; ba.lse = (const float *)(w + L.lse);
-    ba.dq1 = (float *)(w + L.dq1); ba.dq2 = (float *)(w + L.dq2);
+    ba.dq = dq; ba.part = (float *)(w + L.part);
     ba.pt = w + L.pt; ba.dst = w + L.dst; ba.dsd = w + L.dsd;
     ba.B = B; ba.H = H; ba.W = W; ba.Wp = Wp; ba.m = m; ba.K = d.K; ba.Kp = Kp; ba.dh = d.dh; ba.dp = dp;
     ba.D = D; ba.rk_hstride = fa.rk_hstride; ba.rt_ld = attn_bwd_rt_ld(Kp); ba.rt_off = attn_bwd_rt_off(m);
     ba.c = (float)(1.0 / sqrt((double)d.dh));
     TXL_TRY(hip_check(launch_rel_attn_bwd(bf, ba, s), "attention backward launch"));
-    // dval = P^T dO, dk = dS^T (q+u) and dr's part dS_d^T (q+v) per (b, h), reduced over W8 queries
-    TXL_TRY(hip_check(launch_gemm(bf, grouped({batched_problem(G, Kp, dp, W8, w + L.pt, Wp, w + L.dOt, Wp, w + L.dvh),
-                                                batched_problem(G, Kp, dp, W8, w + L.dst, Wp, w + L.qut, Wp, w + L.dkh),
-                                                batched_problem(G, Kp, dp, W8, w + L.dsd, Wp, w + L.qvt, Wp, w + L.drh)}),
-                                      s), "gradient GEMM launch"));
-    return hip_check(launch_bwd_unpack(d, (const float *)(w + L.dq1), (const float *)(w + L.dq2),
-                                       (const float *)(w + L.dkh), (const float *)(w + L.dvh),
-                                       (const float *)(w + L.drh), dq, dk, dval, dr, du, dv,
-                                       (float *)(w + L.part), s),
-                     "backward unpack launch");
+    // dval = P^T dO and dk = dS^T (q+u) per (b, h), written straight into [B][K][D]; dr's part
+    // dS_d^T (q+v) per (b, h); all reduced over W8 queries
+    GemmProblem gv = batched_problem(G, Kp, dp, W8, w + L.pt, Wp, w + L.dOt, Wp, dval);
+    GemmProblem gk = batched_problem(G, Kp, dp, W8, w + L.dst, Wp, w + L.qut, Wp, dk);
+    for (GemmProblem *p : {&gv, &gk}) {
+        p->epi = EPI_GROWS; p->heads = H; p->dh = d.dh; p->dhp = dp;
+        p->c_ld = D; p->c_bstride = (long long)d.K * D; p->c_rows = d.K;
+    }
+    GemmProblem gr = batched_problem(G, Kp, dp, W8, w + L.dsd, Wp, w + L.qvt, Wp, w + L.drh);
+    TXL_TRY(hip_check(launch_gemm(bf, grouped({gv, gk, gr}), s), "gradient GEMM launch"));
+    return hip_check(launch_bwd_finish(d, (const float *)(w + L.drh), (const float *)(w + L.part), dr, du, dv, s),
+                     "backward reduction launch");
 }
 
 int txl_kv_cache_capacity(int M, int W) {

@@ -367,7 +367,16 @@ __global__ void __launch_bounds__(256, 1) rel_attn_bwd_kernel(const AttnBwdArgs 
         if (kb + 1 < nkb) step(std::integral_constant<int, 1>(), kb + 1);
     }
 
-    if (!wave_has_queries) return;
+    // du, dv partials: slot (b, query block, wave) of each head holds the column sums of
+    // dq's two parts over the wave's queries (lanes past W hold exact zeros)
+    const int nparts = A.B * nqb * kWaves;
+    float *pu = A.part + ((long long)h * nparts + (b * nqb + qblk) * kWaves + w) * 64;
+    float *pv = pu + (long long)A.H * nparts * 64;
+    if (!wave_has_queries) {
+        pu[lane] = 0.f;
+        pv[lane] = 0.f;
+        return;
+    }
     // the distances the last block left open
     flush(m + iw - kb_last * kKB - 96, (kKB - kKB * kb_last) & (kRing - 1), kb_last * kKB + kKB - 1);
     // zeros where no key of the wave is visible: key rows past its last block,
@@ -377,18 +386,40 @@ __global__ void __launch_bounds__(256, 1) rel_attn_bwd_kernel(const AttnBwdArgs 
         dst[(long long)j * A.Wp + qi] = from_f32<T>(0.f);
     }
     for (int d = m + iw + 32 + hf; d < A.Kp; d += 2) dsd[(long long)d * A.Wp + qi] = from_f32<T>(0.f);
+    // column sums through the wave's band buffer (free now): row a = query, column c
+    {
+        constexpr int CP = 68;                           // 32 x 68 floats fit the 32 x kGPitch buffer
+        float *buf = sm.g[w];
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            wave_lds_sync();
+#pragma unroll
+            for (int o = 0; o < NO; ++o)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int c = 32 * o + crow(4 * q, lane);
+                    const f32x16 &acc = pass ? dqv[o] : dqu[o];
+                    if (c < DP)
+                        *reinterpret_cast<f32x4 *>(buf + fr * CP + c) =
+                            f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+                }
+            wave_lds_sync();
+            float sum = 0.f;
+            if (lane < DP)
+#pragma unroll 8
+                for (int a = 0; a < 32; ++a) sum += buf[a * CP + lane];
+            (pass ? pv : pu)[lane] = sum;
+        }
+    }
     if (!q_ok) return;
-    float *o1 = A.dq1 + ((long long)bh * A.Wp + qi) * DP;
-    float *o2 = A.dq2 + ((long long)bh * A.Wp + qi) * DP;
+    // dq = content part + distance part, row layout [B][W][D]
+    float *dqrow = A.dq + ((long long)b * A.W + qi) * A.D + h * A.dh;
 #pragma unroll
     for (int o = 0; o < NO; ++o)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = 32 * o + crow(4 * q, lane);
-            if (c < DP) {
-                *reinterpret_cast<f32x4 *>(o1 + c) = f32x4{dqu[o][4 * q], dqu[o][4 * q + 1], dqu[o][4 * q + 2], dqu[o][4 * q + 3]};
-                *reinterpret_cast<f32x4 *>(o2 + c) = f32x4{dqv[o][4 * q], dqv[o][4 * q + 1], dqv[o][4 * q + 2], dqv[o][4 * q + 3]};
-            }
+        for (int i = 0; i < 16; ++i) {
+            const int c = 32 * o + crow(i, lane);
+            if (c < A.dh) dqrow[c] = dqu[o][i] + dqv[o][i];
         }
 }
 

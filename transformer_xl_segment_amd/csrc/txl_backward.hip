@@ -15,61 +15,123 @@ namespace txl {
 
 namespace {
 
-// dst[(b*H + h)][t][c] = (src[b][t][h*dh + c] (+ bias[h*dh + c])) * scale for t < nrows, c < dh;
-// zero elsewhere (t < nrows_p, c < dp). One thread per eight consecutive columns: one or two
-// 16-byte stores (dp is a multiple of 16).
-template <typename T>
-__global__ void heads_kernel(const T *src, long long src_bs, int B, int nrows, int nrows_p, int D, int H, int dh,
-                             int dp, const T *bias, float scale, T *dst) {
-    const int c8n = dp >> 3;
-    const int n = B * H * nrows_p * c8n;
-    for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += gridDim.x * blockDim.x) {
-        const int c0 = (idx % c8n) * 8;
-        const int rt = idx / c8n;
-        const int t = rt % nrows_p, g = rt / nrows_p;
-        const int b = g / H, h = g - b * H;
-        float x[8];
+// One pass over the rows of a [B][nrows][D] operand, per head h of entry g = b*H + h and
+// k = 0, 1 (bias0 / bias1, either may be null; out*1 null: k = 0 only), x = src[b][t][h*dh + c]:
+//   hm_k[g][t][c] = (x + bias_k[h*dh + c]) * hm_scale      t < nrows_p, c < dp   (head-major)
+//   tr_k[g][c][t] = x + bias_k[h*dh + c]                   c < dp, t < nrows_p   (transposed)
+// zero for t >= nrows or c >= dh. A workgroup owns 64 rows of one entry: loads and head-major
+// stores along c, transposed stores along t through an LDS tile. VEC (16-byte aligned rows,
+// dh % 8 == 0): a thread moves eight consecutive elements per access.
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256) pack_kernel(const T *src, long long src_bs, int nrows, int nrows_p, int D,
+                                                   int H, int dh, int dp, const T *bias0, const T *bias1,
+                                                   float hm_scale, T *hm0, T *hm1, T *tr0, T *tr1) {
+    __shared__ float tile[64][65];
+    const int g = blockIdx.y, b = g / H, h = g - b * H;
+    const int t0 = blockIdx.x * 64;
+    const int tid = threadIdx.x;
+    const bool two = hm1 || tr1;
+    const T *s = src + (long long)b * src_bs + h * dh;
+    constexpr int E = VEC ? 8 : 1;                       // elements per access
+    constexpr int TPR = 64 / E;                          // threads per row of 64 columns
+    constexpr int RPI = 256 / TPR;                       // rows per iteration
+    const int c0 = (tid % TPR) * E;
+    float bb0[E], bb1[E];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = 0.f;
-        if (t < nrows) {
-            const T *row = src + (long long)b * src_bs + (long long)t * D + h * dh;
+    for (int e = 0; e < E; ++e) {
+        bb0[e] = (bias0 && c0 + e < dh) ? to_f32(bias0[h * dh + c0 + e]) : 0.f;
+        bb1[e] = (bias1 && c0 + e < dh) ? to_f32(bias1[h * dh + c0 + e]) : 0.f;
+    }
+    for (int rr = tid / TPR; rr < 64; rr += RPI) {
+        const int t = t0 + rr;
+        float x[E];
+        if constexpr (VEC) {
+            if (t < nrows && c0 < dh) {
+                if constexpr (sizeof(T) == 2) {
+                    const bf16x8 v = *reinterpret_cast<const bf16x8 *>(s + (long long)t * D + c0);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int c = c0 + k;
-                if (c < dh) x[k] = (to_f32(row[c]) + (bias ? to_f32(bias[h * dh + c]) : 0.f)) * scale;
+                    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+                } else {
+                    const f32x4 lo = *reinterpret_cast<const f32x4 *>(s + (long long)t * D + c0);
+                    const f32x4 hi = *reinterpret_cast<const f32x4 *>(s + (long long)t * D + c0 + 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { x[e] = lo[e]; x[4 + e] = hi[e]; }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[e] = 0.f;
+            }
+        } else {
+            x[0] = (t < nrows && c0 < dh) ? to_f32(s[(long long)t * D + c0]) : 0.f;
+        }
+        const bool rin = t < nrows;
+#pragma unroll
+        for (int e = 0; e < E; ++e) tile[rr][c0 + e] = x[e];
+        if (c0 < dp && t < nrows_p) {
+            T *o0 = hm0 + ((long long)g * nrows_p + t) * dp + c0;
+            T *o1 = two && hm1 ? hm1 + ((long long)g * nrows_p + t) * dp + c0 : nullptr;
+            float y0[E], y1[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const bool in = rin && c0 + e < dh;
+                y0[e] = in ? (x[e] + bb0[e]) * hm_scale : 0.f;
+                y1[e] = in ? (x[e] + bb1[e]) * hm_scale : 0.f;
+            }
+            if constexpr (VEC && sizeof(T) == 2) {
+                if (hm0) *reinterpret_cast<bf16x8 *>(o0) = bf16x8{(bf16)y0[0], (bf16)y0[1], (bf16)y0[2], (bf16)y0[3],
+                                                                  (bf16)y0[4], (bf16)y0[5], (bf16)y0[6], (bf16)y0[7]};
+                if (o1) *reinterpret_cast<bf16x8 *>(o1) = bf16x8{(bf16)y1[0], (bf16)y1[1], (bf16)y1[2], (bf16)y1[3],
+                                                                 (bf16)y1[4], (bf16)y1[5], (bf16)y1[6], (bf16)y1[7]};
+            } else if constexpr (VEC) {
+                if (hm0) {
+                    *reinterpret_cast<f32x4 *>(o0) = f32x4{y0[0], y0[1], y0[2], y0[3]};
+                    *reinterpret_cast<f32x4 *>(o0 + 4) = f32x4{y0[4], y0[5], y0[6], y0[7]};
+                }
+                if (o1) {
+                    *reinterpret_cast<f32x4 *>(o1) = f32x4{y1[0], y1[1], y1[2], y1[3]};
+                    *reinterpret_cast<f32x4 *>(o1 + 4) = f32x4{y1[4], y1[5], y1[6], y1[7]};
+                }
+            } else {
+                if (hm0) o0[0] = from_f32<T>(y0[0]);
+                if (o1) o1[0] = from_f32<T>(y1[0]);
             }
         }
-        T *out = dst + (long long)idx * 8;
-        if constexpr (sizeof(T) == 2) {
-            *reinterpret_cast<bf16x8 *>(out) = bf16x8{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3],
-                                                      (bf16)x[4], (bf16)x[5], (bf16)x[6], (bf16)x[7]};
-        } else {
-            *reinterpret_cast<f32x4 *>(out) = f32x4{x[0], x[1], x[2], x[3]};
-            *reinterpret_cast<f32x4 *>(out + 4) = f32x4{x[4], x[5], x[6], x[7]};
-        }
     }
-}
-
-// 64 x 64 tiles through LDS: element (g, row, col) of src (entry g at g*src_gs, rows
-// src_ld apart) goes to dst + h*dst_hs + col*dst_cs + b*dst_bs + row with g = b*H + h.
-template <typename T>
-__global__ void __launch_bounds__(256) transpose_kernel(const T *src, long long src_gs, int H, int nrow, int ncol,
-                                                        long long src_ld, T *dst, long long dst_hs,
-                                                        long long dst_cs, long long dst_bs) {
-    __shared__ T tile[64][65];
-    const int g = blockIdx.z, b = g / H, h = g - b * H;
-    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    const T *s = src + (long long)g * src_gs;
-    for (int rr = ty; rr < 64; rr += 4) {
-        const int r = r0 + rr, c = c0 + tx;
-        tile[rr][tx] = (r < nrow && c < ncol) ? s[(long long)r * src_ld + c] : from_f32<T>(0.f);
-    }
+    if (!tr0 && !tr1) return;                           // uniform over the workgroup
     __syncthreads();
-    T *d = dst + (long long)h * dst_hs + (long long)b * dst_bs;
-    for (int cc = ty; cc < 64; cc += 4) {
-        const int c = c0 + cc, r = r0 + tx;
-        if (c < ncol && r < nrow) d[(long long)c * dst_cs + r] = tile[tx][cc];
+    // transposed: thread (c, group of E rows); column c of rows t0 + tt .. + E
+    for (int idx = tid; idx < dp * TPR; idx += 256) {
+        const int c = idx / TPR, tt = (idx % TPR) * E;
+        const bool cin = c < dh;
+        const float b0 = (bias0 && cin) ? to_f32(bias0[h * dh + c]) : 0.f;
+        const float b1 = (bias1 && cin) ? to_f32(bias1[h * dh + c]) : 0.f;
+        float y0[E], y1[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool in = cin && t0 + tt + e < nrows;
+            const float x = tile[tt + e][c];
+            y0[e] = in ? x + b0 : 0.f;
+            y1[e] = in ? x + b1 : 0.f;
+        }
+        const long long o = ((long long)g * dp + c) * nrows_p + t0 + tt;
+        if constexpr (VEC && sizeof(T) == 2) {
+            if (tr0) *reinterpret_cast<bf16x8 *>(tr0 + o) = bf16x8{(bf16)y0[0], (bf16)y0[1], (bf16)y0[2], (bf16)y0[3],
+                                                                   (bf16)y0[4], (bf16)y0[5], (bf16)y0[6], (bf16)y0[7]};
+            if (two && tr1) *reinterpret_cast<bf16x8 *>(tr1 + o) = bf16x8{(bf16)y1[0], (bf16)y1[1], (bf16)y1[2], (bf16)y1[3],
+                                                                          (bf16)y1[4], (bf16)y1[5], (bf16)y1[6], (bf16)y1[7]};
+        } else if constexpr (VEC) {
+            if (tr0) {
+                *reinterpret_cast<f32x4 *>(tr0 + o) = f32x4{y0[0], y0[1], y0[2], y0[3]};
+                *reinterpret_cast<f32x4 *>(tr0 + o + 4) = f32x4{y0[4], y0[5], y0[6], y0[7]};
+            }
+            if (two && tr1) {
+                *reinterpret_cast<f32x4 *>(tr1 + o) = f32x4{y1[0], y1[1], y1[2], y1[3]};
+                *reinterpret_cast<f32x4 *>(tr1 + o + 4) = f32x4{y1[4], y1[5], y1[6], y1[7]};
+            }
+        } else {
+            if (tr0) tr0[o] = from_f32<T>(y0[0]);
+            if (two && tr1) tr1[o] = from_f32<T>(y1[0]);
+        }
     }
 }
 
@@ -105,79 +167,37 @@ __global__ void rt_table_kernel(const T *r, int K, int D, int H, int dh, int dp,
     }
 }
 
-// dq = dq1 + dq2 and the unpacking of dk, dval and (summed over the batch) dr into row layouts;
-// one thread per output element (every count here is below 2^30).
-__global__ void bwd_unpack_kernel(BwdDims d, const float *dq1, const float *dq2, const float *dkh,
-                                  const float *dvh, const float *drh, float *dq, float *dk, float *dval,
-                                  float *dr) {
-    const int nq = d.B * d.W * d.D, nk = d.B * d.K * d.D, nr = d.K * d.D;
-    for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < nq + 2 * nk + nr; idx += gridDim.x * blockDim.x) {
-        if (idx < nq) {
-            const int col = idx % d.D, bt = idx / d.D;
-            const int t = bt % d.W, b = bt / d.W;
-            const int h = col / d.dh, c = col - h * d.dh;
-            const long long src = (((long long)b * d.H + h) * d.Wp + t) * d.dp + c;
-            dq[idx] = dq1[src] + dq2[src];
-        } else if (idx < nq + 2 * nk) {
-            const bool isv = idx >= nq + nk;
-            const int e = idx - nq - (isv ? nk : 0);
-            const int col = e % d.D, bj = e / d.D;
-            const int j = bj % d.K, b = bj / d.K;
-            const int h = col / d.dh, c = col - h * d.dh;
-            const long long src = (((long long)b * d.H + h) * d.Kp + j) * d.dp + c;
-            if (isv) dval[e] = dvh[src];
-            else dk[e] = dkh[src];
-        } else {
-            const int e = idx - nq - 2 * nk;
-            const int col = e % d.D, j = e / d.D;
-            const int h = col / d.dh, c = col - h * d.dh;
-            const long long gs = (long long)d.H * d.Kp * d.dp;         // between batch rows
-            const float *p = drh + ((long long)h * d.Kp + j) * d.dp + c;
-            float s = 0.f;
-            for (int b = 0; b < d.B; ++b) s += p[b * gs];
-            dr[e] = s;
-        }
+// dr[j][h*dh + c] = sum over batch rows b of drh[b*H + h][j][c]; one thread per element.
+__global__ void bwd_dr_kernel(BwdDims d, const float *drh, float *dr) {
+    const int n = d.K * d.D;
+    const long long gs = (long long)d.H * d.Kp * d.dp;          // between batch rows
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) {
+        const int col = e % d.D, j = e / d.D;
+        const int h = col / d.dh, c = col - h * d.dh;
+        const float *p = drh + ((long long)h * d.Kp + j) * d.dp + c;
+        float s = 0.f;
+        for (int b = 0; b < d.B; ++b) s += p[b * gs];
+        dr[e] = s;
     }
 }
 
-// du, dv: per head, column sums of dq1 (resp. dq2) over every (b, t < W) row,
-// in two stages: workgroup (h, which, chunk) sums one chunk of kBiasChunk rows
-// into part[which][h][chunk][c]; then workgroup (h, which) adds the chunks.
-constexpr int kBiasChunk = 256;
-
-__global__ void __launch_bounds__(256) bwd_bias_partial_kernel(BwdDims d, const float *dq1, const float *dq2,
-                                                               float *part, int nchunk) {
+// du, dv: workgroup (which, h) adds that head's nparts per-wave column sums in a fixed order.
+__global__ void __launch_bounds__(256) bwd_bias_kernel(BwdDims d, const float *part, int nparts, float *du,
+                                                       float *dv) {
     __shared__ float red[4][64];
-    const int chunk = blockIdx.x % nchunk;
-    const int hw = blockIdx.x / nchunk;                  // h * 2 + which
-    const int h = hw >> 1;
-    const float *src = (hw & 1) ? dq2 : dq1;
+    const int which = blockIdx.x / d.H, h = blockIdx.x - which * d.H;
     const int c = threadIdx.x & 63, grp = threadIdx.x >> 6;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (c < d.dh) {
-        const int r1 = min((chunk + 1) * kBiasChunk, d.B * d.W);
-        int k = 0;
-        for (int row = chunk * kBiasChunk + grp; row < r1; row += 4, k = (k + 1) & 3) {   // row = b * W + t
-            const int b = row / d.W, t = row - b * d.W;
-            acc[k] += src[(((long long)b * d.H + h) * d.Wp + t) * d.dp + c];
-        }
-    }
-    red[grp][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const float *p = part + ((long long)which * d.H + h) * nparts * 64 + c;
+    // eight independent chains (the loads of one round are all in flight together)
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int k = grp;
+    for (; k + 28 < nparts; k += 32)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += p[(long long)(k + 4 * u) * 64];
+    for (int u = 0; k < nparts; k += 4, ++u) acc[u] += p[(long long)k * 64];
+    red[grp][c] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
     __syncthreads();
-    if (grp == 0 && c < d.dh)
-        part[((long long)hw * nchunk + chunk) * 64 + c] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
-}
-
-__global__ void __launch_bounds__(256) bwd_bias_final_kernel(BwdDims d, const float *part, int nchunk, float *du,
-                                                             float *dv) {
-    __shared__ float red[4][64];
-    const int hw = blockIdx.x, h = hw >> 1;
-    const int c = threadIdx.x & 63, grp = threadIdx.x >> 6;
-    float s = 0.f;
-    for (int k = grp; k < nchunk; k += 4) s += part[((long long)hw * nchunk + k) * 64 + c];
-    red[grp][c] = s;
-    __syncthreads();
-    if (grp == 0 && c < d.dh) ((hw & 1) ? dv : du)[h * d.dh + c] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+    if (grp == 0 && c < d.dh) (which ? dv : du)[h * d.dh + c] = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
 }
 
 int grid_for(long long n) {
@@ -186,73 +206,55 @@ int grid_for(long long n) {
 }
 
 template <typename T>
-void heads(const BwdDims &d, const void *src, long long src_bs, int nrows, int nrows_p, const void *bias, float scale,
-           void *dst, hipStream_t s) {
-    const long long n = (long long)d.B * d.H * nrows_p * (d.dp / 8);
-    hipLaunchKernelGGL(heads_kernel<T>, dim3(grid_for(n)), dim3(256), 0, s, (const T *)src, src_bs, d.B, nrows,
-                       nrows_p, d.D, d.H, d.dh, d.dp, (const T *)bias, scale, (T *)dst);
+void pack_rows(const BwdDims &d, const void *src, long long src_bs, int nrows, int nrows_p, const void *bias0,
+               const void *bias1, float hm_scale, void *hm0, void *hm1, void *tr0, void *tr1, hipStream_t s) {
+    const dim3 grid(nrows_p / 64, d.B * d.H), block(256);
+    const bool vec = d.dh % 8 == 0 && (d.D * sizeof(T)) % 16 == 0 && (src_bs * sizeof(T)) % 16 == 0 &&
+                     (uintptr_t)src % 16 == 0 && (!bias0 || (uintptr_t)bias0 % 16 == 0) &&
+                     (!bias1 || (uintptr_t)bias1 % 16 == 0);
+    if (vec)
+        hipLaunchKernelGGL((pack_kernel<T, true>), grid, block, 0, s, (const T *)src, src_bs, nrows, nrows_p, d.D, d.H,
+                           d.dh, d.dp, (const T *)bias0, (const T *)bias1, hm_scale, (T *)hm0, (T *)hm1, (T *)tr0,
+                           (T *)tr1);
+    else
+        hipLaunchKernelGGL((pack_kernel<T, false>), grid, block, 0, s, (const T *)src, src_bs, nrows, nrows_p, d.D,
+                           d.H, d.dh, d.dp, (const T *)bias0, (const T *)bias1, hm_scale, (T *)hm0, (T *)hm1,
+                           (T *)tr0, (T *)tr1);
 }
 
 template <typename T>
-void pack(const BwdDims &d, const void *q, const void *k, const void *val, const void *r, const void *u,
-          const void *v, const void *dO, float qscale, void *qu, void *qv, void *dOh, void *ke, void *vk, void *rk,
-          void *rt, hipStream_t s) {
+void pack(const BwdDims &d, const BwdPack &o, const void *q, const void *k, const void *val, const void *r,
+          const void *u, const void *v, const void *dO, float qscale, hipStream_t s) {
     const long long qbs = (long long)d.W * d.D, kbs = (long long)d.K * d.D;
-    heads<T>(d, q, qbs, d.W, d.Wp, u, qscale, qu, s);
-    heads<T>(d, q, qbs, d.W, d.Wp, v, qscale, qv, s);
-    heads<T>(d, dO, qbs, d.W, d.Wp, nullptr, 1.f, dOh, s);
-    heads<T>(d, k, kbs, d.K, d.Kp, nullptr, 1.f, ke, s);
-    heads<T>(d, val, kbs, d.K, d.Kp, nullptr, 1.f, vk, s);
+    pack_rows<T>(d, q, qbs, d.W, d.Wp, u, v, qscale, o.qu, o.qv, o.qut, o.qvt, s);
+    pack_rows<T>(d, dO, qbs, d.W, d.Wp, nullptr, nullptr, 1.f, o.dOh, nullptr, o.dOt, nullptr, s);
+    pack_rows<T>(d, k, kbs, d.K, d.Kp, nullptr, nullptr, 1.f, o.ke, nullptr, o.ket, nullptr, s);
+    pack_rows<T>(d, val, kbs, d.K, d.Kp, nullptr, nullptr, 1.f, o.vk, nullptr, o.vt, nullptr, s);
     const long long nrk = (long long)d.H * rk_table_rows(d.Kp) * d.dp;
     hipLaunchKernelGGL(rk_table_kernel<T>, dim3(grid_for(nrk)), dim3(256), 0, s, (const T *)r, d.K, d.D, d.H, d.dh,
-                       d.dp, d.Kp, rk_frag_off(d.m), (T *)rk);
+                       d.dp, d.Kp, rk_frag_off(d.m), (T *)o.rk);
     const int ld = attn_bwd_rt_ld(d.Kp);
     const long long nrt = (long long)d.H * d.dp * ld;
     hipLaunchKernelGGL(rt_table_kernel<T>, dim3(grid_for(nrt)), dim3(256), 0, s, (const T *)r, d.K, d.D, d.H, d.dh,
-                       d.dp, ld, attn_bwd_rt_off(d.m), (T *)rt);
+                       d.dp, ld, attn_bwd_rt_off(d.m), (T *)o.rt);
 }
 
 }  // namespace
 
-hipError_t launch_bwd_pack(bool is_bf16, const BwdDims &d, const void *q, const void *k, const void *val,
-                           const void *r, const void *u, const void *v, const void *dO, float qscale, void *qu,
-                           void *qv, void *dOh, void *ke, void *vk, void *rk, void *rt, hipStream_t s) {
-    if (is_bf16) pack<bf16>(d, q, k, val, r, u, v, dO, qscale, qu, qv, dOh, ke, vk, rk, rt, s);
-    else pack<float>(d, q, k, val, r, u, v, dO, qscale, qu, qv, dOh, ke, vk, rk, rt, s);
+hipError_t launch_bwd_pack(bool is_bf16, const BwdDims &d, const BwdPack &o, const void *q, const void *k,
+                           const void *val, const void *r, const void *u, const void *v, const void *dO,
+                           float qscale, hipStream_t s) {
+    if (is_bf16) pack<bf16>(d, o, q, k, val, r, u, v, dO, qscale, s);
+    else pack<float>(d, o, q, k, val, r, u, v, dO, qscale, s);
     return hipGetLastError();
 }
 
-hipError_t launch_heads(bool is_bf16, const BwdDims &d, const void *src, long long src_bs, int nrows, int nrows_p,
-                        const void *bias, float scale, void *dst, hipStream_t s) {
-    if (is_bf16) heads<bf16>(d, src, src_bs, nrows, nrows_p, bias, scale, dst, s);
-    else heads<float>(d, src, src_bs, nrows, nrows_p, bias, scale, dst, s);
-    return hipGetLastError();
-}
+int bwd_parts(const BwdDims &d) { return d.B * ((d.W + ATTN_QBLOCK - 1) / ATTN_QBLOCK) * 4; }
 
-hipError_t launch_transpose(bool is_bf16, const void *src, long long src_gs, int G, int H, int nrow, int ncol,
-                            long long src_ld, void *dst, long long dst_hs, long long dst_cs, long long dst_bs,
-                            hipStream_t s) {
-    const dim3 grid((ncol + 63) / 64, (nrow + 63) / 64, G), block(256);
-    if (is_bf16)
-        hipLaunchKernelGGL(transpose_kernel<bf16>, grid, block, 0, s, (const bf16 *)src, src_gs, H, nrow, ncol, src_ld,
-                           (bf16 *)dst, dst_hs, dst_cs, dst_bs);
-    else
-        hipLaunchKernelGGL(transpose_kernel<float>, grid, block, 0, s, (const float *)src, src_gs, H, nrow, ncol, src_ld,
-                           (float *)dst, dst_hs, dst_cs, dst_bs);
-    return hipGetLastError();
-}
-
-int bwd_bias_chunks(const BwdDims &d) { return (d.B * d.W + kBiasChunk - 1) / kBiasChunk; }
-
-hipError_t launch_bwd_unpack(const BwdDims &d, const float *dq1, const float *dq2, const float *dkh,
-                             const float *dvh, const float *drh, float *dq, float *dk, float *dval, float *dr,
-                             float *du, float *dv, float *part, hipStream_t s) {
-    const long long n = (long long)d.B * d.W * d.D + 2LL * d.B * d.K * d.D + (long long)d.K * d.D;
-    hipLaunchKernelGGL(bwd_unpack_kernel, dim3(grid_for(n)), dim3(256), 0, s, d, dq1, dq2, dkh, dvh, drh, dq, dk,
-                       dval, dr);
-    const int nchunk = bwd_bias_chunks(d);
-    hipLaunchKernelGGL(bwd_bias_partial_kernel, dim3(2 * d.H * nchunk), dim3(256), 0, s, d, dq1, dq2, part, nchunk);
-    hipLaunchKernelGGL(bwd_bias_final_kernel, dim3(d.H * 2), dim3(256), 0, s, d, part, nchunk, du, dv);
+hipError_t launch_bwd_finish(const BwdDims &d, const float *drh, const float *part, float *dr, float *du, float *dv,
+                             hipStream_t s) {
+    hipLaunchKernelGGL(bwd_dr_kernel, dim3(grid_for((long long)d.K * d.D)), dim3(256), 0, s, d, drh, dr);
+    hipLaunchKernelGGL(bwd_bias_kernel, dim3(2 * d.H), dim3(256), 0, s, d, part, bwd_parts(d), du, dv);
     return hipGetLastError();
 }
 

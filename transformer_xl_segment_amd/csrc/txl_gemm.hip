@@ -253,6 +253,19 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
                         ((T *)P.c1)[(bh * P.dhp + c + i) * P.kv_slots + slot] = from_f32<T>(x[i]);
                 } else if (P.epi == EPI_KV) {
                     store8<T, true>((T *)P.c0 + (bh * P.kv_slots + kv_slot(P, t)) * P.dhp + c, x);
+                } else if (P.epi == EPI_GROWS) {
+                    if (t < P.c_rows) {
+                        const int bb = b / P.heads, gh = b - bb * P.heads;
+                        float *dst = (float *)P.c0 + (long long)bb * P.c_bstride + (long long)t * P.c_ld + gh * P.dh + c;
+                        if (c + 8 <= P.dh && ((uintptr_t)dst & 15) == 0) {
+                            *reinterpret_cast<f32x4 *>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+                            *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i)
+                                if (c + i < P.dh) dst[i] = x[i];
+                        }
+                    }
                 } else if (P.epi == EPI_RFRAG) {
                     // eight consecutive columns of a row stay contiguous (c % 8 == 0)
                     store8<T, true>((T *)P.c0 + hh * P.frag_hstride + rk_elem(t, c, P.frag_off, P.dhp), x);

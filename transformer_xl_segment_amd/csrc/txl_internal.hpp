@@ -33,6 +33,8 @@ enum EpiMode {
     EPI_HEADS = 3,   // c0 head-major [b][hh][t][c]
     EPI_RFRAG = 4,   // c0 distance-key table of head hh (hh * frag_hstride), row t, column c in the
                      // fragment-major order of rk_elem (rows offset by frag_off)
+    EPI_GROWS = 5,   // batch entry b = (bb, hh) = (b / heads, b % heads): fp32 c0 + bb*c_bstride + t*c_ld +
+                     // hh*dh + c for t < c_rows and c < dh (column c of dhp = the entry's only head)
 };
 
 struct GemmProblem {
@@ -69,6 +71,7 @@ struct GemmProblem {
     long long frag_hstride;      // EPI_RFRAG: elements per head
     long long b_bstride;         // B_ROWS: elements between the B operands of batch entries (0: one B;
                                  // nonzero requires seg_rows % 128 == 0 so no tile straddles entries)
+    int c_rows;                  // EPI_GROWS: rows of each entry that are written
 };
 
 struct GemmLaunch {
@@ -163,14 +166,14 @@ hipError_t launch_add_positions(bool is_bf16, const void *x, long long x_bstride
 //   rt         [H][dp][rt_ld]  distance keys transposed: distance d at column d + rt_off
 //              (attn_bwd_rt_off(m), attn_bwd_rt_ld(Kp)), zero outside 0 <= d < K
 //   o          [B][W][D]  forward output;  lse [B][H][Wp]  its log-sum-exp (log2 units)
-// Writes dq1, dq2 [B][H][Wp][dp] fp32 (the content and distance parts of dq, rows < W),
-// pt, dst [B][H][Kp][Wp] (p and c p (dP - D), key-major) and dsd [B][H][Kp][Wp] (the
+// Writes dq [B][W][D] fp32; part [2][H][B * ceil(W / ATTN_QBLOCK) * 4][64] fp32, per wave
+// of 32 queries the column sums of dq's content (du) and distance (dv) parts; pt, dst [B][H][Kp][Wp] (p and c p (dP - D), key-major) and dsd [B][H][Kp][Wp] (the
 // latter re-indexed by distance d = m + i - j); columns < W8 (W rounded up to 8) hold
 // data, zero where no key is visible (in particular past W); c = 1/sqrt(dh).
 struct AttnBwdArgs {
     const void *qu, *qv, *dO, *ke, *vk, *kt, *rk, *rt, *o;
     const float *lse;
-    float *dq1, *dq2;
+    float *dq, *part;
     void *pt, *dst, *dsd;
     int B, H, W, Wp, m, K, Kp, dh, dp, D;
     long long rk_hstride;
@@ -185,30 +188,24 @@ int attn_bwd_rt_ld(int Kp);
 struct BwdDims {
     int B, H, W, Wp, W8, m, K, Kp, dh, dp, D;
 };
-// q, dO [B][W][D] -> qu = (q + u) * qscale, qv = (q + v) * qscale, dOh  [G][Wp][dp]   (G = B*H, zero
-// padding); k, val [B][K][D] -> ke, vk [G][Kp][dp]; r [K][D] -> rk (the attention kernels' distance-key
-// table, rk_elem layout with row offset rk_frag_off(m), rk_table_rows(Kp)*dp per head) and rt
-// ([H][dp][attn_bwd_rt_ld(Kp)], distance d at column d + attn_bwd_rt_off(m))
-hipError_t launch_bwd_pack(bool is_bf16, const BwdDims &d, const void *q, const void *k, const void *val,
-                           const void *r, const void *u, const void *v, const void *dO, float qscale, void *qu,
-                           void *qv, void *dOh, void *ke, void *vk, void *rk, void *rt, hipStream_t s);
-// dst[(b*H + h)][t][c] = (src[b][t][h*dh + c] + bias[h*dh + c]) * scale, t < nrows, c < dh (bias may be
-// null); zero up to nrows_p rows and dp columns
-hipError_t launch_heads(bool is_bf16, const BwdDims &d, const void *src, long long src_bs, int nrows, int nrows_p,
-                        const void *bias, float scale, void *dst, hipStream_t s);
-// dst[...] = src[g][row][col] transposed per batch entry g = b*H + h: element (g, row, col) at
-// src + g*src_gs + row*src_ld + col goes to dst + h*dst_hs + col*dst_cs + b*dst_bs + row
-// (rows < nrow, cols < ncol)
-hipError_t launch_transpose(bool is_bf16, const void *src, long long src_gs, int G, int H, int nrow, int ncol,
-                            long long src_ld, void *dst, long long dst_hs, long long dst_cs, long long dst_bs,
-                            hipStream_t s);
-// dq = dq1 + dq2 (head-major fp32) -> [B][W][D]; du, dv = column sums of dq1, dq2;
-// dk, dval [G][Kp][dp] -> [B][K][D]; dr [G][Kp][dp] summed over the batch -> [K][D]
-// (part: scratch of 2 * H * bwd_bias_chunks(d) * 64 floats)
-int bwd_bias_chunks(const BwdDims &d);
-hipError_t launch_bwd_unpack(const BwdDims &d, const float *dq1, const float *dq2, const float *dkh,
-                             const float *dvh, const float *drh, float *dq, float *dk, float *dval, float *dr,
-                             float *du, float *dv, float *part, hipStream_t s);
+// Packed operands of the backward (G = B*H entries, zero padding past the data):
+//   qu, qv = (q + u) * qscale, (q + v) * qscale and dOh  [G][Wp][dp];  qut, qvt = (q + u), (q + v)
+//   and dOt transposed [G][dp][Wp];  ke, vk [G][Kp][dp] and ket, vt [G][dp][Kp] (keys, values);
+//   rk: the attention kernels' distance-key table (rk_elem layout, row offset rk_frag_off(m),
+//   rk_table_rows(Kp)*dp per head); rt [H][dp][attn_bwd_rt_ld(Kp)], distance d at column
+//   d + attn_bwd_rt_off(m)
+struct BwdPack {
+    void *qu, *qv, *dOh, *qut, *qvt, *dOt, *ke, *vk, *ket, *vt, *rk, *rt;
+};
+hipError_t launch_bwd_pack(bool is_bf16, const BwdDims &d, const BwdPack &o, const void *q, const void *k,
+                           const void *val, const void *r, const void *u, const void *v, const void *dO,
+                           float qscale, hipStream_t s);
+// per-wave partial sums of du, dv written by the attention backward
+int bwd_parts(const BwdDims &d);
+// dr [K][D] = drh [G][Kp][dp] summed over the batch; du, dv [D] from part
+// ([2][H][bwd_parts(d)][64] fp32, fixed summation order)
+hipError_t launch_bwd_finish(const BwdDims &d, const float *drh, const float *part, float *dr, float *du, float *dv,
+                             hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Small kernels.
