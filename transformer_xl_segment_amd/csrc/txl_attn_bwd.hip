@@ -62,6 +62,8 @@ struct BwdSmem {
 };
 
 __device__ __forceinline__ float frag_at(const Frag<bf16> &f, int t) { return (float)f.v[t]; }
+__device__ __forceinline__ bf16 frag_elem(const Frag<bf16> &f, int t) { return f.v[t]; }
+__device__ __forceinline__ float frag_elem(const Frag<float> &f, int t) { return t < 4 ? f.lo[t] : f.hi[t - 4]; }
 __device__ __forceinline__ float frag_at(const Frag<float> &f, int t) { return t < 4 ? f.lo[t] : f.hi[t - 4]; }
 __device__ __forceinline__ void frag_set(Frag<bf16> &f, int t, float x) { f.v[t] = (bf16)x; }
 __device__ __forceinline__ void frag_set(Frag<float> &f, int t, float x) {
@@ -212,6 +214,12 @@ __global__ void __launch_bounds__(256, 1) rel_attn_bwd_kernel(const AttnBwdArgs 
     if (nkb > 0) gload(0);
 
     float *grow = sm.g[w] + fr * kGPitch;
+    // byte offsets of this lane's stores, fixed for the kernel: rows 4*hf + r of a group
+    // of four keys (p, dS) and row 8*hf of a group of eight distances, column qi
+    uint32_t poff[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) poff[r] = (uint32_t)(((4 * hf + r) * A.Wp + qi) * (int)sizeof(T));
+    const uint32_t doff = (uint32_t)((8 * hf * A.Wp + qi) * (int)sizeof(T));
     T *ring = sm.ring[w] + fr * RP;
     f32x16 dqu[NO], dqv[NO];
 #pragma unroll
@@ -244,22 +252,36 @@ __global__ void __launch_bounds__(256, 1) rel_attn_bwd_kernel(const AttnBwdArgs 
     // Distances [base, base + 64) of the ring, which start at slot p0: masked to
     // the keys seen so far (0 <= j <= jmax, d >= 0), written out for dr and
     // multiplied into dq's distance part.
-    auto flush = [&](int base, int p0, int jmax) __attribute__((always_inline)) {
+    // Only the first block's window (keys below 0, never written) and the last one (keys past
+    // the wave's last block, stale) need the mask; every other entry was written by this
+    // block or the one before it, zero where the key is not visible.
+    auto flush = [&](int base, int p0, int jmax, bool masked) __attribute__((always_inline)) {
         wave_lds_sync();
+        const bool rows_in = base >= 0 && base + 63 < A.Kp;     // every row of the window exists
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
             const int d0 = base + 16 * s4 + 8 * hf;
             Frag<T> fb;
             load8(fb, ring + p0 + 16 * s4 + 8 * hf);
+            if (masked) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int d = d0 + t, j = m + qi - d;
-                if (d < 0 || j < 0 || j > jmax) frag_set(fb, t, 0.f);
+                for (int t = 0; t < 8; ++t) {
+                    const int d = d0 + t, j = m + qi - d;
+                    if (d < 0 || j < 0 || j > jmax) frag_set(fb, t, 0.f);
+                }
             }
+            if (rows_in) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int d = d0 + t;
-                if (d >= 0 && d < A.Kp) dsd[(long long)d * A.Wp + qi] = from_f32<T>(frag_at(fb, t));
+                for (int t = 0; t < 8; ++t) {
+                    char *rowp = (char *)dsd + (long long)(base + 16 * s4 + t) * A.Wp * (long long)sizeof(T);
+                    *reinterpret_cast<T *>(rowp + doff) = frag_elem(fb, t);
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int d = d0 + t;
+                    if (d >= 0 && d < A.Kp) dsd[(long long)d * A.Wp + qi] = frag_elem(fb, t);
+                }
             }
 #pragma unroll
             for (int o = 0; o < NO; ++o) {
@@ -330,14 +352,20 @@ __global__ void __launch_bounds__(256, 1) rel_attn_bwd_kernel(const AttnBwdArgs 
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) dpa[sb][i] = A.c * sacc[sb][i] * (dpa[sb][i] - Dq);
-        // ---- p and dS, key-major (row j0 + b, column qi)
+        // ---- p and dS, key-major (row j0 + b, column qi): a uniform row base per group of
+        // four keys plus the lane's fixed offset
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const long long off = (long long)(j0 + 32 * sb + crow(i, lane)) * A.Wp + qi;
-                pt[off] = from_f32<T>(sacc[sb][i]);
-                dst[off] = from_f32<T>(dpa[sb][i]);
+            for (int q = 0; q < 4; ++q) {
+                const long long ro = (long long)(j0 + 32 * sb + 8 * q) * A.Wp * (long long)sizeof(T);
+                char *pb = (char *)pt + ro;
+                char *db = (char *)dst + ro;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    *reinterpret_cast<T *>(pb + poff[r]) = from_f32<T>(sacc[sb][4 * q + r]);
+                    *reinterpret_cast<T *>(db + poff[r]) = from_f32<T>(dpa[sb][4 * q + r]);
+                }
             }
         // ---- dq^T (content) += K^T dS^T, 16 keys per MFMA
 #pragma unroll
@@ -353,13 +381,16 @@ __global__ void __launch_bounds__(256, 1) rel_attn_bwd_kernel(const AttnBwdArgs 
         }
         // ---- dS into the ring: key b of query a at distance cw + a - b, slot
         // (d - (m + iw) + 160) mod 128
+        {
+            const int L = fr - 4 * hf + 160 - kKB * kb;
 #pragma unroll
-        for (int sb = 0; sb < 2; ++sb)
+            for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                ring[(fr - (32 * sb + crow(i, lane)) - kKB * kb + 160) & (kRing - 1)] = from_f32<T>(dpa[sb][i]);
+                for (int i = 0; i < 16; ++i)
+                    ring[(L - (32 * sb + 8 * (i >> 2) + (i & 3))) & (kRing - 1)] = from_f32<T>(dpa[sb][i]);
+        }
         // distances [cw - 32, cw + 31] are complete
-        flush(m + iw - j0 - 32, (kRing - kKB * kb) & (kRing - 1), j0 + kKB - 1);
+        flush(m + iw - j0 - 32, (kRing - kKB * kb) & (kRing - 1), j0 + kKB - 1, kb == 0);
     };
 
     for (int kb = 0; kb < nkb; kb += 2) {
@@ -378,7 +409,7 @@ __global__ void __launch_bounds__(256, 1) rel_attn_bwd_kernel(const AttnBwdArgs 
         return;
     }
     // the distances the last block left open
-    flush(m + iw - kb_last * kKB - 96, (kKB - kKB * kb_last) & (kRing - 1), kb_last * kKB + kKB - 1);
+    flush(m + iw - kb_last * kKB - 96, (kKB - kKB * kb_last) & (kRing - 1), kb_last * kKB + kKB - 1, true);
     // zeros where no key of the wave is visible: key rows past its last block,
     // distances past its last query's
     for (int j = (kb_last + 1) * kKB + hf; j < A.Kp; j += 2) {
