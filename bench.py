@@ -440,6 +440,8 @@ def main():
                     help="skip the comparison with vanilla sliding-window evaluation")
     ap.add_argument("--stack16-only", action="store_true",
                     help="time only the 16-layer bf16 stack's schedule (for counter runs of its kernels)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the attention backward at the headline shape (for kernel traces)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline step (for counter runs); implies the two --no-* flags")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -473,6 +475,9 @@ def main():
     wl = syn.WORKLOADS[WORKLOAD]
     B, D, H, W, M = wl.B, wl.D, wl.H, wl.W, wl.M
     dh = D // H
+    if args.backward_only:
+        print(json.dumps({"backward": time_backward(tb, torch, B, W, M, D, H, dev, 10)}), flush=True)
+        return
     prob = syn.draw_problem(wl)
     bf = torch.bfloat16
     x = torch.from_numpy(prob.x).to(dev).to(bf)                 # [B, S*W, D]

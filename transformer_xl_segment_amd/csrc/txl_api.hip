@@ -729,6 +729,8 @@ txl_status txl_rel_attn_bwd(txl_dtype dtype, int B, int W, int D, int H, int m, 
         p->c_ld = D; p->c_bstride = (long long)d.K * D; p->c_rows = d.K;
     }
     GemmProblem gr = batched_problem(G, Kp, dp, W8, w + L.dsd, Wp, w + L.qvt, Wp, w + L.drh);
+    // key j (distance d) sees no query i < j - m (d - m): each A row is zero before that query
+    for (GemmProblem *p : {&gv, &gk, &gr}) { p->kz_on = 1; p->kz_lag = m; }
     TXL_TRY(hip_check(launch_gemm(bf, grouped({gv, gk, gr}), s), "gradient GEMM launch"));
     return hip_check(launch_bwd_finish(d, (const float *)(w + L.drh), (const float *)(w + L.part), dr, du, dv, s),
                      "backward reduction launch");

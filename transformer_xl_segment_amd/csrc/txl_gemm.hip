@@ -553,10 +553,13 @@ __global__ void __launch_bounds__(kThreads, 3) gemm_lds_kernel(const GemmLaunch 
     // for them before the fragment reads anyway): k-tile kt+2 is requested
     // right after the barrier of k-tile kt and complete at the barrier of
     // k-tile kt+1, one k-tile of products later.
-    issue(0, 0);
-    if (nk > 1) issue(1, 1);
+    // a causal band of zeros in A: this tile's rows are zero before k-tile kt0
+    int kt0 = 0;
+    if (P.kz_on) kt0 = min(max(0, m0 - bidx * P.seg_rows - P.kz_lag) / BK, nk - 1);   // >= 1 k-tile runs
+    issue(kt0, 0);
+    if (kt0 + 1 < nk) issue(kt0 + 1, 1);
     int b = 0;                                           // buffer of k-tile kt
-    for (int kt = 0; kt < nk; ++kt) {
+    for (int kt = kt0; kt < nk; ++kt) {
         // every wave's chunks of k-tile kt are in LDS, and every wave is done
         // reading the buffer of k-tile kt-1, which k-tile kt+2 now fills
         wait_loads();

@@ -72,6 +72,8 @@ struct GemmProblem {
     long long b_bstride;         // B_ROWS: elements between the B operands of batch entries (0: one B;
                                  // nonzero requires seg_rows % 128 == 0 so no tile straddles entries)
     int c_rows;                  // EPI_GROWS: rows of each entry that are written
+    int kz_on, kz_lag;           // kz_on: row t of every entry of A is zero for k < t - kz_lag (a causal
+                                 // band), so a tile may start its reduction there
 };
 
 struct GemmLaunch {
