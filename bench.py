@@ -59,16 +59,28 @@ def attn_bytes(B, W, m, D, es):
     return es * (2 * B * W * D + 2 * B * K * D + K * D + B * W * D)
 
 
-def traffic_for(kernel_src: str, path: str):
+def kernel_digest(sources) -> str:
+    """sha256 over the kernel's source files, concatenated in the given order."""
+    h = hashlib.sha256()
+    for src in sources:
+        with open(src, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+# the attention kernel's translation unit: its file and the headers it includes
+ATTN_SOURCES = [os.path.join(ROOT, "transformer_xl_segment_amd", "csrc", n)
+                for n in ("txl_attn.hip", "txl_attn_tile.hpp", "txl_device.hpp", "txl_internal.hpp")]
+
+
+def traffic_for(sources, path: str):
     """Measured HBM bytes per launch from a committed counter summary, or None
-    if the kernel source has changed since the counters were taken."""
+    if the kernel's sources have changed since the counters were taken."""
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(kernel_src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("kernel_sha256") != digest:
+    if rec.get("kernel_sha256") != kernel_digest(sources):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -517,7 +529,7 @@ def main():
     a_flops = attn_flops(B, H, dh, W, m)
     a_avg_s = attn_ms * 1e-3 / launches
     a_tflops = a_flops / a_avg_s / 1e12
-    traffic = traffic_for(os.path.join(ROOT, "transformer_xl_segment_amd", "csrc", "txl_attn.hip"),
+    traffic = traffic_for(ATTN_SOURCES,
                           os.path.join(ROOT, "profiles", "traffic_rel_attn_kernel_attn_w512_bf16.json"))
     rec = {
         "metric": "rel-attn tokens/s and TFLOP/s (% bf16 MFMA peak) at W=M=512, d_head=64, 1 GPU",
