@@ -42,6 +42,14 @@ CASES = [
     ("dh64_two_qblocks", 2, 128, 2, 130, 70),
     ("dh41_odd", 2, 82, 2, 29, 45),
     ("dh64_long_memory", 1, 64, 1, 20, 200),
+    # one query (W = 1: a single lane of one wave carries data)
+    ("dh16_one_query", 1, 32, 2, 1, 3),
+    # three query blocks, the last wave partly filled
+    ("dh48_three_qblocks", 1, 96, 2, 300, 20),
+    # K = m + W = 128 exactly: the last distance window reaches past the padded rows
+    ("dh64_k_equals_padding", 2, 64, 1, 100, 28),
+    # a long memory behind a five-row segment
+    ("dh32_short_segment", 1, 64, 2, 5, 300),
 ]
 
 
