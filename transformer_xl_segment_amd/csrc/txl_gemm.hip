@@ -166,14 +166,14 @@ __device__ __forceinline__ int kv_slot(const GemmProblem &P, int t) {
     return s >= P.kv_slots ? s - P.kv_slots : s;
 }
 
-template <typename T, bool VEC, int BM>
+template <typename T, bool VEC, int BM, int BN = 128>
 __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, int m0, int n0, int tid,
                                          float inv_seg) {
     const bool trans = P.epi == EPI_KV && n0 >= P.b_split;
     if (!trans) {
         const int cg = tid & 15;                       // column group: columns n0 + 8*cg .. +7
         const int n = n0 + 8 * cg;
-        if (n >= P.cols) return;
+        if (8 * cg >= BN || n >= P.cols) return;
         const bool full = n + 8 <= P.cols;
         float bias[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         float uu[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -282,6 +282,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem &P, const float *cs, 
         const int lane = tid & 63, wv = tid >> 6;
         for (int task = wv; task < BM / 4; task += 4) {  // task = (row group rg, column half ch)
             const int rg = task >> 1, ch = task & 1;
+            if (64 * ch >= BN) continue;
             const int nl = 64 * ch + lane;
             const int n = n0 + nl;
             const int row = m0 + 8 * rg;
@@ -442,11 +443,12 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
 // ---------------------------------------------------------------------------
 constexpr int kLRow = 64;                                 // bytes per row of one k-tile
 
-template <int BM>
+template <int BM, int BN>
 struct GemmLdsSmem {
-    char buf[3][(BM + kBN) * kLRow];
+    char buf[3][(BM + BN) * kLRow];
 };
-static_assert(sizeof(GemmLdsSmem<64>) >= 64 * 132 * 4, "C staging must fit in the operand buffers");
+static_assert(sizeof(GemmLdsSmem<64, 128>) >= 64 * 132 * 4, "C staging must fit in the operand buffers");
+static_assert(sizeof(GemmLdsSmem<128, 64>) >= 64 * 132 * 4, "C staging must fit in the operand buffers");
 
 // Source of lanes whose chunk lies past kdim or in a row without data.
 __device__ __align__(16) unsigned int g_zero_chunk[4];
@@ -458,15 +460,17 @@ typedef __attribute__((address_space(3))) void *lds_ptr;
 // written LDS.
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
 
-template <typename T, int BM>
-__global__ void __launch_bounds__(kThreads, 3) gemm_lds_kernel(const GemmLaunch g) {
+// BN = 64 (problems of at most 64 columns): 36 KB of LDS, four workgroups per CU.
+template <typename T, int BM, int BN>
+__global__ void __launch_bounds__(kThreads, BN == 64 ? 4 : 3) gemm_lds_kernel(const GemmLaunch g) {
     constexpr int MI = BM / 64;                          // 32-row blocks per wave
-    constexpr int ROWS = BM + kBN;                       // rows per k-tile (A, then B)
+    constexpr int NJ = BN / 64;                          // 32-column blocks per wave
+    constexpr int ROWS = BM + BN;                        // rows per k-tile (A, then B)
     constexpr int NI = ROWS / 16 / 4;                    // load instructions per wave per k-tile
     constexpr int BK = kLRow / (int)sizeof(T);           // elements per row of a k-tile
     constexpr int EPC = 16 / (int)sizeof(T);             // elements per chunk
     static_assert(ROWS % 64 == 0, "whole load instructions per wave");
-    __shared__ GemmLdsSmem<BM> sm;
+    __shared__ GemmLdsSmem<BM, BN> sm;
 
     const int total = g.total_tiles;
     const int gid = blockIdx.x;
@@ -478,7 +482,7 @@ __global__ void __launch_bounds__(kThreads, 3) gemm_lds_kernel(const GemmLaunch 
     else P = g.p[0];
     const int lt = tile - P.tile_begin;
     const int tm = lt / P.tiles_n, tn = lt - tm * P.tiles_n;
-    const int m0 = tm * BM, n0 = tn * kBN;
+    const int m0 = tm * BM, n0 = tn * BN;
     const float inv_seg = 1.0f / (float)P.seg_rows;
 
     const int tid = threadIdx.x;
@@ -514,11 +518,11 @@ __global__ void __launch_bounds__(kThreads, 3) gemm_lds_kernel(const GemmLaunch 
         }
     };
 
-    f32x16 acc[MI][2];
+    f32x16 acc[MI][NJ];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = zero16();
+        for (int j = 0; j < NJ; ++j) acc[i][j] = zero16();
 
     const int fr = lane & 31, fh = lane >> 5;
     const int sw = (fr >> 2) & 3;                        // this lane's row swizzle
@@ -535,16 +539,16 @@ __global__ void __launch_bounds__(kThreads, 3) gemm_lds_kernel(const GemmLaunch 
     auto mma_tile = [&](const char *bufp) {
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            Frag<T> fa[MI], fb[2];
+            Frag<T> fa[MI], fb[NJ];
             const int e0 = ks * 16 + fh * 8;
 #pragma unroll
             for (int i = 0; i < MI; ++i) frag(fa[i], bufp, wm * (BM / 2) + i * 32 + fr, e0);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) frag(fb[j], bufp, BM + wn * 64 + j * 32 + fr, e0);
+            for (int j = 0; j < NJ; ++j) frag(fb[j], bufp, BM + wn * (BN / 2) + j * 32 + fr, e0);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) mma16(acc[i][j], fb[j], fa[i]);   // C^T block: lane = row of C
+                for (int j = 0; j < NJ; ++j) mma16(acc[i][j], fb[j], fa[i]);   // C^T block: lane = row of C
         }
     };
 
@@ -578,15 +582,15 @@ __global__ void __launch_bounds__(kThreads, 3) gemm_lds_kernel(const GemmLaunch 
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NJ; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<f32x4 *>(&cs[(wm * (BM / 2) + i * 32 + fr - 64 * half) * kCPitch + wn * 64 +
+                        *reinterpret_cast<f32x4 *>(&cs[(wm * (BM / 2) + i * 32 + fr - 64 * half) * kCPitch + wn * (BN / 2) +
                                                        j * 32 + crow(4 * q, lane)]) =
                             f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
         }
         __syncthreads();
-        epilogue<T, true, 64>(P, cs, m0 + 64 * half, n0, tid, inv_seg);
+        epilogue<T, true, 64, BN>(P, cs, m0 + 64 * half, n0, tid, inv_seg);
         if (half + 1 < BM / 64) __syncthreads();
     }
 }
@@ -615,10 +619,10 @@ template <int BM>
 void launch_bm(bool is_bf16, bool vec, const GemmLaunch &g, hipStream_t s) {
     dim3 grid(g.total_tiles), block(kThreads);
     if (is_bf16) {
-        if (vec) hipLaunchKernelGGL((gemm_lds_kernel<bf16, BM>), grid, block, 0, s, g);
+        if (vec) hipLaunchKernelGGL((gemm_lds_kernel<bf16, BM, kBN>), grid, block, 0, s, g);
         else hipLaunchKernelGGL((gemm_kernel<bf16, false, BM>), grid, block, 0, s, g);
     } else {
-        if (vec) hipLaunchKernelGGL((gemm_lds_kernel<float, BM>), grid, block, 0, s, g);
+        if (vec) hipLaunchKernelGGL((gemm_lds_kernel<float, BM, kBN>), grid, block, 0, s, g);
         else hipLaunchKernelGGL((gemm_kernel<float, false, BM>), grid, block, 0, s, g);
     }
 }
@@ -629,8 +633,29 @@ constexpr int kSmallGrid = 512;
 
 hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s) {
     if (g.total_tiles <= 0) return hipSuccess;
-    bool vec = true;
-    for (int i = 0; i < g.count; ++i) vec = vec && gemm_vec_ok(is_bf16, g.p[i]);
+    bool vec = true, narrow = true;
+    for (int i = 0; i < g.count; ++i) {
+        vec = vec && gemm_vec_ok(is_bf16, g.p[i]);
+        narrow = narrow && g.p[i].cols <= 64 && g.p[i].epi != EPI_KV;
+    }
+    if (vec && narrow && g.total_tiles >= kSmallGrid) {
+        // every problem fits one 64-column tile: 128 x 64 tiles, none of the MFMA
+        // work and LDS rows spent on columns past the problem
+        GemmLaunch gn = g;
+        int t = 0;
+        for (int i = 0; i < gn.count; ++i) {
+            GemmProblem &P = gn.p[i];
+            P.tiles_n = 1;
+            P.tile_begin = t;
+            P.tile_count = (P.rows + 127) / 128;
+            t += P.tile_count;
+        }
+        gn.total_tiles = t;
+        dim3 grid(gn.total_tiles), block(kThreads);
+        if (is_bf16) hipLaunchKernelGGL((gemm_lds_kernel<bf16, 128, 64>), grid, block, 0, s, gn);
+        else hipLaunchKernelGGL((gemm_lds_kernel<float, 128, 64>), grid, block, 0, s, gn);
+        return hipGetLastError();
+    }
     if (g.total_tiles >= kSmallGrid) {
         launch_bm<128>(is_bf16, vec, g, s);
     } else {
