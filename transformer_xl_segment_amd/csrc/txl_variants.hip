@@ -12,6 +12,7 @@
 // term after the fact, and add absolute positions to rows.
 #include <math.h>
 
+#include "txl_attn_tile.hpp"
 #include "txl_device.hpp"
 #include "txl_internal.hpp"
 
@@ -39,121 +40,146 @@ __global__ void shaw_rows_kernel(T *rk, const T *aK, int clip, int K, int rows, 
 // Shaw's value term, added to the attention output o [B][W][D] (head slices of
 // width dh). Because aV is constant for distances >= clip and the weights of a
 // query sum to one,
-//   sum_j p_ij aV[min(delta, clip)] = aV[clip] + sum_{delta < min(clip, m+i+1)} p_i(delta) (aV[delta] - aV[clip]).
-// A workgroup takes 16 consecutive queries of one (b, h). It stages in LDS,
-// once, the key rows the 16 bands touch, the distance rows aK[d] for d < clip
-// and the differences aV[d] - aV[clip] (global reads coalesced, rows padded to
-// an odd number of dwords so lanes reading different rows hit distinct banks).
-// Each wave then takes four queries in turn: lanes score the band's keys (the
-// same pre-scaled operands as the attention kernel, fp32 sums), p = exp2(s -
-// lse) with the kernel's log-sum-exp, and lanes own output columns to sum over
-// the band.
+//   sum_j p_ij aV[min(delta, clip)] = aV[clip] + sum_{delta < min(clip, m+i+1)} p_i(delta) (aV[delta] - aV[clip]),
+// a product over at most 128 distances per query, which runs on the matrix
+// cores. A workgroup takes 128 queries of one (b, h), 32 per wave, as the
+// attention kernel does, and stages once aK (rows d < clip, zero-padded to dp
+// columns) and (aV[d] - aV[clip])^T. Per wave:
+//   - content scores of the band's keys m + i_wave - clip + 1 .. m + i_wave + 31
+//     (at most 159), K (q+u)^T, stored to LDS per query in key order;
+//   - the distance scores G = aK (q+v)^T, directly in distance order;
+//   - each lane reads its content scores back skewed into distance order
+//     (key m + i - d of query i), p = exp2(s - lse) with the attention
+//     kernel's log-sum-exp, masked to d < min(clip, m + i + 1);
+//   - O^T += (aV - aV[clip])^T P^T, then o += O + aV[clip].
 constexpr int kShawMaxClip = 128;
-constexpr int kShawQueries = 16;
+constexpr int kShawBand = kShawMaxClip + 32;        // keys of one wave's band (at most 159)
+constexpr int kShawPitch = kShawBand + 4;           // floats per query row: 16-byte writes, skewed reads on distinct banks
 
 template <typename T, int DP>
 struct ShawSmem {
-    static constexpr int kRowDw = DP * (int)sizeof(T) / 4;        // dwords of one operand row
-    static constexpr int kPitchDw = kRowDw + 1;                     // odd: conflict-free row-wise reads
-    uint32_t k[(kShawMaxClip + kShawQueries) * kPitchDw];
-    uint32_t ak[kShawMaxClip * kPitchDw];
-    float dv[kShawMaxClip * DP];
-    float p[4][kShawMaxClip];
-    float q[4][2][DP];
+    static constexpr int NO = (DP + 31) / 32;
+    static constexpr int kPitchAK = DP * (int)sizeof(T) + 16;                          // aK row, bytes
+    static constexpr int kPitchDV = kShawMaxClip * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);   // dV^T row, bytes
+    float cs[4][32 * kShawPitch];
+    char ak[kShawMaxClip * kPitchAK];
+    char dvt[NO * 32 * kPitchDV];
 };
 
-// Adds the products of one operand dword (one fp32 or two bf16 columns) with
-// the query columns it belongs to.
-template <typename T> __device__ __forceinline__ float dot_dw(uint32_t x, const float *q, float s);
-template <> __device__ __forceinline__ float dot_dw<float>(uint32_t x, const float *q, float s) {
-    return fmaf(q[0], __uint_as_float(x), s);
-}
-template <> __device__ __forceinline__ float dot_dw<bf16>(uint32_t x, const float *q, float s) {
-    s = fmaf(q[0], __uint_as_float(x << 16), s);
-    return fmaf(q[1], __uint_as_float(x & 0xffff0000u), s);
-}
-
 template <typename T, int DP>
-__global__ void __launch_bounds__(256) shaw_values_kernel(const T *qu, const T *qv, const T *ke, const T *aK,
-                                                          const float *lse, const T *aV, T *o, int H, int W,
-                                                          int Wp, int m, int Kp, int dh, int D, int clip) {
+__global__ void __launch_bounds__(256, 1) shaw_values_kernel(const AttnArgs A, const T *aK, const T *aV, int clip) {
     typedef ShawSmem<T, DP> SM;
-    constexpr int RD = SM::kRowDw, PD = SM::kPitchDw, EPD = 4 / (int)sizeof(T);   // columns per dword
+    constexpr int NS = DP / 16, NO = SM::NO;
     __shared__ SM sm;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int nqb = (W + kShawQueries - 1) / kShawQueries;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int fr = lane & 31, hf = lane >> 5;
+    const int nqb = (A.W + 127) / 128;
     const int bh = blockIdx.x / nqb;
-    const int i0 = (blockIdx.x - bh * nqb) * kShawQueries;
-    const int iend = min(i0 + kShawQueries, W);
-    const int b = bh / H, h = bh - b * H;
-    // keys of the 16 bands: jlo .. m + iend - 1
-    const int jlo = max(0, m + i0 - clip + 1);
-    const int nk = m + iend - jlo;
-    // (independent loads, unrolled so that several are in flight at once)
-    const uint32_t *kg = reinterpret_cast<const uint32_t *>(ke + ((long long)bh * Kp + jlo) * DP);
-#pragma unroll 8
-    for (int idx = threadIdx.x; idx < nk * RD; idx += 256) {
-        const int r = idx / RD, u = idx - r * RD;
-        sm.k[r * PD + u] = kg[idx];
+    const int i0 = (blockIdx.x - bh * nqb) * 128;
+    const int b = bh / A.H, h = bh - b * A.H;
+    const int m = A.m, dh = A.dh;
+    const int ndb = (clip + 31) / 32;                    // 32-distance blocks of the band
+
+    // staging: aK rows d < clip (zero past dh), and dV^T[c][d] = aV[d][c] - aV[clip][c]
+    // (zero for d >= clip or c >= dh)
+    for (int idx = tid; idx < kShawMaxClip * DP; idx += 256) {
+        const int d = idx / DP, c = idx - d * DP;
+        const float x = (d < clip && c < dh) ? to_f32(aK[(long long)d * dh + c]) : 0.f;
+        reinterpret_cast<T *>(sm.ak + d * SM::kPitchAK)[c] = from_f32<T>(x);
     }
-    // aK rows 0 .. clip-1, zero past column dh
-    T *akl = reinterpret_cast<T *>(sm.ak);
-#pragma unroll 8
-    for (int idx = threadIdx.x; idx < clip * DP; idx += 256) {
-        const int r = idx / DP, c = idx - r * DP;
-        akl[r * PD * EPD + c] = c < dh ? aK[(long long)r * dh + c] : from_f32<T>(0.f);
-    }
-    // rows d = w, w + 4, ... of the value differences (columns >= dh are never read)
-    const float tail = lane < dh ? to_f32(aV[(long long)clip * dh + lane]) : 0.f;
-    if (lane < dh) {
-#pragma unroll 8
-        for (int d = w; d < clip; d += 4) sm.dv[d * DP + lane] = to_f32(aV[(long long)d * dh + lane]) - tail;
+    for (int idx = tid; idx < NO * 32 * kShawMaxClip; idx += 256) {
+        const int c = idx / kShawMaxClip, d = idx - c * kShawMaxClip;
+        const float x = (d < clip && c < dh) ? to_f32(aV[(long long)d * dh + c]) - to_f32(aV[(long long)clip * dh + c])
+                                             : 0.f;
+        reinterpret_cast<T *>(sm.dvt + c * SM::kPitchDV)[d] = from_f32<T>(x);
     }
     __syncthreads();
-    for (int qq = 0; qq < kShawQueries / 4; ++qq) {
-        const int i = i0 + 4 * qq + w;
-        if (i >= W) break;                                        // wave-uniform
-        const int nb = min(clip, m + i + 1);                      // band distances 0 .. nb-1
-        if (lane < DP) {
-            sm.q[w][0][lane] = to_f32(qu[((long long)bh * Wp + i) * DP + lane]);
-            sm.q[w][1][lane] = to_f32(qv[((long long)bh * Wp + i) * DP + lane]);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const float l = lse[(long long)bh * Wp + i];
-        for (int d = lane; d < nb; d += 64) {
-            const uint32_t *kr = sm.k + (m + i - d - jlo) * PD;
-            const uint32_t *ar = sm.ak + d * PD;
-            float s[4] = {0.f, 0.f, 0.f, 0.f};       // four independent chains
+
+    const int iw = i0 + 32 * w;
+    if (iw >= A.W) return;                               // no barrier follows
+    const int qi = iw + fr;
+    const bool q_ok = qi < A.W;
+    const int qc = min(qi, A.Wp - 1);
+    const T *qu = (const T *)A.qu + ((long long)bh * A.Wp + qc) * DP;
+    const T *qv = (const T *)A.qv + ((long long)bh * A.Wp + qc) * DP;
+    Frag<T> fqu[NS], fqv[NS];
 #pragma unroll
-            for (int u = 0; u < RD; ++u) {
-                s[u & 3] = dot_dw<T>(kr[u], &sm.q[w][0][EPD * u], s[u & 3]);
-                s[u & 3] = dot_dw<T>(ar[u], &sm.q[w][1][EPD * u], s[u & 3]);
-            }
-            sm.p[w][d] = exp2f(((s[0] + s[1]) + (s[2] + s[3])) - l);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < dh) {
-            float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-            int d = 0;
-            for (; d + 4 <= nb; d += 4) {
-                acc0 = fmaf(sm.p[w][d], sm.dv[d * DP + lane], acc0);
-                acc1 = fmaf(sm.p[w][d + 1], sm.dv[(d + 1) * DP + lane], acc1);
-                acc2 = fmaf(sm.p[w][d + 2], sm.dv[(d + 2) * DP + lane], acc2);
-                acc3 = fmaf(sm.p[w][d + 3], sm.dv[(d + 3) * DP + lane], acc3);
-            }
-            for (; d < nb; ++d) acc0 = fmaf(sm.p[w][d], sm.dv[d * DP + lane], acc0);
-            T *dst = o + ((long long)b * W + i) * D + (long long)h * dh + lane;
-            *dst = from_f32<T>(to_f32(*dst) + (tail + ((acc0 + acc1) + (acc2 + acc3))));
-        }
-        // the next query reuses q and p of this wave
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int s = 0; s < NS; ++s) {
+        load8(fqu[s], qu + 16 * s + 8 * hf);
+        load8(fqv[s], qv + 16 * s + 8 * hf);
     }
+    const float lse = q_ok ? A.lse[(long long)bh * A.Wp + qi] : 0.f;
+
+    f32x16 oacc[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) oacc[o] = zero16();
+    if (clip > 0) {
+        // ---- content scores of the band keys jb .. je, key order, into the wave's rows
+        const int je = min(A.K - 1, m + iw + 31);
+        const int jb = max(0, m + iw - clip + 1);
+        const int nkb = (je - jb + 32) / 32;               // <= 5
+        const T *ke = (const T *)A.ke + (long long)bh * A.C * DP;
+        float *crow_p = sm.cs[w] + fr * kShawPitch;
+#pragma unroll
+        for (int kb = 0; kb < kShawBand / 32; ++kb) {
+            if (kb < nkb) {
+                int j = min(jb + 32 * kb + fr, je);        // rows past je load a valid key, never read
+                j += A.khead;
+                if (j >= A.C) j -= A.C;
+                f32x16 sc = zero16();
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    Frag<T> fk;
+                    load8(fk, ke + (long long)j * DP + 16 * s + 8 * hf);
+                    mma16(sc, fk, fqu[s]);
+                }
+                write_gblock(crow_p, sc, 32 * kb, hf);
+            }
+        }
+        // ---- distance scores G (distance order), p, and the value product
+        const int base0 = m + iw - jb;                     // key position of distance 0 for query iw
+        wave_lds_sync();
+#pragma unroll
+        for (int db = 0; db < kShawMaxClip / 32; ++db) {
+            if (db < ndb) {
+                f32x16 g = zero16();
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    Frag<T> fa;
+                    load8(fa, reinterpret_cast<const T *>(sm.ak + (32 * db + fr) * SM::kPitchAK) + 16 * s + 8 * hf);
+                    mma16(g, fa, fqv[s]);
+                }
+                // register i: distance d = 32 db + crow(i) of query qi, key position base0 + fr - d
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int d = 32 * db + crow(i, lane);
+                    const int jj = max(base0 + fr - d, 0);
+                    const bool ok = q_ok && d < clip && d <= m + qi;
+                    g[i] = ok ? __builtin_amdgcn_exp2f(crow_p[jj] + g[i] - lse) : 0.f;
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    Frag<T> fp;
+                    p_frag(fp, g, 8 * half);
+#pragma unroll
+                    for (int o = 0; o < NO; ++o) {
+                        Frag<T> fv;
+                        load_vt(fv, sm.dvt + (32 * o + fr) * SM::kPitchDV, 32 * db + 16 * half + 4 * hf);
+                        mma16(oacc[o], fv, fp);
+                    }
+                }
+            }
+        }
+    }
+    if (!q_ok) return;
+    T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.D + h * dh;
+#pragma unroll
+    for (int o = 0; o < NO; ++o)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int c = 32 * o + crow(i, lane);
+            if (c < dh) orow[c] = from_f32<T>(to_f32(orow[c]) + oacc[o][i] + to_f32(aV[(long long)clip * dh + c]));
+        }
 }
 
 // y[b][t] = x[b][t] + U[pos0 + t], U the [sin | cos] sinusoid of the absolute
@@ -206,10 +232,9 @@ hipError_t launch_shaw_rows(bool is_bf16, void *rk, const void *aK, int clip, in
 
 template <typename T, int DP>
 void launch_shaw_values_t(const AttnArgs &a, const void *aK, const void *aV, int clip, hipStream_t s) {
-    const int nqb = (a.W + kShawQueries - 1) / kShawQueries;
-    hipLaunchKernelGGL((shaw_values_kernel<T, DP>), dim3(a.B * a.H * nqb), dim3(256), 0, s, (const T *)a.qu,
-                       (const T *)a.qv, (const T *)a.ke, (const T *)aK, (const float *)a.lse, (const T *)aV,
-                       (T *)a.o, a.H, a.W, a.Wp, a.m, a.Kp, a.dh, a.D, clip);
+    const int nqb = (a.W + 127) / 128;
+    hipLaunchKernelGGL((shaw_values_kernel<T, DP>), dim3(a.B * a.H * nqb), dim3(256), 0, s, a, (const T *)aK,
+                       (const T *)aV, clip);
 }
 
 template <typename T>
