@@ -43,31 +43,31 @@ __global__ void shaw_rows_kernel(T *rk, const T *aK, int clip, int K, int rows, 
 //   sum_j p_ij aV[min(delta, clip)] = aV[clip] + sum_{delta < min(clip, m+i+1)} p_i(delta) (aV[delta] - aV[clip]),
 // a product over at most 128 distances per query, which runs on the matrix
 // cores. A workgroup takes 128 queries of one (b, h), 32 per wave, as the
-// attention kernel does, and stages once aK (rows d < clip, zero-padded to dp
-// columns) and (aV[d] - aV[clip])^T. Per wave:
-//   - content scores of the band's keys m + i_wave - clip + 1 .. m + i_wave + 31
-//     (at most 159), K (q+u)^T, stored to LDS per query in key order;
-//   - the distance scores G = aK (q+v)^T, directly in distance order;
-//   - each lane reads its content scores back skewed into distance order
-//     (key m + i - d of query i), p = exp2(s - lse) with the attention
-//     kernel's log-sum-exp, masked to d < min(clip, m + i + 1);
-//   - O^T += (aV - aV[clip])^T P^T, then o += O + aV[clip].
+// attention kernel does, and stages (aV[d] - aV[clip])^T once. Per wave and
+// chunk of 64 distances (at most two):
+//   - content scores K (q+u)^T of the 95 keys the chunk reaches (key
+//     m + i_wave + a - d for query a), written per query in key order to the
+//     wave's band buffer;
+//   - distance scores G = aK (q+v)^T in distance order, aK read from the
+//     attention kernel's distance table (row ATTN_RPAD + d holds aK[min(d, clip)]);
+//   - the content score of distance d read back at band position a - d' + 63
+//     (d' = d - 64 chunk), p = exp2(s - lse) with the attention kernel's
+//     log-sum-exp, masked to d < min(clip, m + i + 1);
+//   - O^T += (aV - aV[clip])^T P^T; finally o += O + aV[clip].
+// 68 KB of LDS for bf16: two workgroups per CU.
 constexpr int kShawMaxClip = 128;
-constexpr int kShawBand = kShawMaxClip + 32;        // keys of one wave's band (at most 159)
-constexpr int kShawPitch = kShawBand + 4;           // floats per query row: 16-byte writes, skewed reads on distinct banks
 
 template <typename T, int DP>
 struct ShawSmem {
     static constexpr int NO = (DP + 31) / 32;
-    static constexpr int kPitchAK = DP * (int)sizeof(T) + 16;                          // aK row, bytes
     static constexpr int kPitchDV = kShawMaxClip * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);   // dV^T row, bytes
-    float cs[4][32 * kShawPitch];
-    char ak[kShawMaxClip * kPitchAK];
+    float g[4][32 * kGPitch];
     char dvt[NO * 32 * kPitchDV];
 };
 
 template <typename T, int DP>
-__global__ void __launch_bounds__(256, 1) shaw_values_kernel(const AttnArgs A, const T *aK, const T *aV, int clip) {
+__global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) shaw_values_kernel(const AttnArgs A, const T *aK,
+                                                                                     const T *aV, int clip) {
     typedef ShawSmem<T, DP> SM;
     constexpr int NS = DP / 16, NO = SM::NO;
     __shared__ SM sm;
@@ -78,15 +78,9 @@ __global__ void __launch_bounds__(256, 1) shaw_values_kernel(const AttnArgs A, c
     const int i0 = (blockIdx.x - bh * nqb) * 128;
     const int b = bh / A.H, h = bh - b * A.H;
     const int m = A.m, dh = A.dh;
-    const int ndb = (clip + 31) / 32;                    // 32-distance blocks of the band
+    (void)aK;                                            // read through the distance table A.rk
 
-    // staging: aK rows d < clip (zero past dh), and dV^T[c][d] = aV[d][c] - aV[clip][c]
-    // (zero for d >= clip or c >= dh)
-    for (int idx = tid; idx < kShawMaxClip * DP; idx += 256) {
-        const int d = idx / DP, c = idx - d * DP;
-        const float x = (d < clip && c < dh) ? to_f32(aK[(long long)d * dh + c]) : 0.f;
-        reinterpret_cast<T *>(sm.ak + d * SM::kPitchAK)[c] = from_f32<T>(x);
-    }
+    // dV^T[c][d] = aV[d][c] - aV[clip][c] (zero for d >= clip or c >= dh)
     for (int idx = tid; idx < NO * 32 * kShawMaxClip; idx += 256) {
         const int c = idx / kShawMaxClip, d = idx - c * kShawMaxClip;
         const float x = (d < clip && c < dh) ? to_f32(aV[(long long)d * dh + c]) - to_f32(aV[(long long)clip * dh + c])
@@ -109,53 +103,54 @@ __global__ void __launch_bounds__(256, 1) shaw_values_kernel(const AttnArgs A, c
         load8(fqv[s], qv + 16 * s + 8 * hf);
     }
     const float lse = q_ok ? A.lse[(long long)bh * A.Wp + qi] : 0.f;
+    const T *ke = (const T *)A.ke + (long long)bh * A.C * DP;
+    const T *rtab = (const T *)A.rk;                     // one table for every head
+    const int roff = rk_frag_off(m);
+    float *grow = sm.g[w] + fr * kGPitch;
 
     f32x16 oacc[NO];
 #pragma unroll
     for (int o = 0; o < NO; ++o) oacc[o] = zero16();
-    if (clip > 0) {
-        // ---- content scores of the band keys jb .. je, key order, into the wave's rows
-        const int je = min(A.K - 1, m + iw + 31);
-        const int jb = max(0, m + iw - clip + 1);
-        const int nkb = (je - jb + 32) / 32;               // <= 5
-        const T *ke = (const T *)A.ke + (long long)bh * A.C * DP;
-        float *crow_p = sm.cs[w] + fr * kShawPitch;
+    for (int dc = 0; 64 * dc < clip; ++dc) {
+        // ---- content scores of keys jbase .. jbase + 95, key order
+        const int jbase = m + iw - 64 * dc - 63;
+        wave_lds_sync();                                 // the previous chunk's reads are done
 #pragma unroll
-        for (int kb = 0; kb < kShawBand / 32; ++kb) {
-            if (kb < nkb) {
-                int j = min(jb + 32 * kb + fr, je);        // rows past je load a valid key, never read
-                j += A.khead;
-                if (j >= A.C) j -= A.C;
-                f32x16 sc = zero16();
+        for (int kb = 0; kb < 3; ++kb) {
+            int j = min(max(jbase + 32 * kb + fr, 0), A.K - 1);    // out-of-range keys are masked below
+            j += A.khead;
+            if (j >= A.C) j -= A.C;
+            f32x16 sc = zero16();
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    Frag<T> fk;
-                    load8(fk, ke + (long long)j * DP + 16 * s + 8 * hf);
-                    mma16(sc, fk, fqu[s]);
-                }
-                write_gblock(crow_p, sc, 32 * kb, hf);
+            for (int s = 0; s < NS; ++s) {
+                Frag<T> fk;
+                load8(fk, ke + (long long)j * DP + 16 * s + 8 * hf);
+                mma16(sc, fk, fqu[s]);
             }
+            write_gblock(grow, sc, 32 * kb, hf);
         }
-        // ---- distance scores G (distance order), p, and the value product
-        const int base0 = m + iw - jb;                     // key position of distance 0 for query iw
         wave_lds_sync();
+        // ---- distance scores, p and the value product, 32 distances at a time
+        const float *rb = grow + fr - 4 * hf;
 #pragma unroll
-        for (int db = 0; db < kShawMaxClip / 32; ++db) {
-            if (db < ndb) {
+        for (int db = 0; db < 2; ++db) {
+            const int d0 = 64 * dc + 32 * db;
+            if (d0 < clip) {
                 f32x16 g = zero16();
+                const int row = ATTN_RPAD + d0 + fr;
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     Frag<T> fa;
-                    load8(fa, reinterpret_cast<const T *>(sm.ak + (32 * db + fr) * SM::kPitchAK) + 16 * s + 8 * hf);
+                    load8(fa, rtab + rk_elem(row, 16 * s + 8 * hf, roff, DP));
                     mma16(g, fa, fqv[s]);
                 }
-                // register i: distance d = 32 db + crow(i) of query qi, key position base0 + fr - d
+                // register i: distance d0 + crow(i) of query qi, band position fr - (32 db + crow(i)) + 63
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int d = 32 * db + crow(i, lane);
-                    const int jj = max(base0 + fr - d, 0);
+                    const int d = d0 + crow(i, lane);
                     const bool ok = q_ok && d < clip && d <= m + qi;
-                    g[i] = ok ? __builtin_amdgcn_exp2f(crow_p[jj] + g[i] - lse) : 0.f;
+                    const float c = rb[63 - 32 * db - 8 * (i >> 2) - (i & 3)];
+                    g[i] = ok ? __builtin_amdgcn_exp2f(c + g[i] - lse) : 0.f;
                 }
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -164,7 +159,7 @@ __global__ void __launch_bounds__(256, 1) shaw_values_kernel(const AttnArgs A, c
 #pragma unroll
                     for (int o = 0; o < NO; ++o) {
                         Frag<T> fv;
-                        load_vt(fv, sm.dvt + (32 * o + fr) * SM::kPitchDV, 32 * db + 16 * half + 4 * hf);
+                        load_vt(fv, sm.dvt + (32 * o + fr) * SM::kPitchDV, d0 + 16 * half + 4 * hf);
                         mma16(oacc[o], fv, fp);
                     }
                 }
