@@ -80,9 +80,11 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) shaw_values_ker
     const int m = A.m, dh = A.dh;
     (void)aK;                                            // read through the distance table A.rk
 
-    // dV^T[c][d] = aV[d][c] - aV[clip][c] (zero for d >= clip or c >= dh)
-    for (int idx = tid; idx < NO * 32 * kShawMaxClip; idx += 256) {
-        const int c = idx / kShawMaxClip, d = idx - c * kShawMaxClip;
+    // dV^T[c][d] = aV[d][c] - aV[clip][c] for the distances the products read,
+    // d < clip rounded up to 32 (zero for d >= clip or c >= dh); reads along c
+    const int dlim = min(kShawMaxClip, (clip + 31) / 32 * 32);
+    for (int idx = tid; idx < dlim * NO * 32; idx += 256) {
+        const int d = idx / (NO * 32), c = idx - d * (NO * 32);
         const float x = (d < clip && c < dh) ? to_f32(aV[(long long)d * dh + c]) - to_f32(aV[(long long)clip * dh + c])
                                              : 0.f;
         reinterpret_cast<T *>(sm.dvt + c * SM::kPitchDV)[d] = from_f32<T>(x);
