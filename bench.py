@@ -473,6 +473,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -552,7 +553,11 @@ def main():
                      "median_launch_us": float(np.median(launch_ms)) * 1e3, "min_launch_us": launch_ms[0] * 1e3,
                      "frac_at_min_launch": a_flops / (launch_ms[0] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                      "algorithmic_flops_per_launch": a_flops,
-                     "compulsory_bytes_per_launch": attn_bytes(B, W, m, D, 2)},
+                     "compulsory_bytes_per_launch": attn_bytes(B, W, m, D, 2),
+                     # the peak again from this run's compute-unit count at the published
+                     # 2.4 GHz (4096 dense bf16 flop per clock per CU); equal to "peak" on MI355X
+                     "device": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+                     "peak_from_compute_units": props.multi_processor_count * 2.4e9 * 4096 / 1e12},
         "attn_tokens_per_s": B * W / a_avg_s,
         "step_tflops": (a_flops + proj_flops(B, W, m, D)) / (ms_per_step * 1e-3) / 1e12,
     }
