@@ -323,7 +323,7 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
         a.nsplit = 1;
     }
     TXL_TRY(hip_check(attn_launch(bf, a, s), "attention launch"));
-    if (a.lse) TXL_TRY(hip_check(launch_shaw_values(bf, a, var->aK, var->aV, var->clip, s), "value-term launch"));
+    if (a.lse) TXL_TRY(hip_check(launch_shaw_values(bf, a, var->aV, var->clip, s), "value-term launch"));
     return TXL_OK;
 }
 

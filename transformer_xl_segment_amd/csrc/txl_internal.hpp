@@ -155,9 +155,9 @@ int shaw_max_clip();
 // Shaw's distance keys: one table in the rk_elem layout (row offset off), row ATTN_RPAD + d = aK[min(d, clip)]
 hipError_t launch_shaw_rows(bool is_bf16, void *rk, const void *aK, int clip, int K, int Kp, int dh, int dp,
                             int off, hipStream_t s);
-// Shaw's value term added to a.o, from a.qu, a.qv, a.ke, a.lse of a finished attention launch and aK
-hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aK, const void *aV, int clip,
-                              hipStream_t s);
+// Shaw's value term added to a.o, from a.qu, a.qv, a.ke, a.lse and the distance table a.rk (the aK rows)
+// of a finished attention launch
+hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aV, int clip, hipStream_t s);
 hipError_t launch_add_positions(bool is_bf16, const void *x, long long x_bstride, void *y, long long y_bstride,
                                 int B, int W, int D, int pos0, hipStream_t s);
 

@@ -66,8 +66,8 @@ struct ShawSmem {
 };
 
 template <typename T, int DP>
-__global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) shaw_values_kernel(const AttnArgs A, const T *aK,
-                                                                                     const T *aV, int clip) {
+__global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) shaw_values_kernel(const AttnArgs A, const T *aV,
+                                                                                     int clip) {
     typedef ShawSmem<T, DP> SM;
     constexpr int NS = DP / 16, NO = SM::NO;
     __shared__ SM sm;
@@ -78,7 +78,6 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) shaw_values_ker
     const int i0 = (blockIdx.x - bh * nqb) * 128;
     const int b = bh / A.H, h = bh - b * A.H;
     const int m = A.m, dh = A.dh;
-    (void)aK;                                            // read through the distance table A.rk
 
     // dV^T[c][d] = aV[d][c] - aV[clip][c] for the distances the products read,
     // d < clip rounded up to 32 (zero for d >= clip or c >= dh); reads along c
@@ -228,27 +227,25 @@ hipError_t launch_shaw_rows(bool is_bf16, void *rk, const void *aK, int clip, in
 }
 
 template <typename T, int DP>
-void launch_shaw_values_t(const AttnArgs &a, const void *aK, const void *aV, int clip, hipStream_t s) {
+void launch_shaw_values_t(const AttnArgs &a, const void *aV, int clip, hipStream_t s) {
     const int nqb = (a.W + 127) / 128;
-    hipLaunchKernelGGL((shaw_values_kernel<T, DP>), dim3(a.B * a.H * nqb), dim3(256), 0, s, a, (const T *)aK,
-                       (const T *)aV, clip);
+    hipLaunchKernelGGL((shaw_values_kernel<T, DP>), dim3(a.B * a.H * nqb), dim3(256), 0, s, a, (const T *)aV, clip);
 }
 
 template <typename T>
-hipError_t launch_shaw_values_dp(const AttnArgs &a, const void *aK, const void *aV, int clip, hipStream_t s) {
+hipError_t launch_shaw_values_dp(const AttnArgs &a, const void *aV, int clip, hipStream_t s) {
     switch (a.dp) {
-        case 16: launch_shaw_values_t<T, 16>(a, aK, aV, clip, s); break;
-        case 32: launch_shaw_values_t<T, 32>(a, aK, aV, clip, s); break;
-        case 48: launch_shaw_values_t<T, 48>(a, aK, aV, clip, s); break;
-        case 64: launch_shaw_values_t<T, 64>(a, aK, aV, clip, s); break;
+        case 16: launch_shaw_values_t<T, 16>(a, aV, clip, s); break;
+        case 32: launch_shaw_values_t<T, 32>(a, aV, clip, s); break;
+        case 48: launch_shaw_values_t<T, 48>(a, aV, clip, s); break;
+        case 64: launch_shaw_values_t<T, 64>(a, aV, clip, s); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aK, const void *aV, int clip,
-                              hipStream_t s) {
-    return is_bf16 ? launch_shaw_values_dp<bf16>(a, aK, aV, clip, s) : launch_shaw_values_dp<float>(a, aK, aV, clip, s);
+hipError_t launch_shaw_values(bool is_bf16, const AttnArgs &a, const void *aV, int clip, hipStream_t s) {
+    return is_bf16 ? launch_shaw_values_dp<bf16>(a, aV, clip, s) : launch_shaw_values_dp<float>(a, aV, clip, s);
 }
 
 hipError_t launch_add_positions(bool is_bf16, const void *x, long long x_bstride, void *y, long long y_bstride,
