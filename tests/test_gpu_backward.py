@@ -66,6 +66,21 @@ def test_backward_small(dtype, case):
     assert max(errs.values()) <= TOL[dtype], errs
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_backward_sharp_scores(dtype):
+    # stress run: sharp softmax rows (score std about 1.4 s^2 for operand scale s: ~11
+    # for fp32 at s = 2.8, ~3 for bf16 at s = 1.5, whose q/k rounding moves a score by
+    # ~|s| 2^-8), so p and dS come from the log-sum-exp path far from uniform rows
+    B, D, H, W, m = 2, 128, 2, 70, 90
+    say(f"backward sharp scores {dtype}")
+    x = _inputs(9400, B, W, m, D, dtype, scale=2.8 if dtype == "fp32" else 1.5)
+    g = _gpu(x, H, dtype)
+    ref = orc.rel_attn_bwd(x["q"], x["k"], x["val"], x["r"], x["u"], x["v"], x["dO"], H)
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
+    say(f"  errors {errs}")
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
 def test_backward_headline_shape_bf16():
     # attn_w512_bf16's shape per batch row (W = m = 512, D = 512, 8 heads of 64)
     # with two batch rows, so the batch sums of dr, du, dv are exercised too
