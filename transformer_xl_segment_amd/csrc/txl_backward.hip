@@ -3,11 +3,12 @@
 //
 // The packing builds the head-major operands the attention kernels read (the
 // pre-scaled (q + u) and (q + v), dO, keys, values, the two distance-key
-// tables) and the transposed ones the batched GEMMs of dval, dk and dr take;
-// the unpacking turns the head-major fp32 gradients back into row layouts and
-// sums du, dv (the column sums of dq's two parts, "Transformer-XL,
-// explained.", the u and v legend entries: one vector per model, shared by
-// every query).
+// tables) and the transposed ones the batched GEMMs of dval, dk and dr take.
+// The reductions sum dr's per-(batch, head) parts over the batch and du, dv
+// from the fused kernel's per-wave partials (the column sums of dq's two
+// parts; "Transformer-XL, explained.", the u and v legend entries: one vector
+// per model, shared by every query). dq, dk and dval are written in their row
+// layouts by the fused kernel and the GEMM epilogue.
 #include "txl_device.hpp"
 #include "txl_internal.hpp"
 
