@@ -94,6 +94,20 @@ def test_backward_headline_shape_bf16():
     assert max(errs.values()) <= TOL["bf16"], errs
 
 
+def test_backward_wide_launch_bf16():
+    # 8 batch rows x 8 heads over K = 512 keys: the gradient GEMMs take 768 tiles, enough for
+    # their 128 x 64 tile path (the smaller cases run the 128 x 128 one); all six gradients,
+    # dr, du and dv summed over every batch row
+    B, D, H, W, m = 8, 512, 8, 128, 384
+    say("backward wide launch bf16")
+    x = _inputs(9500, B, W, m, D, "bf16", scale=0.5)
+    g = _gpu(x, H, "bf16")
+    ref = orc.rel_attn_bwd(x["q"], x["k"], x["val"], x["r"], x["u"], x["v"], x["dO"], H)
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES}
+    say(f"  errors {errs}")
+    assert max(errs.values()) <= TOL["bf16"], errs
+
+
 def test_backward_full_batch_rows_bf16():
     # the full batch of 16: per-row gradients of rows 0 and 15 against the oracle
     # on those rows alone (rows are independent for dq, dk, dval)
