@@ -58,7 +58,7 @@ def lib() -> ctypes.CDLL:
         L.orc_layer_fwd.argtypes = [ctypes.c_int] * 6 + [_dp] * 2 + [_dp] * 7 + [_dp] * 8 + [_dp, ctypes.c_int, _dp]
         L.orc_mem_update.argtypes = [ctypes.c_int] * 4 + [_dp, ctypes.c_int, _dp, _dp, _ip]
         L.orc_stack_fwd.argtypes = ([ctypes.c_int] * 9 + [_dp] + [_dp] * 7 + [_dp] * 8
-                                    + [_dp, ctypes.c_int, _dp, _dp, _ip])
+                                    + [_dp, ctypes.c_int, _dp, _dp, _ip, _dp, _ip])
         L.orc_attn_variant.argtypes = [ctypes.c_int] * 6 + [_dp] * 8 + [ctypes.c_int, _dp]
         L.orc_add_positions.argtypes = [ctypes.c_int] * 4 + [_dp, _dp]
         L.orc_rel_attn_bwd.argtypes = [ctypes.c_int] * 5 + [_dp] * 13
@@ -228,8 +228,13 @@ def mem_update(mem: Optional[np.ndarray], h: np.ndarray, M: int) -> np.ndarray:
 
 
 def stack_fwd(x: np.ndarray, params: Sequence[Dict[str, np.ndarray]], R: np.ndarray, H: int,
-              W: int, M: int, full_layer: bool) -> Tuple[np.ndarray, List[np.ndarray]]:
+              W: int, M: int, full_layer: bool,
+              mems0: Optional[Sequence[np.ndarray]] = None) -> Tuple[np.ndarray, List[np.ndarray]]:
     """Segment-by-segment forward over the stream x [B, S*W, D].
+
+    ``mems0`` (optional): the logical memory of every layer to start from
+    ([B, m_l, D] each, oldest row first, m_l <= M), as returned by an earlier
+    call; by default every memory starts empty.
 
     Returns y [B, S*W, D] (last layer's output per segment) and the final
     logical memory of every layer ([B, m_l, D] each).
@@ -255,9 +260,21 @@ def stack_fwd(x: np.ndarray, params: Sequence[Dict[str, np.ndarray]], R: np.ndar
     y = np.empty_like(x)
     mems = np.zeros((L, B, M, D))
     lens = (ctypes.c_int * L)()
+    mems_in, lens_in = None, None
+    if mems0 is not None:
+        assert len(mems0) == L
+        mems_in = np.zeros((L, B, M, D))
+        lens_in = (ctypes.c_int * L)()
+        for l, mm in enumerate(mems0):
+            ml = 0 if mm is None else mm.shape[1]
+            assert ml <= M
+            if ml:
+                mems_in[l, :, :ml] = _f64(mm)
+            lens_in[l] = ml
     st = lib().orc_stack_fwd(B, W, D, H, F, L, S, M, 1 if full_layer else 0, _ptr(x),
                              *[_ptr(a) for a in arrs], *[_ptr(a) for a in lay],
                              _ptr(R), R.shape[0], _ptr(y), _ptr(mems),
-                             ctypes.cast(lens, _ip))
+                             ctypes.cast(lens, _ip), _ptr(mems_in),
+                             None if lens_in is None else ctypes.cast(lens_in, _ip))
     _check(st, "stack_fwd")
     return y, [mems[l, :, :lens[l]].copy() for l in range(L)]

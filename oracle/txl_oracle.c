@@ -515,9 +515,11 @@ int orc_mem_update(int B, int M, int D, int m, const double *mem, int W, const d
  * cache of layer n-1's states). Layer parameters are stacked along a leading
  * axis of size L. full_layer = 0 runs the attention + output projection only
  * (single-layer attention workloads); full_layer = 1 runs the post-LN block.
- * The memory of every layer starts empty. y [B][S*W][D] receives the last
- * layer's output per segment; mems_out (optional, [L][B][M][D]) and
- * mem_len_out (optional, [L]) receive the final memories.
+ * The memory of every layer starts empty, or, when mems_in ([L][B][M][D],
+ * oldest row first) and mem_len_in ([L]) are given, holds those rows (a stream
+ * resumed after earlier segments). y [B][S*W][D] receives the last layer's
+ * output per segment; mems_out (optional, [L][B][M][D]) and mem_len_out
+ * (optional, [L]) receive the final memories in the same form.
  */
 int orc_stack_fwd(int B, int W, int D, int H, int F, int L, int S, int M, int full_layer,
                   const double *x,
@@ -527,10 +529,15 @@ int orc_stack_fwd(int B, int W, int D, int H, int F, int L, int S, int M, int fu
                   const double *ln1_g, const double *ln1_b,
                   const double *W1, const double *b1, const double *W2, const double *b2,
                   const double *ln2_g, const double *ln2_b,
-                  const double *R, int R_len, double *y, double *mems_out, int *mem_len_out)
+                  const double *R, int R_len, double *y, double *mems_out, int *mem_len_out,
+                  const double *mems_in, const int *mem_len_in)
 {
     if (B < 1 || W < 1 || D < 1 || H < 1 || L < 1 || S < 1 || M < 1 || !x || !y) return ORC_ERR_ARG;
     if (full_layer && F < 1) return ORC_ERR_ARG;
+    if ((mems_in == NULL) != (mem_len_in == NULL)) return ORC_ERR_ARG;
+    if (mem_len_in)
+        for (int l = 0; l < L; ++l)
+            if (mem_len_in[l] < 0 || mem_len_in[l] > M) return ORC_ERR_ARG;
     const size_t DD = (size_t)D * D;
     const size_t seg = (size_t)W * D;
     double *mems = calloc((size_t)L * B * M * D, sizeof(double));
@@ -541,6 +548,13 @@ int orc_stack_fwd(int B, int W, int D, int H, int F, int L, int S, int M, int fu
     if (!mems || !tmp_mem || !mlen || !hin || !hout) {
         free(mems); free(tmp_mem); free(mlen); free(hin); free(hout);
         return ORC_ERR_NOMEM;
+    }
+    /* a stream resumed from carried memories (same [L][B][M][D] layout and
+     * lengths as mems_out / mem_len_out): the memory is the only state that
+     * crosses a segment boundary, so nothing else is needed */
+    if (mems_in) {
+        memcpy(mems, mems_in, sizeof(double) * (size_t)L * B * M * D);
+        memcpy(mlen, mem_len_in, sizeof(int) * (size_t)L);
     }
     int st = ORC_OK;
     for (int t = 0; t < S && st == ORC_OK; ++t) {

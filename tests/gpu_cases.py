@@ -54,16 +54,19 @@ def nan_workspace(nbytes: int) -> torch.Tensor:
 
 
 def run_attn_segments(prob: syn.Problem, R: np.ndarray, batch: Optional[Sequence[int]] = None,
-                      warm: bool = False, check_every: bool = True) -> Dict[str, float]:
+                      warm: bool = False, check_every: bool = True,
+                      R_gpu: Optional[torch.Tensor] = None) -> Dict[str, float]:
     """Single-layer attention workloads: per segment rel_attn_fwd then mem_update,
-    compared with the oracle segment by segment (optionally on a batch subset)."""
+    compared with the oracle segment by segment (optionally on a batch subset).
+    The oracle always takes its own table R; the GPU takes R too unless R_gpu
+    (for instance the library's own txl_sinusoid_table output) is given."""
     wl = prob.wl
     dt = wl.dtype
     p = prob.params[0]
     B, W, D, H, M = prob.x.shape[0], wl.W, wl.D, wl.H, wl.M
     x = dev(prob.x, dt)
     params = tb.LayerParams.from_numpy(p, TDT[dt], "cuda")
-    Rd = dev(R, dt)
+    Rd = dev(R, dt) if R_gpu is None else R_gpu
     ring = tb.MemoryRing.empty(B, M, D, TDT[dt], "cuda")
     ws = nan_workspace(tb.workspace_bytes(tb.OP_REL_ATTN, TDT[dt], B, W, M, D, H))
     omem = None

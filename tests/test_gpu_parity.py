@@ -202,6 +202,19 @@ def test_workload_attn_w512_bf16():
     assert max(errs.values()) <= TOL[wl.dtype], errs
 
 
+def test_workload_attn_w512_bf16_library_table():
+    # end to end with the distance table the library computes itself
+    # (txl_sinusoid_table) on the GPU side; the oracle keeps its own fp64 table
+    wl = syn.WORKLOADS["attn_w512_bf16"]
+    say(f"workload {wl.name} with the library's sinusoid table")
+    prob = syn.draw_problem(wl)
+    R_len = wl.M + wl.W
+    Rg = tb.sinusoid_table(R_len, wl.D, TDT[wl.dtype], "cuda")
+    errs = run_attn_segments(prob, table(R_len, wl.D, wl.dtype), batch=[0, wl.B - 1], R_gpu=Rg)
+    say(f"  errors {errs}")
+    assert max(errs.values()) <= TOL[wl.dtype], errs
+
+
 @pytest.mark.parametrize("warm", [False, True])
 def test_workload_longmem_m1600_bf16(warm):
     wl = syn.WORKLOADS["longmem_m1600_bf16"]
@@ -220,6 +233,8 @@ def test_workload_stack16(name):
     wl = syn.WORKLOADS[name]
     say(f"workload {wl.name}")
     prob = syn.draw_problem(wl)
-    errs = _run_block_segments(prob, table(wl.M + wl.W, wl.D, wl.dtype), batch=[0])
+    # the first and the last batch row: the last one sits at a nonzero batch
+    # offset of every operand (d_model 410 rows are only dword-aligned)
+    errs = _run_block_segments(prob, table(wl.M + wl.W, wl.D, wl.dtype), batch=[0, wl.B - 1])
     say(f"  errors {errs}")
     assert max(errs.values()) <= TOL[wl.dtype], errs

@@ -1,0 +1,152 @@
+"""GPU tests of the carried state and of launch-shape independence.
+
+- A stream resumed from carried memory rings: k segments through
+  txl_stack_fwd_segments, then the remaining S - k segments in a second call
+  with the same rings, equal one straight call bit for bit and stay within
+  tolerance of the oracle ("Transformer-XL, explained.", method step 2: the
+  cache is the only state a segment takes from the past).
+- A softmax row dominated by one key of the first key block, so that one half
+  of the wave's lanes sees only underflowing probabilities in that block
+  while its later blocks hold visible keys (checked against the oracle).
+- The same rows through launches of different shapes (64- and 128-row GEMM
+  tiles, a key-split attention launch, the register-staged GEMM for operands
+  that are not 16-byte aligned) agree with each other and with the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from transformer_xl_segment_amd import binding as tb
+from transformer_xl_segment_amd import synthetic as syn
+
+from gpu_cases import TOL, TDT, dev, host, nan_workspace, rel_err, run_attn_segments, say, table
+
+pytestmark = pytest.mark.gpu
+
+
+def _stack_call(x, rings, params, Rd, H, W, F, ws):
+    return tb.stack_fwd_segments(x.contiguous(), rings, params, Rd, H, W, F, workspace=ws)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("W,M,k", [(30, 45, 2), (24, 16, 3), (40, 40, 1)])
+def test_stack_resume_bit_exact(dtype, W, M, k):
+    B, D, H, F, L, S = 2, 82, 2, 130, 3, 5
+    say(f"stack resume {dtype} W={W} M={M} split after {k}")
+    wl = syn.Workload("resume", dtype, B=B, D=D, H=H, W=W, M=M, S=S, F=F, layers=L, op="stack",
+                      seed_w=3000 + W, seed_x=4000 + M)
+    prob = syn.draw_problem(wl, affine=True, weight_scale=0.2 if dtype == "fp32" else 0.1)
+    tdt = TDT[dtype]
+    x = dev(prob.x, dtype)
+    params = [tb.LayerParams.from_numpy(p, tdt, "cuda") for p in prob.params]
+    R = table(M + W, D, dtype)
+    Rd = dev(R, dtype)
+    ws = nan_workspace(tb.workspace_bytes(tb.OP_STACK, tdt, B, W, M, D, H, F))
+    # straight run
+    rings = [tb.MemoryRing.empty(B, M, D, tdt, "cuda") for _ in range(L)]
+    y = _stack_call(x, rings, params, Rd, H, W, F, ws)
+    # split run: the second call starts from the rings the first left behind
+    rings2 = [tb.MemoryRing.empty(B, M, D, tdt, "cuda") for _ in range(L)]
+    ya = _stack_call(x[:, :k * W], rings2, params, Rd, H, W, F, ws)
+    yb = _stack_call(x[:, k * W:], rings2, params, Rd, H, W, F, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([ya, yb], dim=1), y)
+    for r1, r2 in zip(rings, rings2):
+        assert (r1.len, r1.head) == (r2.len, r2.head)
+        assert torch.equal(r1.logical(), r2.logical())
+    # and the resumed part against the oracle resumed from its own memories
+    _, mems_a = orc.stack_fwd(prob.x[:, :k * W], prob.params, R, H, W, M, full_layer=True)
+    ref_b, ref_mems = orc.stack_fwd(prob.x[:, k * W:], prob.params, R, H, W, M, full_layer=True,
+                                    mems0=mems_a)
+    yh = host(yb)
+    errs = {f"seg{k + t}": rel_err(yh[:, t * W:(t + 1) * W], ref_b[:, t * W:(t + 1) * W])
+            for t in range(S - k)}
+    for l, r in enumerate(rings2):
+        errs[f"mem{l}"] = rel_err(host(r.logical()), ref_mems[l])
+    say(f"  errors {errs}")
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_dominant_key_in_first_block(dtype):
+    # Every query prefers key 0 by 150 (natural units, after the 1/sqrt(dh)
+    # scale): with Wq = 0 the content score is u.k_j, u = 20 e_0, k_0 = 30 e_0
+    # and every other key orthogonal to e_0. In a query's first key block the
+    # keys held by the other half of the wave (4..7, 12..15, ...) then have
+    # probabilities below 2^-200, which underflow; its later blocks (queries
+    # >= 64 see keys 64.. and 128..) hold only such keys. The output is v_0 up
+    # to e^-150 terms.
+    B, D, H, W = 2, 16, 1, 200
+    rng = np.random.default_rng(77)
+    z = np.zeros((D, D))
+    I = np.eye(D)
+    p = {"Wq": z, "WkE": I, "WkR": z, "Wv": I, "Wo": I,
+         "u": 20.0 * I[0], "v": np.zeros(D)}
+    h = rng.standard_normal((B, W, D))
+    h[:, :, 0] = 0.0
+    h[:, 0, :] = 0.0
+    h[:, 0, 0] = 30.0
+    h[:, 0, 1] = 1.0
+    h = h.astype(np.float32)
+    if dtype == "bf16":
+        h = syn.round_to_bf16(h)
+    p = {k_: (syn.round_to_bf16(a.astype(np.float32)) if dtype == "bf16" else a.astype(np.float32))
+         for k_, a in p.items()}
+    R = table(W, D, dtype)
+    out = tb.rel_attn_fwd(dev(h, dtype), None, tb.LayerParams.from_numpy(p, TDT[dtype], "cuda"),
+                          dev(R, dtype), H)
+    torch.cuda.synchronize()
+    ref = orc.rel_attn(h.astype(np.float64), None, p, R, H)
+    g = host(out)
+    # the oracle's output is row 0 of h (v_0) for every query
+    np.testing.assert_allclose(ref, np.broadcast_to(h[:, :1, :].astype(np.float64), ref.shape), atol=1e-12)
+    e = rel_err(g, ref)
+    say(f"dominant key {dtype}: error {e:.3e}")
+    assert e <= TOL[dtype], e
+
+
+def _attn_once(prob, R, B_run, misaligned=False):
+    """One full-memory segment of the attention workload for the first B_run
+    rows; misaligned=True hands the rows over with a batch stride that is not a
+    multiple of 16 bytes (the register-staged GEMM path)."""
+    wl = prob.wl
+    dt = wl.dtype
+    W, D, H, M = wl.W, wl.D, wl.H, wl.M
+    tdt = TDT[dt]
+    params = tb.LayerParams.from_numpy(prob.params[0], tdt, "cuda")
+    Rd = dev(R, dt)
+    ring = tb.MemoryRing.empty(B_run, M, D, tdt, "cuda")
+    mem_rows = dev(prob.x[:B_run, :M], dt)
+    tb.mem_update(ring, mem_rows)
+    seg = prob.x[:B_run, M:M + W]
+    if misaligned:
+        buf = torch.zeros(B_run, W * D + 2, dtype=tdt, device="cuda")
+        buf[:, :W * D] = dev(seg, dt).reshape(B_run, W * D)
+        h = torch.as_strided(buf, (B_run, W, D), (W * D + 2, D, 1))
+    else:
+        h = dev(seg, dt)
+    out = tb.rel_attn_fwd(h, ring, params, Rd, H)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def test_launch_shapes_agree():
+    # headline shape: 16 rows (128-row GEMM tiles, one attention part per query
+    # block) against 1 row (64-row tiles, the key range split over 4 parts and
+    # merged) and against 16 rows with a 4-byte-aligned batch stride
+    wl = syn.WORKLOADS["attn_w512_bf16"]
+    wl = syn.Workload(**{**wl.__dict__, "S": 2})
+    prob = syn.draw_problem(wl)
+    say("launch shapes: headline attention, rows 0 and 15")
+    R = table(wl.M + wl.W, wl.D, wl.dtype)
+    a16 = _attn_once(prob, R, 16)
+    a1 = _attn_once(prob, R, 1)
+    am = _attn_once(prob, R, 16, misaligned=True)
+    ref = orc.rel_attn(prob.x[[0, 15], wl.M:wl.M + wl.W].astype(np.float64),
+                       prob.x[[0, 15], :wl.M].astype(np.float64), prob.params[0], R, wl.H)
+    errs = {"16_vs_oracle": rel_err(a16[[0, 15]], ref), "1_vs_oracle": rel_err(a1[[0]], ref[[0]]),
+            "misaligned_vs_oracle": rel_err(am[[0, 15]], ref),
+            "1_vs_16": rel_err(a1[0], a16[0]), "misaligned_vs_16": rel_err(am, a16)}
+    say(f"  errors {errs}; aligned and 4-byte-aligned rows bit-identical: {np.array_equal(am, a16)}")
+    assert max(errs.values()) <= TOL["bf16"], errs

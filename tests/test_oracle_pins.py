@@ -389,6 +389,45 @@ def test_reach_grows_one_segment_per_layer():
             np.testing.assert_array_equal(y[:, seg], y2[:, seg])
 
 
+@pytest.mark.parametrize("W,M,k", [(3, 5, 1), (4, 4, 2), (4, 2, 3), (3, 7, 2)])
+def test_resume_from_carried_memories_equals_straight_run(W, M, k):
+    # "Transformer-XL, explained.", method step 2: the cached states are the only
+    # thing a segment takes from the past, read as a fixed input. So k segments,
+    # then the remaining S - k segments started from the memories the first call
+    # left behind, give the straight S-segment run bit for bit (same arithmetic in
+    # the same order), outputs and final memories alike.
+    B, S, D, H, F, L = 2, 5, 8, 2, 16, 3
+    rng = np.random.default_rng(40 + 10 * W + M + k)
+    params = [_params(rng, D, F=F, affine=True) for _ in range(L)]
+    x = rng.standard_normal((B, S * W, D))
+    R = _R(M + W, D)
+    y, mems = orc.stack_fwd(x, params, R, H, W, M, full_layer=True)
+    ya, mems_a = orc.stack_fwd(x[:, :k * W], params, R, H, W, M, full_layer=True)
+    yb, mems_b = orc.stack_fwd(x[:, k * W:], params, R, H, W, M, full_layer=True, mems0=mems_a)
+    np.testing.assert_array_equal(np.concatenate([ya, yb], axis=1), y)
+    for l in range(L):
+        np.testing.assert_array_equal(mems_b[l], mems[l])
+    # layer 0's carried memory is the last min(M, kW) stack input rows; and the
+    # resumed part is not the same as a run from empty memories (the carry matters)
+    np.testing.assert_array_equal(mems_a[0], x[:, max(0, k * W - M):k * W])
+    y0, _ = orc.stack_fwd(x[:, k * W:], params, R, H, W, M, full_layer=True)
+    assert np.max(np.abs(y0[:, :W] - yb[:, :W])) > 1e-6
+
+
+def test_resume_single_layer_matches_stream_brute_force():
+    # the resumed attention-only run equals the brute-force stream attention of
+    # the whole stream on the segments after the split point
+    B, W, M, S, D, H, k = 2, 3, 5, 5, 8, 2, 2
+    rng = np.random.default_rng(44)
+    p = _params(rng, D)
+    x = rng.standard_normal((B, S * W, D))
+    R = _R(S * W, D)
+    _, mems_a = orc.stack_fwd(x[:, :k * W], [p], R, H, W, M, full_layer=False)
+    yb, _ = orc.stack_fwd(x[:, k * W:], [p], R, H, W, M, full_layer=False, mems0=mems_a)
+    ref = _stream_brute_force(x, p, R, H, W, M)
+    np.testing.assert_allclose(yb, ref[:, k * W:], rtol=1e-11, atol=1e-12)
+
+
 # --------------------------------------------------------------------------
 # Encodings Transformer-XL is compared against (Shaw et al.; absolute).
 # --------------------------------------------------------------------------

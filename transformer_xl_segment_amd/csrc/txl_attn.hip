@@ -241,8 +241,13 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     f32x16 oacc[NO];
 #pragma unroll
     for (int o = 0; o < NO; ++o) oacc[o] = zero16();
-    // running maximum (the base the scores are taken relative to) and sum
+    // running maximum (the base the scores are taken relative to) and sum;
+    // `started` turns true at the first block in which the query sees a key.
+    // It follows the block maximum mx, which both lanes of a query share, so
+    // the two halves of the wave always re-base together (l_run is only this
+    // half's partial sum and may stay zero while the other half's is not).
     float m_run = 0.f, l_run = 0.f;
+    bool started = false;
 
     // Band of key block kb: distances cw-63 .. cw+31 with cw = m + iw - 64*kb.
     // gb[kb & 1] holds the chunk cw-63 .. cw (two 32-distance blocks); the band's
@@ -331,7 +336,8 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
         mx = half_max(mx);
         // lazy re-base: to the first block's maximum, then whenever a block
         // maximum exceeds the base by more than 8
-        const bool rebase = mx > 8.f || (l_run == 0.f && mx > -INFINITY);
+        const bool rebase = mx > 8.f || (!started && mx > -INFINITY);
+        started = started || mx > -INFINITY;
         if (__any(rebase)) {
             const float shift = rebase ? mx : 0.f;
             const float alpha = __builtin_amdgcn_exp2f(-shift);
