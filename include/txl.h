@@ -34,7 +34,8 @@
  *    pre-LayerNorm residual sums are kept in fp32.
  *  - All pointers are device pointers unless stated otherwise; every buffer
  *    belongs to the caller. The library never allocates device memory: scratch
- *    space is the caller's workspace, sized by txl_workspace_bytes().
+ *    space is the caller's workspace, sized by txl_workspace_bytes() (the one
+ *    exception, txl_rel_attn_fwd_noalloc, uses a fixed array in the library).
  *  - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and
  *    nothing waits for it: results are ready when the stream reaches them.
  *  - Strides are in elements. `*_bstride` is the distance between batch rows;
@@ -165,6 +166,29 @@ txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H,
                             const void *R, int R_len,
                             void *out, long long out_bstride,
                             void *ws, size_t ws_bytes, void *stream);
+
+/* txl_rel_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, launches and results as
+ * txl_rel_attn_fwd; the scratch space is a fixed device array of
+ * TXL_NOALLOC_SCRATCH_BYTES inside the library instead of the caller's
+ * workspace. The call itself allocates nothing; each GPU the library is loaded
+ * on holds its own copy of the array until the process ends.
+ *  - A call whose workspace (txl_workspace_bytes(TXL_OP_REL_ATTN, dtype, B, W,
+ *    mem->len, D, H, 0)) exceeds TXL_NOALLOC_SCRATCH_BYTES returns
+ *    TXL_ERR_WORKSPACE before touching the device (64 MiB covers B = 16,
+ *    W = M = 512, D = 512 in bf16).
+ *  - Every call on one GPU shares that GPU's array and leaves its contents
+ *    behind; nothing in it needs to start zeroed (every scratch element is
+ *    written before it is read). Calls that overlap on one GPU (two streams,
+ *    or two threads) race on the array: serialize them.
+ *  - The calling thread's current device must be the device of `stream`. */
+#define TXL_NOALLOC_SCRATCH_BYTES (64u << 20)
+txl_status txl_rel_attn_fwd_noalloc(txl_dtype dtype, int B, int W, int D, int H,
+                                    const void *h, long long h_bstride,
+                                    const txl_mem *mem, const txl_layer_params *p,
+                                    const void *R, int R_len,
+                                    void *out, long long out_bstride, void *stream);
 
 /* Memory update (simulator: mem = last M rows of h~ = [mem; h]). Appends the
  * last min(W, M) rows of h [B][W][D] (batch stride h_bstride) to the ring,

@@ -87,6 +87,32 @@ def test_rel_attn_rejects_bad_arguments():
     assert b"workspace" in tb.lib().txl_last_error()
 
 
+def test_noalloc_rejects_bad_arguments_and_oversized_calls():
+    # every check of txl_rel_attn_fwd_noalloc runs before its first device call
+    L = tb.lib()
+    assert tb.NOALLOC_SCRATCH_BYTES == 64 << 20
+    import re
+    hdr = open(tb.HEADER_PATH).read()
+    assert re.search(r"#define TXL_NOALLOC_SCRATCH_BYTES \(64u << 20\)", hdr)
+    p = _params()
+
+    def call(B=1, W=4, D=16, H=2, hs=64, mem=None, R=FAKE, R_len=8, out=FAKE, os_=64, dt=tb.TXL_BF16):
+        return L.txl_rel_attn_fwd_noalloc(dt, B, W, D, H, FAKE, hs, ctypes.byref(mem) if mem else None,
+                                          ctypes.byref(p), R, R_len, out, os_, None)
+    assert call(D=18, H=4) == tb.TXL_ERR_ARG
+    assert call(dt=5) == tb.TXL_ERR_UNSUPPORTED
+    assert call(R=None) == tb.TXL_ERR_ARG
+    assert call(out=FAKE + 2) == tb.TXL_ERR_ARG
+    assert call(mem=tb._Mem(FAKE, 4, 5, 0)) == tb.TXL_ERR_ARG
+    # the headline shape fits the fixed scratch; twice its batch does not
+    ws = L.txl_workspace_bytes
+    assert ws(tb.OP_REL_ATTN, tb.TXL_BF16, 16, 512, 512, 512, 8, 0) <= tb.NOALLOC_SCRATCH_BYTES
+    assert ws(tb.OP_REL_ATTN, tb.TXL_BF16, 32, 512, 512, 512, 8, 0) > tb.NOALLOC_SCRATCH_BYTES
+    big = tb._Mem(FAKE, 512, 512, 0)
+    assert call(B=32, W=512, D=512, H=8, hs=512 * 512, os_=512 * 512, mem=big, R_len=1024) == tb.TXL_ERR_WORKSPACE
+    assert b"scratch" in L.txl_last_error()
+
+
 def test_mem_update_rejects_bad_arguments():
     L = tb.lib()
     m = tb._Mem(FAKE, 4, 0, 0)

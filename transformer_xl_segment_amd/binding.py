@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
         L.txl_workspace_bytes.restype = sz
         L.txl_sinusoid_table.argtypes = [i, i, i, vp, vp]
         L.txl_rel_attn_fwd.argtypes = [i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp, sz, vp]
+        L.txl_rel_attn_fwd_noalloc.argtypes = [i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp]
         L.txl_mem_update.argtypes = [i, i, i, Mp, vp, ll, i, vp]
         L.txl_layer_fwd.argtypes = [i, i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_stack_fwd_segments.argtypes = [i, i, i, i, i, i, i, i, vp, Mp, P, vp, i, vp, vp, sz, vp]
@@ -81,7 +82,7 @@ def lib() -> ctypes.CDLL:
         L.txl_profile_begin.argtypes = [i]
         L.txl_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.txl_profile_times.argtypes = [ctypes.POINTER(ctypes.c_double), i, ctypes.POINTER(ctypes.c_int)]
-        for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_mem_update", "txl_layer_fwd",
+        for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_rel_attn_fwd_noalloc", "txl_mem_update", "txl_layer_fwd",
                   "txl_stack_fwd_segments", "txl_stack_fwd_window", "txl_kv_cache_capacity",
                   "txl_attn_fwd_variant", "txl_add_positions", "txl_rel_attn_bwd", "txl_kv_cache_append",
                   "txl_rel_attn_fwd_cached", "txl_profile_begin", "txl_profile_end", "txl_profile_times"):
@@ -241,6 +242,28 @@ def rel_attn_fwd(h: torch.Tensor, mem: Optional[MemoryRing], params: LayerParams
                                   R.data_ptr(), R.shape[0], out.data_ptr(), os_, ws.data_ptr(),
                                   ws.numel() * ws.element_size(), _stream(h.device)),
            "txl_rel_attn_fwd")
+    return out
+
+
+# TXL_NOALLOC_SCRATCH_BYTES of txl.h: the fixed scratch of txl_rel_attn_fwd_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def rel_attn_fwd_noalloc(h: torch.Tensor, mem: Optional[MemoryRing], params: LayerParams, R: torch.Tensor,
+                         H: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """txl_rel_attn_fwd with the library's fixed scratch array in place of a
+    workspace (pass ``out`` to make the call allocate nothing at all)."""
+    B, W, D = h.shape
+    hs = _rows_view(h, "h")
+    if out is None:
+        out = torch.empty(B, W, D, dtype=h.dtype, device=h.device)
+    os_ = _rows_view(out, "out")
+    ms = mem._struct() if mem is not None else None
+    ps = params._struct()
+    _check(lib().txl_rel_attn_fwd_noalloc(dtype_code(h.dtype), B, W, D, H, h.data_ptr(), hs,
+                                          ctypes.byref(ms) if ms is not None else None, ctypes.byref(ps),
+                                          R.data_ptr(), R.shape[0], out.data_ptr(), os_, _stream(h.device)),
+           "txl_rel_attn_fwd_noalloc")
     return out
 
 

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -456,9 +457,12 @@ txl_status txl_sinusoid_table(txl_dtype dtype, int R_len, int D, void *R, void *
     return hip_check(launch_sinusoid(dtype == TXL_BF16, R, R_len, D, (hipStream_t)stream), "sinusoid launch");
 }
 
-txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H, const void *h, long long h_bstride,
-                            const txl_mem *mem, const txl_layer_params *p, const void *R, int R_len, void *out,
-                            long long out_bstride, void *ws, size_t ws_bytes, void *stream) {
+namespace {
+
+// Argument checks of txl_rel_attn_fwd and txl_rel_attn_fwd_noalloc (all but the workspace).
+txl_status check_rel_attn(txl_dtype dtype, int B, int W, int D, int H, const void *h, long long h_bstride,
+                          const txl_mem *mem, const txl_layer_params *p, const void *R, int R_len, const void *out,
+                          long long out_bstride) {
     TXL_TRY(check_shape(dtype, B, W, D, H));
     TXL_TRY(check_rows(h, h_bstride, W, D, dtype, "h"));
     TXL_TRY(check_rows(out, out_bstride, W, D, dtype, "out"));
@@ -468,6 +472,16 @@ txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H, const v
     TXL_TRY(check_rows_budget(B, W, m));
     if (!R || !al4(R)) return fail(TXL_ERR_ARG, "R must be a non-NULL 4-byte aligned pointer");
     if (R_len < m + W) return fail(TXL_ERR_ARG, "R_len=%d < mem len + W = %d", R_len, m + W);
+    return TXL_OK;
+}
+
+}  // namespace
+
+txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H, const void *h, long long h_bstride,
+                            const txl_mem *mem, const txl_layer_params *p, const void *R, int R_len, void *out,
+                            long long out_bstride, void *ws, size_t ws_bytes, void *stream) {
+    TXL_TRY(check_rel_attn(dtype, B, W, D, H, h, h_bstride, mem, p, R, R_len, out, out_bstride));
+    const int m = mem ? mem->len : 0;
     const Layout L = plan(TXL_OP_REL_ATTN, dtype, B, W, m + W, D, H, 0);
     if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
     if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
@@ -476,6 +490,60 @@ txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H, const v
     TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, mem, nullptr, p, R, w, L, s));
     GemmProblem wo = rows_problem(B, W, D, D, w + L.o, D, (long long)W * D, p->Wo, out, D, out_bstride);
     return hip_check(launch_gemm(dtype == TXL_BF16, single(wo), s), "output projection launch");
+}
+
+// ---------------------------------------------------------------------------
+// txl_rel_attn_fwd_noalloc: the same launches with the workspace in a fixed
+// device array. Each GPU the library runs on holds its own copy (module-load
+// memory, kept until the process ends). Host code never hands the array's name
+// to a kernel or a copy: its device address comes from hipGetSymbolAddress,
+// looked up once per device with that device current.
+// ---------------------------------------------------------------------------
+namespace {
+
+static_assert(TXL_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size must keep 256-byte alignment");
+static __device__ __align__(256) char scratch[TXL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxScratchDevices];
+
+// Device address of the current device's copy of `scratch`.
+txl_status scratch_address(void **out) {
+    int dev = -1;
+    TXL_TRY(hip_check(hipGetDevice(&dev), "hipGetDevice"));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(TXL_ERR_UNSUPPORTED, "device %d: txl_rel_attn_fwd_noalloc supports devices 0..%d", dev,
+                    kMaxScratchDevices - 1);
+    ScratchSlot &slot = g_scratch[dev];
+    std::call_once(slot.once, [&slot] { slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch)); });
+    if (slot.err != hipSuccess || !slot.ptr)
+        return fail(TXL_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(slot.err));
+    *out = slot.ptr;
+    return TXL_OK;
+}
+
+}  // namespace
+
+txl_status txl_rel_attn_fwd_noalloc(txl_dtype dtype, int B, int W, int D, int H, const void *h,
+                                    long long h_bstride, const txl_mem *mem, const txl_layer_params *p,
+                                    const void *R, int R_len, void *out, long long out_bstride, void *stream) {
+    TXL_TRY(check_rel_attn(dtype, B, W, D, H, h, h_bstride, mem, p, R, R_len, out, out_bstride));
+    const int m = mem ? mem->len : 0;
+    // sized by this call's key count; every check runs before any device call
+    const size_t need = plan(TXL_OP_REL_ATTN, dtype, B, W, m + W, D, H, 0).total;
+    if (need > (size_t)TXL_NOALLOC_SCRATCH_BYTES)
+        return fail(TXL_ERR_WORKSPACE, "txl_rel_attn_fwd_noalloc: this call needs %zu bytes of scratch, the fixed "
+                    "array holds %zu (call txl_rel_attn_fwd with a workspace instead)", need,
+                    (size_t)TXL_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    TXL_TRY(scratch_address(&ws));
+    return txl_rel_attn_fwd(dtype, B, W, D, H, h, h_bstride, mem, p, R, R_len, out, out_bstride, ws,
+                            (size_t)TXL_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 txl_status txl_mem_update(txl_dtype dtype, int B, int D, txl_mem *mem, const void *h, long long h_bstride, int W,
