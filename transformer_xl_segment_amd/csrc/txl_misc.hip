@@ -15,40 +15,37 @@ namespace txl {
 namespace {
 
 // Memory update (segment-recurrence simulator: mem = last M rows of [mem; h]).
-// The B * n rows to copy are one sequence of words (16 bytes, or 4 when a row
-// or a base is not 16-byte aligned); a 256-thread workgroup moves kRingUnroll
-// consecutive runs of 256 words, all loads issued before the stores.
+// For one batch row the n source rows are contiguous, and so are their ring
+// slots up to the wrap: the copy is two contiguous runs, slots pos0 .. M-1 and
+// then 0 onwards. Grid (blocks, B): each workgroup moves kRingUnroll runs of
+// 256 words (16 bytes, or 4 when a row or a base is not 16-byte aligned) of
+// one batch row, all loads issued before the stores, with no division.
 constexpr int kRingUnroll = 4;
 
 template <bool VEC>
-__global__ void __launch_bounds__(256) ring_write_kernel(char *ring, int M, long long row_bytes, int pos0,
+__global__ void __launch_bounds__(256) ring_write_kernel(char *ring, int M, int row_words, int pos0,
                                                          const char *src, long long src_bstride_bytes,
-                                                         int src_row0, int n, int B) {
+                                                         int src_row0, int n) {
     typedef typename std::conditional<VEC, u32x4, uint32_t>::type Word;
     constexpr int WB = (int)sizeof(Word);
-    const long long row_words = row_bytes / WB;
-    const long long total = (long long)B * n * row_words;
-    const long long base = (long long)blockIdx.x * 256 * kRingUnroll + threadIdx.x;
+    const int b = blockIdx.y;
+    const int total = n * row_words;                             // words of this batch row
+    const int split = min(n, M - pos0) * row_words;              // words before the wrap
+    const Word *s0 = reinterpret_cast<const Word *>(src + (long long)b * src_bstride_bytes) + (long long)src_row0 * row_words;
+    Word *d0 = reinterpret_cast<Word *>(ring) + (long long)b * M * row_words;
+    const int base = blockIdx.x * 256 * kRingUnroll + threadIdx.x;
     Word v[kRingUnroll];
-    char *dst[kRingUnroll];
 #pragma unroll
     for (int u = 0; u < kRingUnroll; ++u) {
-        const long long w = base + 256LL * u;
-        dst[u] = nullptr;
-        if (w < total) {
-            const long long r = w / row_words;                 // r = b * n + t
-            const long long o = (w - r * row_words) * WB;
-            const int b = (int)(r / n), t = (int)(r - (long long)b * n);
-            int pr = pos0 + t;
-            if (pr >= M) pr -= M;
-            v[u] = *reinterpret_cast<const Word *>(src + (long long)b * src_bstride_bytes +
-                                                   (long long)(src_row0 + t) * row_bytes + o);
-            dst[u] = ring + ((long long)b * M + pr) * row_bytes + o;
-        }
+        const int w = base + 256 * u;
+        if (w < total) v[u] = s0[w];
     }
 #pragma unroll
-    for (int u = 0; u < kRingUnroll; ++u)
-        if (dst[u]) *reinterpret_cast<Word *>(dst[u]) = v[u];
+    for (int u = 0; u < kRingUnroll; ++u) {
+        const int w = base + 256 * u;
+        if (w < total) d0[w < split ? (long long)pos0 * row_words + w : w - split] = v[u];
+    }
+    (void)WB;
 }
 
 // LayerNorm of the NumPy layer on "Implementing Transformer-XL":
@@ -117,16 +114,21 @@ hipError_t launch_ring_write(bool is_bf16, void *ring, int M, int D, int pos0, c
     const long long row_bytes = D * es;
     const bool vec = (row_bytes % 16 == 0) && (((uintptr_t)ring | (uintptr_t)src) % 16 == 0) &&
                      ((src_bstride * es) % 16 == 0);
-    const long long words = (long long)B * n * (row_bytes / (vec ? 16 : 4));
     const long long per_block = 256LL * kRingUnroll;
-    dim3 grid((unsigned)((words + per_block - 1) / per_block)), block(256);
+    const long long row_words_ll = row_bytes / (vec ? 16 : 4);
+    const long long words = (long long)n * row_words_ll;         // per batch row
+    // 32-bit word indices within a batch row, one grid row per batch row
+    if (words > 0x7fffffffLL - per_block || (long long)M * row_words_ll > 0x7fffffffLL || B > 65535)
+        return hipErrorInvalidValue;
+    const int row_words = (int)row_words_ll;
+    dim3 grid((unsigned)((words + per_block - 1) / per_block), (unsigned)B), block(256);
     if (grid.x == 0) return hipSuccess;
     if (vec)
-        hipLaunchKernelGGL(ring_write_kernel<true>, grid, block, 0, s, (char *)ring, M, row_bytes, pos0,
-                           (const char *)src, src_bstride * es, src_row0, n, B);
+        hipLaunchKernelGGL(ring_write_kernel<true>, grid, block, 0, s, (char *)ring, M, row_words, pos0,
+                           (const char *)src, src_bstride * es, src_row0, n);
     else
-        hipLaunchKernelGGL(ring_write_kernel<false>, grid, block, 0, s, (char *)ring, M, row_bytes, pos0,
-                           (const char *)src, src_bstride * es, src_row0, n, B);
+        hipLaunchKernelGGL(ring_write_kernel<false>, grid, block, 0, s, (char *)ring, M, row_words, pos0,
+                           (const char *)src, src_bstride * es, src_row0, n);
     return hipGetLastError();
 }
 
