@@ -69,15 +69,29 @@ constexpr int kMaxSplit = 8;      // most key parts per query block
 template <typename T, int DP, bool DIST>
 struct AttnSmem {
     static constexpr int NO = (DP + 31) / 32;                  // 32-row blocks of O^T
-    static constexpr int kPitchK = DP * (int)sizeof(T) + 16;   // bytes per key row
-    // bytes per value row (V^T): bf16 rows are read 8 bytes per lane, so an
-    // 8-byte pad (34 dwords) spreads 32 lanes over distinct bank pairs; fp32
-    // rows are read 16 bytes per lane and take a 16-byte pad
-    static constexpr int kPitchV = kKB * (int)sizeof(T) + (sizeof(T) == 2 ? 8 : 16);
+    // bf16: key and value rows of 128 bytes whose 16-byte chunks are
+    // XOR-swizzled by the row (chunk q of row r at position q ^ (r % 8)), so the
+    // 16-byte fragment reads of 8 consecutive rows hit 8 distinct bank groups.
+    // fp32: padded rows, 16 bytes past the data.
+    static constexpr bool SWZ = sizeof(T) == 2;
+    static constexpr int kPitchK = SWZ ? 128 : DP * (int)sizeof(T) + 16;   // bytes per key row
+    static constexpr int kPitchV = SWZ ? 128 : kKB * (int)sizeof(T) + 16;  // bytes per value row (V^T)
     float g[DIST ? kWaves : 1][DIST ? 32 * kGPitch : 4];
-    char k[kKB * kPitchK];
-    char v[NO * 32 * kPitchV];
+    alignas(16) char k[kKB * kPitchK];
+    alignas(16) char v[NO * 32 * kPitchV];
 };
+
+// bf16 key tiles hold their rows permuted inside each group of 16: row r
+// holds key perm_key(r) of the block. Score register i of half hf in 32-key
+// block sb (C row 32 sb + crow(i, hf)) then holds key reg_key(sb, i, hf), and
+// the eight keys of each P.V fragment (registers 8 p' .. 8 p' + 7 of one half)
+// are consecutive, so the matching V^T fragment is one 16-byte read.
+__device__ __forceinline__ int perm_key(int r) {
+    return (r & ~15) | (r & 3) | (((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 3);
+}
+__device__ __forceinline__ constexpr int reg_key_perm(int sb, int i, int hf) {
+    return 32 * sb + 16 * (i >> 3) + 8 * hf + (i & 7);
+}
 
 // Row sum of eight probabilities already packed as the bf16 B operand.
 __device__ __forceinline__ float psum(const Frag<bf16> &f, float acc) {
@@ -122,7 +136,9 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     const int b = bh / A.H, h = bh - b * A.H;
     const int i0 = qblk * kQB;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform across the wave: held in a scalar register, so
+    // the per-wave conditions below are scalar branches
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int fr = lane & 31, hf = lane >> 5;
     const int m = A.m;
     const int iw = i0 + 32 * w;                      // first query of this wave
@@ -193,6 +209,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     constexpr int KPT = (KCH + 255) / 256, VPT = (VCH + 255) / 256;
     constexpr int KCPR = DP * (int)sizeof(T) / 16;         // chunks per key row
     constexpr int VCPR = kKB * (int)sizeof(T) / 16;        // chunks per V^T row
+    constexpr bool SWZ = SM::SWZ;
     u32x4 rkt[KPT], rvt[VPT];
 #define TXL_KV_GLOAD(kb_)                                                                          \
     do {                                                                                           \
@@ -201,7 +218,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
             const int idx = tid + 256 * c;                                                         \
             if (KCH % 256 == 0 || idx < KCH) {                                                     \
                 const int r_ = idx / KCPR, q_ = idx - r_ * KCPR;                                   \
-                const int s_ = key_slot(j0_ + r_);                                                 \
+                const int s_ = key_slot(j0_ + (SWZ ? perm_key(r_) : r_));                          \
                 rkt[c] = *reinterpret_cast<const u32x4 *>((const char *)(ke + (long long)s_ * DP) + q_ * 16); \
             }                                                                                      \
         }                                                                                          \
@@ -220,16 +237,14 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
             const int idx = tid + 256 * c;                                                         \
             if (KCH % 256 == 0 || idx < KCH) {                                                     \
                 const int r_ = idx / KCPR, q_ = idx - r_ * KCPR;                                   \
-                *reinterpret_cast<u32x4 *>(sm.k + r_ * SM::kPitchK + q_ * 16) = rkt[c];             \
+                *reinterpret_cast<u32x4 *>(sm.k + r_ * SM::kPitchK + ((SWZ ? q_ ^ (r_ & 7) : q_) << 4)) = rkt[c]; \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int c = 0; c < VPT; ++c) {                                          \
             const int idx = tid + 256 * c;                                                         \
             if (VCH % 256 == 0 || idx < VCH) {                                                     \
                 const int r_ = idx / VCPR, q_ = idx - r_ * VCPR;                                   \
-                u32x2 *dv_ = reinterpret_cast<u32x2 *>(sm.v + r_ * SM::kPitchV + q_ * 16);          \
-                dv_[0] = u32x2{rvt[c][0], rvt[c][1]};                                              \
-                dv_[1] = u32x2{rvt[c][2], rvt[c][3]};                                              \
+                *reinterpret_cast<u32x4 *>(sm.v + r_ * SM::kPitchV + ((SWZ ? q_ ^ (r_ & 7) : q_) << 4)) = rvt[c]; \
             }                                                                                      \
         }                                                                                          \
     } while (0)
@@ -300,13 +315,22 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
             for (int i = 0; i < 16; ++i) sacc[0][i] = sacc[1][i] = -m_run;
         } else {
         wave_lds_sync();
-        // key b = 32*sb + crow(i) of query a needs band offset a - b + 63
+        // key b of query a needs band offset a - b + 63 (b = 32 sb + crow(i) for
+        // fp32 tiles, reg_key_perm(sb, i, hf) for the permuted bf16 ones)
         {
-            const float *rb = grow + fr - 4 * hf;
+            if constexpr (SWZ) {
+                const float *rb = grow + fr - 8 * hf + 63;
 #pragma unroll
-            for (int sb = 0; sb < 2; ++sb)
+                for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[sb][i] = rb[63 - 32 * sb - 8 * (i >> 2) - (i & 3)] - m_run;
+                    for (int i = 0; i < 16; ++i) sacc[sb][i] = rb[-(32 * sb + 16 * (i >> 3) + (i & 7))] - m_run;
+            } else {
+                const float *rb = grow + fr - 4 * hf;
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sacc[sb][i] = rb[63 - 32 * sb - 8 * (i >> 2) - (i & 3)] - m_run;
+            }
         }
         }
         // ---- content term on top: S^T += K (q+u)^T
@@ -315,7 +339,11 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 Frag<T> f;
-                load8(f, reinterpret_cast<const T *>(sm.k + (32 * sb + fr) * SM::kPitchK + (16 * s + 8 * hf) * (int)sizeof(T)));
+                if constexpr (SWZ)
+                    f.v = *reinterpret_cast<const bf16x8 *>(__builtin_assume_aligned(
+                        sm.k + (32 * sb + fr) * SM::kPitchK + (((2 * s + hf) ^ (fr & 7)) << 4), 16));
+                else
+                    load8(f, reinterpret_cast<const T *>(sm.k + (32 * sb + fr) * SM::kPitchK + (16 * s + 8 * hf) * (int)sizeof(T)));
                 mma16(sacc[sb], f, fqu[s]);
             }
         // ---- causal mask on blocks that reach past the wave's first query
@@ -325,7 +353,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
             for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (32 * sb + crow(i, lane) > lim) sacc[sb][i] = -INFINITY;
+                    if ((SWZ ? reg_key_perm(sb, i, hf) : 32 * sb + crow(i, lane)) > lim) sacc[sb][i] = -INFINITY;
         }
         // ---- online softmax (log2 domain; the scores are held relative to m_run)
         float mx = sacc[0][0];
@@ -389,7 +417,11 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 #pragma unroll
             for (int o = 0; o < NO; ++o) {
                 Frag<T> fv;
-                load_vt(fv, sm.v + (32 * o + fr) * SM::kPitchV, 16 * p + 4 * hf);
+                if constexpr (SWZ)      // keys 16 p + 8 hf .. + 7: one swizzled chunk
+                    fv.v = *reinterpret_cast<const bf16x8 *>(__builtin_assume_aligned(
+                        sm.v + (32 * o + fr) * SM::kPitchV + (((2 * p + hf) ^ (fr & 7)) << 4), 16));
+                else
+                    load_vt(fv, sm.v + (32 * o + fr) * SM::kPitchV, 16 * p + 4 * hf);
                 mma16(oacc[o], fv, fp4[p]);
             }
         }
