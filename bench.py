@@ -8,9 +8,13 @@ projection and the memory-ring update, all through the C ABI
 (txl_rel_attn_fwd + txl_mem_update). Inputs are seeded synthetic tensors
 already resident in HBM when the timed region starts.
 
-Prints ONE JSON line with the whole-job throughput (tokens/s), the attention
-kernel's roofline position (its own launches timed with HIP events inside the
-timed region) and the CPU oracle timed on a bounded sample of the same work.
+Prints ONE JSON line with the whole-job throughput (tokens/s) of a timed region
+that holds the steps alone, the attention kernel's roofline position (its own
+launches timed with HIP event pairs in a second timed region of the same steps,
+whose throughput is reported beside the first) and the CPU oracle timed on a
+bounded sample of the same work. The 16-layer stacks (bf16 and fp32) and the
+one-layer fp32 layer workload are timed over their segment schedules against
+the MFMA peak of their own dtype.
 A second timed region runs the same segments with the memory kept as projected
 keys and values (txl_rel_attn_fwd_cached), reported under "kv_cache". Then
 "sliding_window" compares segment-recurrent evaluation with vanilla evaluation,
@@ -33,7 +37,9 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 WORKLOAD = "attn_w512_bf16"
+STACK_WORKLOADS = ("stack16_bf16", "stack16_fp32", "layer_ffn_fp32")
 BF16_PEAK_TFLOPS = 2516.6        # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+FP32_PEAK_TFLOPS = 157.3         # published dense fp32 MFMA peak (256 flop/clk/CU)
 HBM_PEAK_GBS = 8000.0
 
 
@@ -181,20 +187,23 @@ def stack_flops(wl, m):
     return attn_flops(B, H, D // H, W, m) + proj_flops(B, W, m, D) + 4.0 * B * W * D * F
 
 
-def time_stack16(tb, torch, syn, dev, reps):
-    """The 16-layer bf16 stack's whole 8-segment schedule from empty memories
-    (txl_stack_fwd_segments), with its algorithmic TFLOP/s."""
-    bf = torch.bfloat16
-    wl = syn.WORKLOADS["stack16_bf16"]
+def time_stack16(tb, torch, syn, dev, reps, name="stack16_bf16"):
+    """A stack workload's whole segment schedule from empty memories
+    (txl_stack_fwd_segments) with its algorithmic TFLOP/s against the MFMA peak
+    of its own dtype (the 16-layer stacks in bf16 and fp32; the one-layer
+    layer_ffn_fp32 workload runs through the same call with L = 1)."""
+    wl = syn.WORKLOADS[name]
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    peak = BF16_PEAK_TFLOPS if wl.dtype == "bf16" else FP32_PEAK_TFLOPS
     B, D, H, W, M, F = wl.B, wl.D, wl.H, wl.W, wl.M, wl.F
     prob = syn.draw_problem(wl)
-    x = torch.from_numpy(prob.x).to(dev).to(bf)
-    lp = [tb.LayerParams.from_numpy(p, bf, dev) for p in prob.params]
-    R = tb.sinusoid_table(M + W, D, bf, dev)
+    x = torch.from_numpy(prob.x).to(dev).to(tdt)
+    lp = [tb.LayerParams.from_numpy(p, tdt, dev) for p in prob.params]
+    R = tb.sinusoid_table(M + W, D, tdt, dev)
     y = torch.empty_like(x)
-    ws = torch.empty(tb.workspace_bytes(tb.OP_STACK, bf, B, W, M, D, H, F), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_STACK, tdt, B, W, M, D, H, F), dtype=torch.uint8, device=dev)
 
-    mems = [tb.MemoryRing.empty(B, M, D, bf, dev) for _ in lp]
+    mems = [tb.MemoryRing.empty(B, M, D, tdt, dev) for _ in lp]
 
     def run(k):
         for r in mems:
@@ -204,9 +213,10 @@ def time_stack16(tb, torch, syn, dev, reps):
     el = _timed(torch, run, reps, 1)
     flops = sum(stack_flops(wl, m) for m in wl.mem_schedule()) * len(lp)
     T = x.shape[1]
-    return {"workload": wl.name, "layers": len(lp), "segments": wl.S, "ms_per_schedule": el * 1e3 / reps,
-            "tokens_per_s": B * T * reps / el, "algorithmic_tflops": flops * reps / el / 1e12,
-            "frac_of_bf16_peak": flops * reps / el / 1e12 / BF16_PEAK_TFLOPS,
+    tf = flops * reps / el / 1e12
+    return {"workload": wl.name, "dtype": wl.dtype, "layers": len(lp), "segments": wl.S,
+            "ms_per_schedule": el * 1e3 / reps, "tokens_per_s": B * T * reps / el,
+            "algorithmic_tflops": tf, "peak_tflops": peak, "frac_of_peak": tf / peak,
             "memory_lengths": wl.mem_schedule()}
 
 
@@ -452,6 +462,8 @@ def main():
                     help="skip the comparison with vanilla sliding-window evaluation")
     ap.add_argument("--stack16-only", action="store_true",
                     help="time only the 16-layer bf16 stack's schedule (for counter runs of its kernels)")
+    ap.add_argument("--stack-only", choices=STACK_WORKLOADS, default=None,
+                    help="time only this stack workload's schedule (for traces and counter runs)")
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the attention backward at the headline shape (for kernel traces)")
     ap.add_argument("--headline-only", action="store_true",
@@ -482,8 +494,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.stack16_only:
-        print(json.dumps({"stack16": time_stack16(tb, torch, syn, dev, 2)}), flush=True)
+    if args.stack16_only or args.stack_only:
+        name = args.stack_only or "stack16_bf16"
+        print(json.dumps({name: time_stack16(tb, torch, syn, dev, 2, name)}), flush=True)
         return
     wl = syn.WORKLOADS[WORKLOAD]
     B, D, H, W, M = wl.B, wl.D, wl.H, wl.W, wl.M
@@ -514,16 +527,29 @@ def main():
     assert ring.len == M
     m = ring.len
 
+    # the steps with a HIP event pair around every attention launch (stamped by
+    # the kernel's own dispatch, on the stream it runs on), for the kernel's
+    # launch durations
     tb.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    elapsed_stamped = time.perf_counter() - t1
+    attn_ms, launches = tb.profile_end()
+    assert launches == args.steps
+    launch_ms = sorted(tb.profile_times(launches))
+
+    # the timed region proper: the same steps again with nothing recorded
+    # between them; its throughput is the reported value
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         step(k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    attn_ms, launches = tb.profile_end()
-    assert launches == args.steps
-    launch_ms = sorted(tb.profile_times(launches))
+    assert ring.len == m
 
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = B * W * args.steps
@@ -559,6 +585,8 @@ def main():
                      "device": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
                      "peak_from_compute_units": props.multi_processor_count * 2.4e9 * 4096 / 1e12},
         "attn_tokens_per_s": B * W / a_avg_s,
+        "event_stamped_region": {"ms_per_step": elapsed_stamped * 1e3 / args.steps,
+                                 "tokens_per_s": tokens / elapsed_stamped},
         "step_tflops": (a_flops + proj_flops(B, W, m, D)) / (ms_per_step * 1e-3) / 1e12,
     }
     if args.headline_only:
@@ -569,6 +597,8 @@ def main():
     rec["longmem_warm"] = longmem_warm(tb, torch, syn, dev, max(10, args.steps // 4))
     rec["mem_update"] = time_mem_update(tb, torch, segs, B, M, D, dev, max(20, args.steps // 2))
     rec["stack16"] = time_stack16(tb, torch, syn, dev, 2)
+    rec["stack16_fp32"] = time_stack16(tb, torch, syn, dev, 2, "stack16_fp32")
+    rec["layer_ffn_fp32"] = time_stack16(tb, torch, syn, dev, 20, "layer_ffn_fp32")
     kv = time_cached(tb, torch, segs, params, R, B, M, W, D, H, out, args.steps, args.warmup)
     kv["speedup_vs_row_memory"] = kv["value"] / rec["value"]
     rec["kv_cache"] = kv

@@ -144,8 +144,8 @@ typedef struct {
  * serves every call of that op with sizes no larger than these. */
 size_t txl_workspace_bytes(txl_op op, txl_dtype dtype, int B, int W, int M, int D, int H, int F);
 
-/* Relative-encoding table R [R_len][D] (explainer, step 4: a sinusoidal encoding
- * of the distance with no trained parameters). Row d holds
+/* Relative-encoding table R [R_len][D] (explainer, step 4). R is a fixed
+ * function of the distance, not a learned table. Row d holds
  *   R[d][k] = sin(d * 10000^(-2k/D)),  R[d][D/2 + k] = cos(d * 10000^(-2k/D)),
  * for k < D/2, evaluated in double precision and rounded to `dtype`.
  * D must be even. */
@@ -261,9 +261,9 @@ txl_status txl_attn_fwd_variant(txl_dtype dtype, txl_pos_variant variant, int B,
 
 /* Backward pass of the relative attention with the memory behind a
  * stop-gradient ("Transformer-XL, explained.", method step 2 and the SG(.)
- * legend entry: the cached states are a fixed input, backpropagation stays in
- * the current segment). Inputs are the projected operands of one segment, in
- * the call's dtype, rows contiguous:
+ * legend entry). The memory rows receive no gradient; their projected keys
+ * and values do, as part of this segment's graph. Inputs are the projected
+ * operands of one segment, in the call's dtype, rows contiguous:
  *   q, dO  [B][W][D]   queries h W_q^T; gradient of the loss w.r.t. the attention
  *                      output o (heads concatenated, before W_o)
  *   k, val [B][K][D]   content keys and values of [mem; h], K = m + W, memory first

@@ -67,10 +67,10 @@ int orc_set_num_threads(int n)
 #endif
 }
 
-/* Relative-encoding table ([XL] step 4 and the legend entry for R_{i-j}:
- * a sinusoidal encoding of the distance with no trained parameters). The
- * pages do not print the formula; the [sin | cos] half-split with base 10000
- * is the reading taken. D must be even. */
+/* Relative-encoding table ([XL] step 4 and the legend entry for R_{i-j}).
+ * R depends on the distance alone and is not learned; the pages do not print
+ * its formula, so the [sin | cos] half-split with base 10000 is the reading
+ * taken. D must be even. */
 int orc_sinusoid_table(int R_len, int D, double *R)
 {
     if (R_len < 0 || D < 2 || (D % 2) != 0 || !R) return ORC_ERR_ARG;
@@ -330,8 +330,9 @@ int orc_attn_variant(int mode, int B, int W, int D, int H, int m,
 
 /*
  * Gradients of relative attention with the memory behind a stop-gradient
- * ([XL] step 2 and the SG(.) legend entry: the cached states are a fixed input
- * and backpropagation stays inside the current segment). Inputs are the
+ * ([XL] step 2 and the SG(.) legend entry). No gradient reaches the memory
+ * rows themselves; gradients flow only through this segment's computation,
+ * which includes the projections of the memory rows. Inputs are the
  * projected operands of one segment:
  *   q    [B][W][D]   queries h W_q^T
  *   k    [B][K][D]   content keys of [mem; h] (K = m + W, memory rows first)

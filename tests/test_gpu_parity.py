@@ -215,6 +215,19 @@ def test_workload_attn_w512_bf16_library_table():
     assert max(errs.values()) <= TOL[wl.dtype], errs
 
 
+def test_large_launch_ragged_bf16():
+    # enough rows for the projections' 256-row GEMM tiles, with ragged tails in
+    # every dimension: 4000 query rows (4000 % 256 = 160), d_model 520 (eight
+    # 64-deep k-tiles and one of 8), heads of 52 padded to 64 (640 columns, five
+    # 128-column tiles), and a memory that wraps around the ring in segment 2
+    wl = _wl("ragged_large", "bf16", B=20, D=520, H=10, W=200, M=300, S=3, seed=77)
+    say(f"ragged large launch {wl.B}x{wl.W} D={wl.D} H={wl.H} M={wl.M}")
+    prob = syn.draw_problem(wl)
+    errs = run_attn_segments(prob, table(wl.M + wl.W, wl.D, wl.dtype), batch=[0, 7, 19])
+    say(f"  errors {errs}")
+    assert max(errs.values()) <= TOL[wl.dtype], errs
+
+
 @pytest.mark.parametrize("warm", [False, True])
 def test_workload_longmem_m1600_bf16(warm):
     wl = syn.WORKLOADS["longmem_m1600_bf16"]

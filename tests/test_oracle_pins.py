@@ -47,7 +47,7 @@ def test_sinusoid_closed_forms():
     # the last frequency is 10000^(-(D-2)/D)
     w = 10000.0 ** (-(D - 2) / D)
     np.testing.assert_allclose(R[:, half - 1], np.sin(d * w), atol=1e-15)
-    # no trained parameters: any longer table extends a shorter one unchanged
+    # R is a function of the distance only: a longer table extends a shorter one unchanged
     np.testing.assert_array_equal(_R(L + 17, D)[:L], R)
 
 
@@ -391,8 +391,8 @@ def test_reach_grows_one_segment_per_layer():
 
 @pytest.mark.parametrize("W,M,k", [(3, 5, 1), (4, 4, 2), (4, 2, 3), (3, 7, 2)])
 def test_resume_from_carried_memories_equals_straight_run(W, M, k):
-    # "Transformer-XL, explained.", method step 2: the cached states are the only
-    # thing a segment takes from the past, read as a fixed input. So k segments,
+    # "Transformer-XL, explained.", method step 2: a segment sees the past only
+    # through the cached memories, which enter as constants. So k segments,
     # then the remaining S - k segments started from the memories the first call
     # left behind, give the straight S-segment run bit for bit (same arithmetic in
     # the same order), outputs and final memories alike.
