@@ -4,9 +4,11 @@
 One step = one steady segment of the hot path on the attn_w512_bf16 workload
 (batch 16, d_model 512, 8 heads of 64, segment W = 512, memory M = 512 full):
 the fused Q/K/V/R projections, the relative-attention kernel, the output
-projection and the memory-ring update, all through the C ABI
-(txl_rel_attn_fwd + txl_mem_update). Inputs are seeded synthetic tensors
-already resident in HBM when the timed region starts.
+projection and the memory-ring update, all through the C ABI in one call
+(txl_rel_attn_fwd_update: the ring copy rides along the output projection's
+launch); the same steps as two calls (txl_rel_attn_fwd + txl_mem_update) are
+timed beside it. Inputs are seeded synthetic tensors already resident in HBM
+when the timed region starts.
 
 Prints ONE JSON line with the whole-job throughput (tokens/s) of a timed region
 that holds the steps alone, the attention kernel's roofline position (its own
@@ -103,15 +105,15 @@ def time_fwd_only(tb, torch, segs, ring, params, R, H, out, ws, steps):
 
 def time_schedule(tb, torch, segs, params, R, B, M, D, H, out, ws, reps):
     """The workload's whole schedule: its S segments from an empty memory, each
-    txl_rel_attn_fwd + txl_mem_update, so the early segments see m < M."""
+    txl_rel_attn_fwd_update (attention and memory update), so the early
+    segments see m < M."""
     ring = tb.MemoryRing.empty(B, M, D, out.dtype, out.device)
     W = out.shape[1]
 
     def sched(k):
         ring.len, ring.head = 0, 0           # an empty memory: the stale rows are never read
         for h in segs:
-            tb.rel_attn_fwd(h, ring, params, R, H, out=out, workspace=ws)
-            tb.mem_update(ring, h)
+            tb.rel_attn_fwd_update(h, ring, params, R, H, out=out, workspace=ws)
 
     el = _timed(torch, sched, reps, 1)
     S = len(segs)
@@ -516,6 +518,9 @@ def main():
 
 
     def step(k):
+        tb.rel_attn_fwd_update(segs[k % len(segs)], ring, params, R, H, out=out, workspace=ws)
+
+    def step_separate(k):
         h = segs[k % len(segs)]
         tb.rel_attn_fwd(h, ring, params, R, H, out=out, workspace=ws)
         tb.mem_update(ring, h)
@@ -551,6 +556,10 @@ def main():
     elapsed = time.perf_counter() - t0
     assert ring.len == m
 
+    # the same steps as two calls, txl_rel_attn_fwd then txl_mem_update (the
+    # memory update in a launch of its own)
+    el_sep = _timed(torch, step_separate, args.steps, 1)
+
     ms_per_step = elapsed * 1e3 / args.steps
     tokens = B * W * args.steps
     a_flops = attn_flops(B, H, dh, W, m)
@@ -572,7 +581,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "B": B, "W": W, "M": M, "m": m, "D": D, "H": H, "d_head": dh,
-                   "step": "txl_rel_attn_fwd + txl_mem_update, one steady segment"},
+                   "step": "txl_rel_attn_fwd_update (attention + memory update), one steady segment"},
         "roofline": {"kernel": "rel_attn_kernel", "bound": "mfma", "achieved": a_tflops,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": a_tflops / BF16_PEAK_TFLOPS,
                      "traffic": traffic, "avg_launch_us": a_avg_s * 1e6,
@@ -587,6 +596,8 @@ def main():
         "attn_tokens_per_s": B * W / a_avg_s,
         "event_stamped_region": {"ms_per_step": elapsed_stamped * 1e3 / args.steps,
                                  "tokens_per_s": tokens / elapsed_stamped},
+        "separate_update_calls": {"ms_per_step": el_sep * 1e3 / args.steps, "tokens_per_s": tokens / el_sep,
+                                  "step": "txl_rel_attn_fwd + txl_mem_update"},
         "step_tflops": (a_flops + proj_flops(B, W, m, D)) / (ms_per_step * 1e-3) / 1e12,
     }
     if args.headline_only:

@@ -69,7 +69,7 @@ typedef enum {
 typedef enum { TXL_FP32 = 0, TXL_BF16 = 1 } txl_dtype;
 
 typedef enum {
-    TXL_OP_REL_ATTN = 0,      /* txl_rel_attn_fwd */
+    TXL_OP_REL_ATTN = 0,      /* txl_rel_attn_fwd, txl_rel_attn_fwd_update */
     TXL_OP_LAYER = 1,         /* txl_layer_fwd */
     TXL_OP_STACK = 2,         /* txl_stack_fwd_segments */
     TXL_OP_REL_ATTN_CACHED = 3, /* txl_rel_attn_fwd_cached */
@@ -189,6 +189,22 @@ txl_status txl_rel_attn_fwd_noalloc(txl_dtype dtype, int B, int W, int D, int H,
                                     const txl_mem *mem, const txl_layer_params *p,
                                     const void *R, int R_len,
                                     void *out, long long out_bstride, void *stream);
+
+/* txl_rel_attn_fwd followed by the memory update of the same segment
+ * (txl_mem_update with the same h and W), in one call: out and the ring hold
+ * exactly what those two calls would leave, and mem->len / mem->head advance
+ * on the host as txl_mem_update advances them. The copy into the ring runs
+ * inside the output projection's launch, after every launch that reads the
+ * old rows, so the step needs no launch of its own for it. mem must not be
+ * NULL (an empty ring has len == 0); out must not overlap h or the ring. On
+ * any error nothing is launched and mem is unchanged. Same workspace as
+ * txl_rel_attn_fwd. */
+txl_status txl_rel_attn_fwd_update(txl_dtype dtype, int B, int W, int D, int H,
+                                   const void *h, long long h_bstride,
+                                   txl_mem *mem, const txl_layer_params *p,
+                                   const void *R, int R_len,
+                                   void *out, long long out_bstride,
+                                   void *ws, size_t ws_bytes, void *stream);
 
 /* Memory update (simulator: mem = last M rows of h~ = [mem; h]). Appends the
  * last min(W, M) rows of h [B][W][D] (batch stride h_bstride) to the ring,

@@ -113,6 +113,29 @@ def test_noalloc_rejects_bad_arguments_and_oversized_calls():
     assert b"scratch" in L.txl_last_error()
 
 
+def test_fused_update_rejects_bad_arguments_and_leaves_memory():
+    # txl_rel_attn_fwd_update: the checks of txl_rel_attn_fwd plus a non-NULL
+    # memory; on any error the ring's len / head stay as they were
+    L = tb.lib()
+    p = _params()
+
+    def call(mem, B=1, W=4, D=16, H=2, hs=64, R=FAKE, R_len=8, out=FAKE, os_=64, dt=tb.TXL_BF16, ws=None,
+             wsb=0):
+        return L.txl_rel_attn_fwd_update(dt, B, W, D, H, FAKE, hs, ctypes.byref(mem) if mem else None,
+                                         ctypes.byref(p), R, R_len, out, os_, ws, wsb, None)
+    assert call(None) == tb.TXL_ERR_ARG
+    assert b"NULL" in L.txl_last_error()
+    m = tb._Mem(FAKE, 4, 4, 1)
+    assert call(m, D=18, H=4) == tb.TXL_ERR_ARG
+    assert call(m, R_len=7) == tb.TXL_ERR_ARG                # needs 4 + 4 rows
+    assert call(m, out=FAKE + 2) == tb.TXL_ERR_ARG
+    assert call(m) == tb.TXL_ERR_WORKSPACE                    # valid, no workspace
+    assert (m.len, m.head) == (4, 1)
+    bad = tb._Mem(FAKE, 4, 5, 0)
+    assert call(bad) == tb.TXL_ERR_ARG
+    assert (bad.len, bad.head) == (5, 0)
+
+
 def test_mem_update_rejects_bad_arguments():
     L = tb.lib()
     m = tb._Mem(FAKE, 4, 0, 0)

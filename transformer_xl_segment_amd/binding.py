@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.txl_sinusoid_table.argtypes = [i, i, i, vp, vp]
         L.txl_rel_attn_fwd.argtypes = [i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_rel_attn_fwd_noalloc.argtypes = [i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp]
+        L.txl_rel_attn_fwd_update.argtypes = [i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_mem_update.argtypes = [i, i, i, Mp, vp, ll, i, vp]
         L.txl_layer_fwd.argtypes = [i, i, i, i, i, i, vp, ll, Mp, P, vp, i, vp, ll, vp, sz, vp]
         L.txl_stack_fwd_segments.argtypes = [i, i, i, i, i, i, i, i, vp, Mp, P, vp, i, vp, vp, sz, vp]
@@ -82,7 +83,8 @@ def lib() -> ctypes.CDLL:
         L.txl_profile_begin.argtypes = [i]
         L.txl_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
         L.txl_profile_times.argtypes = [ctypes.POINTER(ctypes.c_double), i, ctypes.POINTER(ctypes.c_int)]
-        for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_rel_attn_fwd_noalloc", "txl_mem_update", "txl_layer_fwd",
+        for f in ("txl_sinusoid_table", "txl_rel_attn_fwd", "txl_rel_attn_fwd_noalloc", "txl_rel_attn_fwd_update",
+                  "txl_mem_update", "txl_layer_fwd",
                   "txl_stack_fwd_segments", "txl_stack_fwd_window", "txl_kv_cache_capacity",
                   "txl_attn_fwd_variant", "txl_add_positions", "txl_rel_attn_bwd", "txl_kv_cache_append",
                   "txl_rel_attn_fwd_cached", "txl_profile_begin", "txl_profile_end", "txl_profile_times"):
@@ -242,6 +244,27 @@ def rel_attn_fwd(h: torch.Tensor, mem: Optional[MemoryRing], params: LayerParams
                                   R.data_ptr(), R.shape[0], out.data_ptr(), os_, ws.data_ptr(),
                                   ws.numel() * ws.element_size(), _stream(h.device)),
            "txl_rel_attn_fwd")
+    return out
+
+
+def rel_attn_fwd_update(h: torch.Tensor, mem: MemoryRing, params: LayerParams, R: torch.Tensor,
+                        H: int, out: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """rel_attn_fwd then mem_update(mem, h) in one call (txl_rel_attn_fwd_update)."""
+    B, W, D = h.shape
+    hs = _rows_view(h, "h")
+    if out is None:
+        out = torch.empty(B, W, D, dtype=h.dtype, device=h.device)
+    os_ = _rows_view(out, "out")
+    nbytes = workspace_bytes(OP_REL_ATTN, h.dtype, B, W, mem.M, D, H)
+    ws = _workspace(nbytes, h.device, workspace)
+    ms = mem._struct()
+    ps = params._struct()
+    _check(lib().txl_rel_attn_fwd_update(dtype_code(h.dtype), B, W, D, H, h.data_ptr(), hs, ctypes.byref(ms),
+                                         ctypes.byref(ps), R.data_ptr(), R.shape[0], out.data_ptr(), os_,
+                                         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(h.device)),
+           "txl_rel_attn_fwd_update")
+    mem._update_from(ms)
     return out
 
 

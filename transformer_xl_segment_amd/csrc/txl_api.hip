@@ -354,16 +354,57 @@ GemmProblem rows_problem(int B, int W, int kdim, int cols, const void *a, long l
     return p;
 }
 
+// mem = last M rows of [mem; h]: plans the ring copy into rc (blocks workgroups)
+// and advances the ring's host-side state; the copy runs in whichever launch
+// carries rc, which must come after every launch that reads the old rows.
+txl_status plan_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const void *h, long long h_bstride, int W,
+                           RingCopy &rc, int &blocks) {
+    const int n = W < mem->M ? W : mem->M;
+    const int pos0 = (int)(((long long)mem->head + mem->len) % mem->M);
+    blocks = plan_ring_copy(dt == TXL_BF16, rc, mem->data, mem->M, D, pos0, h, h_bstride, W - n, n, B);
+    if (blocks < 0) return fail(TXL_ERR_UNSUPPORTED, "memory update of %d rows of %d elements exceeds 32-bit indexing",
+                                n, D);
+    if (mem->len + n <= mem->M) {
+        mem->len += n;
+    } else {
+        mem->head = (int)(((long long)mem->head + mem->len + n - mem->M) % mem->M);
+        mem->len = mem->M;
+    }
+    return TXL_OK;
+}
+
+txl_status enqueue_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const void *h, long long h_bstride, int W,
+                              hipStream_t s) {
+    RingCopy rc;
+    int blocks = 0;
+    txl_mem next = *mem;
+    TXL_TRY(plan_mem_update(dt, B, D, &next, h, h_bstride, W, rc, blocks));
+    TXL_TRY(hip_check(launch_ring_copy(rc, blocks, s), "memory update launch"));
+    *mem = next;
+    return TXL_OK;
+}
+
+// One layer; with `update` (the layer's own memory, the ring `mem` reads) the
+// memory update mem = last M rows of [mem; h] rides along the output
+// projection's launch, which comes after every read of the old rows.
 txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const void *h, long long h_bstride,
                          const txl_mem *mem, const txl_layer_params *p, const void *R, void *y,
-                         long long y_bstride, char *ws, const Layout &L, hipStream_t s) {
+                         long long y_bstride, char *ws, const Layout &L, hipStream_t s,
+                         txl_mem *update = nullptr) {
     const bool bf = dt == TXL_BF16;
     TXL_TRY(enqueue_attention(dt, B, W, D, H, h, h_bstride, mem, nullptr, p, R, ws, L, s));
     const long long WD = (long long)W * D;
     // z = h + O Wo^T (fp32)
     GemmProblem wo = rows_problem(B, W, D, D, ws + L.o, D, WD, p->Wo, ws + L.z, D, WD);
     wo.res = h; wo.res_ld = D; wo.res_bstride = h_bstride; wo.out_f32 = 1;
-    TXL_TRY(hip_check(launch_gemm(bf, single(wo), s), "output projection launch"));
+    GemmLaunch gwo = single(wo);
+    txl_mem next;
+    if (update) {
+        next = *update;
+        TXL_TRY(plan_mem_update(dt, B, D, &next, h, h_bstride, W, gwo.rc, gwo.copy_blocks));
+    }
+    TXL_TRY(hip_check(launch_gemm(bf, gwo, s), "output projection launch"));
+    if (update) *update = next;
     TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), p->ln1_g, p->ln1_b, ws + L.h1, WD, B, W, D, s),
                       "LayerNorm launch"));
     // f = ReLU(h1 W1^T + b1)
@@ -379,20 +420,6 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
     return TXL_OK;
 }
 
-txl_status enqueue_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const void *h, long long h_bstride, int W,
-                              hipStream_t s) {
-    const int n = W < mem->M ? W : mem->M;
-    const int pos0 = (int)(((long long)mem->head + mem->len) % mem->M);
-    TXL_TRY(hip_check(launch_ring_write(dt == TXL_BF16, mem->data, mem->M, D, pos0, h, h_bstride, W - n, n, B, s),
-                      "memory update launch"));
-    if (mem->len + n <= mem->M) {
-        mem->len += n;
-    } else {
-        mem->head = (int)(((long long)mem->head + mem->len + n - mem->M) % mem->M);
-        mem->len = mem->M;
-    }
-    return TXL_OK;
-}
 
 // Workspace of the backward pass (one region per operand, 256-byte aligned).
 struct BwdLayout {
@@ -490,6 +517,26 @@ txl_status txl_rel_attn_fwd(txl_dtype dtype, int B, int W, int D, int H, const v
     TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, mem, nullptr, p, R, w, L, s));
     GemmProblem wo = rows_problem(B, W, D, D, w + L.o, D, (long long)W * D, p->Wo, out, D, out_bstride);
     return hip_check(launch_gemm(dtype == TXL_BF16, single(wo), s), "output projection launch");
+}
+
+txl_status txl_rel_attn_fwd_update(txl_dtype dtype, int B, int W, int D, int H, const void *h, long long h_bstride,
+                                   txl_mem *mem, const txl_layer_params *p, const void *R, int R_len, void *out,
+                                   long long out_bstride, void *ws, size_t ws_bytes, void *stream) {
+    if (!mem) return fail(TXL_ERR_ARG, "memory is NULL (txl_rel_attn_fwd_update updates it)");
+    TXL_TRY(check_rel_attn(dtype, B, W, D, H, h, h_bstride, mem, p, R, R_len, out, out_bstride));
+    const Layout L = plan(TXL_OP_REL_ATTN, dtype, B, W, mem->len + W, D, H, 0);
+    if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
+    if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    char *w = (char *)ws;
+    txl_mem next = *mem;
+    GemmLaunch gwo = single(rows_problem(B, W, D, D, w + L.o, D, (long long)W * D, p->Wo, out, D, out_bstride));
+    // the copy is planned before any launch so that a refused update launches nothing
+    TXL_TRY(plan_mem_update(dtype, B, D, &next, h, h_bstride, W, gwo.rc, gwo.copy_blocks));
+    TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, mem, nullptr, p, R, w, L, s));
+    TXL_TRY(hip_check(launch_gemm(dtype == TXL_BF16, gwo, s), "output projection launch"));
+    *mem = next;
+    return TXL_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -608,8 +655,8 @@ txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, i
             const bool last = l == n_layers - 1;
             char *hout = last ? (char *)y + (size_t)t * W * D * es : w + ((l & 1) ? L.hb1 : L.hb0);
             const long long hout_bs = last ? seq * D : (long long)W * D;
-            TXL_TRY(enqueue_block(dtype, B, W, D, H, F, hin, hin_bs, &mems[l], &params[l], R, hout, hout_bs, w, L, s));
-            TXL_TRY(enqueue_mem_update(dtype, B, D, &mems[l], hin, hin_bs, W, s));
+            TXL_TRY(enqueue_block(dtype, B, W, D, H, F, hin, hin_bs, &mems[l], &params[l], R, hout, hout_bs, w, L, s,
+                                  &mems[l]));
             hin = hout;
             hin_bs = hout_bs;
         }

@@ -306,6 +306,10 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
     constexpr int kChA = BM * (kRowBytes / 16) / kThreads;          // 16-byte chunks per thread, A
     constexpr int kChB = kBN * (kRowBytes / 16) / kThreads;         // ... B
     __shared__ GemmSmem<BM> sm;
+    if ((int)blockIdx.x >= g.total_tiles) {                         // a memory-update workgroup
+        ring_copy_block(g.rc, blockIdx.x - g.total_tiles);
+        return;
+    }
     // XCD-aware remap: deal consecutive tiles to the same XCD.
     const int total = g.total_tiles;
     const int gid = blockIdx.x;
@@ -471,6 +475,10 @@ __global__ void __launch_bounds__(kThreads, BN == 64 ? 4 : 3) gemm_lds_kernel(co
     constexpr int EPC = 16 / (int)sizeof(T);             // elements per chunk
     static_assert(ROWS % 64 == 0, "whole load instructions per wave");
     __shared__ GemmLdsSmem<BM, BN> sm;
+    if ((int)blockIdx.x >= g.total_tiles) {                         // a memory-update workgroup
+        ring_copy_block(g.rc, blockIdx.x - g.total_tiles);
+        return;
+    }
 
     const int total = g.total_tiles;
     const int gid = blockIdx.x;
@@ -617,7 +625,7 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p) {
 
 template <int BM>
 void launch_bm(bool is_bf16, bool vec, const GemmLaunch &g, hipStream_t s) {
-    dim3 grid(g.total_tiles), block(kThreads);
+    dim3 grid(g.total_tiles + g.copy_blocks), block(kThreads);
     if (is_bf16) {
         if (vec) hipLaunchKernelGGL((gemm_lds_kernel<bf16, BM, kBN>), grid, block, 0, s, g);
         else hipLaunchKernelGGL((gemm_kernel<bf16, false, BM>), grid, block, 0, s, g);
@@ -632,7 +640,11 @@ void launch_bm(bool is_bf16, bool vec, const GemmLaunch &g, hipStream_t s) {
 constexpr int kSmallGrid = 512;
 
 hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s) {
-    if (g.total_tiles <= 0) return hipSuccess;
+    if (g.total_tiles <= 0 && g.copy_blocks <= 0) return hipSuccess;
+    if (g.total_tiles <= 0) {                     // a memory update alone
+        hipLaunchKernelGGL((gemm_kernel<bf16, false, 64>), dim3(g.copy_blocks), dim3(kThreads), 0, s, g);
+        return hipGetLastError();
+    }
     bool vec = true, narrow = true;
     for (int i = 0; i < g.count; ++i) {
         vec = vec && gemm_vec_ok(is_bf16, g.p[i]);
@@ -651,7 +663,7 @@ hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s) {
             t += P.tile_count;
         }
         gn.total_tiles = t;
-        dim3 grid(gn.total_tiles), block(kThreads);
+        dim3 grid(gn.total_tiles + gn.copy_blocks), block(kThreads);
         if (is_bf16) hipLaunchKernelGGL((gemm_lds_kernel<bf16, 128, 64>), grid, block, 0, s, gn);
         else hipLaunchKernelGGL((gemm_lds_kernel<float, 128, 64>), grid, block, 0, s, gn);
         return hipGetLastError();

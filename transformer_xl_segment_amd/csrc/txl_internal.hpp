@@ -76,11 +76,63 @@ struct GemmProblem {
                                  // band), so a tile may start its reduction there
 };
 
+// Memory update riding along a GEMM launch (segment-recurrence simulator: mem =
+// last M rows of [mem; h]): the workgroups after the launch's tiles copy, for
+// every batch row b, the n source rows src_row0 .. src_row0+n-1 of b into ring
+// slots pos0, pos0+1, ... (mod M). One batch row's copy is two contiguous runs
+// (before and after the wrap), moved in words of 16 bytes (vec) or 4 bytes;
+// word indices within a batch row fit 32 bits. blocks_x workgroups per batch
+// row, each kRingCopyUnroll x 256 words.
+struct RingCopy {
+    char *ring;
+    const char *src;
+    long long src_bstride_bytes;
+    int M, row_words, pos0, src_row0, n, blocks_x, vec;
+};
+constexpr int kRingCopyUnroll = 4;
+
 struct GemmLaunch {
     GemmProblem p[3];
     int count;
     int total_tiles;
+    RingCopy rc;
+    int copy_blocks;             // workgroups after the tiles that run rc (0: none)
 };
+
+// Workgroup `blk` (0 <= blk < blocks_x * B) of a ring copy, 256 threads.
+__device__ __forceinline__ void ring_copy_block(const RingCopy &rc, int blk) {
+    const int b = blk / rc.blocks_x, bx = blk - b * rc.blocks_x;
+    const int total = rc.n * rc.row_words;                       // words of this batch row
+    const int split = min(rc.n, rc.M - rc.pos0) * rc.row_words;  // words before the wrap
+    const int base = bx * 256 * kRingCopyUnroll + (int)threadIdx.x;
+    const char *s0 = rc.src + (long long)b * rc.src_bstride_bytes;
+    char *d0 = rc.ring + (long long)b * rc.M * rc.row_words * (rc.vec ? 16 : 4);
+    auto run = [&](auto word) {
+        typedef decltype(word) Word;
+        const Word *s = reinterpret_cast<const Word *>(s0) + (long long)rc.src_row0 * rc.row_words;
+        Word *d = reinterpret_cast<Word *>(d0);
+        Word v[kRingCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kRingCopyUnroll; ++u) {
+            const int w = base + 256 * u;
+            if (w < total) v[u] = s[w];
+        }
+#pragma unroll
+        for (int u = 0; u < kRingCopyUnroll; ++u) {
+            const int w = base + 256 * u;
+            if (w < total) d[w < split ? (long long)rc.pos0 * rc.row_words + w : w - split] = v[u];
+        }
+    };
+    typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+    if (rc.vec) run(u32x4_());
+    else run(uint32_t());
+}
+
+// Plans the copy "ring rows (pos0 + t) % M of every batch entry <- src rows
+// src_row0 + t, t < n" into rc; returns the number of workgroups (B * blocks_x,
+// 0 for nothing to copy) or -1 if the sizes exceed the 32-bit word indexing.
+int plan_ring_copy(bool is_bf16, RingCopy &rc, void *ring, int M, int D, int pos0, const void *src,
+                   long long src_bstride, int src_row0, int n, int B);
 
 // Returns a hipError_t from the launch.
 hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s);
@@ -212,9 +264,8 @@ hipError_t launch_bwd_finish(const BwdDims &d, const float *drh, const float *pa
 // ---------------------------------------------------------------------------
 // Small kernels.
 // ---------------------------------------------------------------------------
-// dst ring rows (pos0 + t) % M of every batch entry <- src rows (src_row0 + t), t < n
-hipError_t launch_ring_write(bool is_bf16, void *ring, int M, int D, int pos0, const void *src,
-                             long long src_bstride, int src_row0, int n, int B, hipStream_t s);
+// A planned ring copy (plan_ring_copy) as its own launch of `blocks` workgroups.
+hipError_t launch_ring_copy(const RingCopy &rc, int blocks, hipStream_t s);
 // y[b][t] = LN(x[b][t]) with fp32 input, T output (batch stride y_bstride)
 hipError_t launch_layer_norm(bool is_bf16, const float *x, const void *g, const void *b, void *y,
                              long long y_bstride, int B, int W, int D, hipStream_t s);

@@ -14,39 +14,9 @@ namespace txl {
 
 namespace {
 
-// Memory update (segment-recurrence simulator: mem = last M rows of [mem; h]).
-// For one batch row the n source rows are contiguous, and so are their ring
-// slots up to the wrap: the copy is two contiguous runs, slots pos0 .. M-1 and
-// then 0 onwards. Grid (blocks, B): each workgroup moves kRingUnroll runs of
-// 256 words (16 bytes, or 4 when a row or a base is not 16-byte aligned) of
-// one batch row, all loads issued before the stores, with no division.
-constexpr int kRingUnroll = 4;
-
-template <bool VEC>
-__global__ void __launch_bounds__(256) ring_write_kernel(char *ring, int M, int row_words, int pos0,
-                                                         const char *src, long long src_bstride_bytes,
-                                                         int src_row0, int n) {
-    typedef typename std::conditional<VEC, u32x4, uint32_t>::type Word;
-    constexpr int WB = (int)sizeof(Word);
-    const int b = blockIdx.y;
-    const int total = n * row_words;                             // words of this batch row
-    const int split = min(n, M - pos0) * row_words;              // words before the wrap
-    const Word *s0 = reinterpret_cast<const Word *>(src + (long long)b * src_bstride_bytes) + (long long)src_row0 * row_words;
-    Word *d0 = reinterpret_cast<Word *>(ring) + (long long)b * M * row_words;
-    const int base = blockIdx.x * 256 * kRingUnroll + threadIdx.x;
-    Word v[kRingUnroll];
-#pragma unroll
-    for (int u = 0; u < kRingUnroll; ++u) {
-        const int w = base + 256 * u;
-        if (w < total) v[u] = s0[w];
-    }
-#pragma unroll
-    for (int u = 0; u < kRingUnroll; ++u) {
-        const int w = base + 256 * u;
-        if (w < total) d0[w < split ? (long long)pos0 * row_words + w : w - split] = v[u];
-    }
-    (void)WB;
-}
+// Memory update (segment-recurrence simulator: mem = last M rows of [mem; h]),
+// as its own launch: one workgroup per ring_copy_block (txl_internal.hpp).
+__global__ void __launch_bounds__(256) ring_write_kernel(const RingCopy rc) { ring_copy_block(rc, blockIdx.x); }
 
 // LayerNorm of the NumPy layer on "Implementing Transformer-XL":
 // gamma * (x - mean) / (std + 1e-6) + beta with the population std. One wave
@@ -107,28 +77,35 @@ __global__ void sinusoid_kernel(T *R, int R_len, int D) {
 
 }  // namespace
 
-hipError_t launch_ring_write(bool is_bf16, void *ring, int M, int D, int pos0, const void *src,
-                             long long src_bstride, int src_row0, int n, int B, hipStream_t s) {
-    if (n <= 0 || B <= 0) return hipSuccess;
+int plan_ring_copy(bool is_bf16, RingCopy &rc, void *ring, int M, int D, int pos0, const void *src,
+                   long long src_bstride, int src_row0, int n, int B) {
+    if (n <= 0 || B <= 0) return 0;
     const long long es = is_bf16 ? 2 : 4;
     const long long row_bytes = D * es;
     const bool vec = (row_bytes % 16 == 0) && (((uintptr_t)ring | (uintptr_t)src) % 16 == 0) &&
                      ((src_bstride * es) % 16 == 0);
-    const long long per_block = 256LL * kRingUnroll;
-    const long long row_words_ll = row_bytes / (vec ? 16 : 4);
-    const long long words = (long long)n * row_words_ll;         // per batch row
-    // 32-bit word indices within a batch row, one grid row per batch row
-    if (words > 0x7fffffffLL - per_block || (long long)M * row_words_ll > 0x7fffffffLL || B > 65535)
-        return hipErrorInvalidValue;
-    const int row_words = (int)row_words_ll;
-    dim3 grid((unsigned)((words + per_block - 1) / per_block), (unsigned)B), block(256);
-    if (grid.x == 0) return hipSuccess;
-    if (vec)
-        hipLaunchKernelGGL(ring_write_kernel<true>, grid, block, 0, s, (char *)ring, M, row_words, pos0,
-                           (const char *)src, src_bstride * es, src_row0, n);
-    else
-        hipLaunchKernelGGL(ring_write_kernel<false>, grid, block, 0, s, (char *)ring, M, row_words, pos0,
-                           (const char *)src, src_bstride * es, src_row0, n);
+    const long long per_block = 256LL * kRingCopyUnroll;
+    const long long row_words = row_bytes / (vec ? 16 : 4);
+    const long long words = (long long)n * row_words;            // per batch row
+    if (words > 0x7fffffffLL - per_block || (long long)M * row_words > 0x7fffffffLL) return -1;
+    const long long bx = (words + per_block - 1) / per_block;
+    if (bx * B > 0x7fffffffLL) return -1;
+    rc.ring = (char *)ring;
+    rc.src = (const char *)src;
+    rc.src_bstride_bytes = src_bstride * es;
+    rc.M = M;
+    rc.row_words = (int)row_words;
+    rc.pos0 = pos0;
+    rc.src_row0 = src_row0;
+    rc.n = n;
+    rc.blocks_x = (int)bx;
+    rc.vec = vec;
+    return (int)(bx * B);
+}
+
+hipError_t launch_ring_copy(const RingCopy &rc, int blocks, hipStream_t s) {
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(ring_write_kernel, dim3(blocks), dim3(256), 0, s, rc);
     return hipGetLastError();
 }
 
