@@ -162,6 +162,21 @@ def test_layer_small(dtype, affine):
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D,F", [(82, 1100), (96, 2048)])
+def test_stack_split_ffn(dtype, D, F):
+    # hidden widths of 1024 and more over few row tiles: in fp32 the second FFN
+    # product splits its reduction in two at a 64-element boundary (1100 -> 576
+    # + 524, 2048 -> 1024 + 1024) and LayerNorm adds the halves (bf16 keeps one
+    # reduction); dword-aligned rows (D = 82) and 16-byte aligned ones (D = 96)
+    say(f"stack with a split FFN reduction {dtype} D={D} F={F}")
+    wl = _wl("stack_split", dtype, 2, D, 2, 24, 30, 3, F=F, layers=2, op="stack", seed=13)
+    prob = syn.draw_problem(wl, affine=True, weight_scale=0.2 if dtype == "fp32" else 0.1)
+    errs = _run_block_segments(prob, table(54, D, dtype))
+    say(f"  errors {errs}")
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_stack_small(dtype):
     say(f"stack small {dtype}")
     wl = _wl("stack_small", dtype, 2, 82, 2, 30, 30, 4, F=130, layers=3, op="stack", seed=12)

@@ -53,7 +53,8 @@ struct Layout {
     size_t lse;                        // encoding variants: per-query log-sum-exp
     size_t part_o, part_ml;            // key-split parts of the attention output
     int nsplit;                        // most key splits any launch of this layout uses
-    size_t z, h1, f;                   // block: fp32 pre-LN sums, LN1 output, FFN hidden
+    size_t z, z2, h1, f;               // block: fp32 pre-LN sums (z2: second half of a split FFN2), LN1 output,
+                                       // FFN hidden
     size_t hb0, hb1;                   // stack: inter-layer activations
     size_t total;
     int Wp, Kp, dp;
@@ -91,6 +92,7 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
     }
     if (op == TXL_OP_LAYER || op == TXL_OP_STACK) {
         L.z = take((size_t)B * W * D * 4);
+        L.z2 = take((size_t)B * W * D * 4);
         L.h1 = take((size_t)B * W * D * es);
         L.f = take((size_t)B * W * F * es);
     }
@@ -340,6 +342,22 @@ GemmLaunch single(const GemmProblem &p) {
     return g;
 }
 
+GemmLaunch grouped(std::initializer_list<GemmProblem> ps) {
+    GemmLaunch g;
+    memset(&g, 0, sizeof(g));
+    int t = 0;
+    for (const GemmProblem &p0 : ps) {
+        GemmProblem &P = g.p[g.count++];
+        P = p0;
+        P.tiles_n = (P.cols + 127) / 128;
+        P.tile_begin = t;
+        P.tile_count = ((P.rows + 127) / 128) * P.tiles_n;
+        t += P.tile_count;
+    }
+    g.total_tiles = t;
+    return g;
+}
+
 // Dense rows GEMM: C(b, t) = A(b, t) W^T (+bias, relu, +res), A/C [B][W][*].
 GemmProblem rows_problem(int B, int W, int kdim, int cols, const void *a, long long a_ld, long long a_bstride,
                          const void *w, void *c, long long c_ld, long long c_bstride) {
@@ -405,17 +423,40 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
     }
     TXL_TRY(hip_check(launch_gemm(bf, gwo, s), "output projection launch"));
     if (update) *update = next;
-    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), p->ln1_g, p->ln1_b, ws + L.h1, WD, B, W, D, s),
+    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), nullptr, p->ln1_g, p->ln1_b, ws + L.h1, WD, B,
+                                        W, D, s),
                       "LayerNorm launch"));
     // f = ReLU(h1 W1^T + b1)
     GemmProblem f1 = rows_problem(B, W, D, F, ws + L.h1, D, WD, p->W1, ws + L.f, F, (long long)W * F);
     f1.bias = p->b1; f1.relu = 1;
     TXL_TRY(hip_check(launch_gemm(bf, single(f1), s), "FFN1 launch"));
-    // z = h1 + f W2^T + b2 (fp32)
+    // z = h1 + f W2^T + b2 (fp32). In fp32 a long reduction over too few tiles
+    // to give every CU two (64-row tiles) is split in two at a k-tile boundary:
+    // the first half carries the bias and the residual into z, the second half
+    // writes its partial sums to z2, and LayerNorm adds the two (the 16-layer
+    // fp32 stack: 75.2 -> 72.5 ms per schedule; in bf16 the split measured
+    // slower, 21.3 -> 21.7 ms, and is not taken).
     GemmProblem f2 = rows_problem(B, W, F, D, ws + L.f, F, (long long)W * F, p->W2, ws + L.z, D, WD);
     f2.bias = p->b2; f2.res = ws + L.h1; f2.res_ld = D; f2.res_bstride = WD; f2.out_f32 = 1;
-    TXL_TRY(hip_check(launch_gemm(bf, single(f2), s), "FFN2 launch"));
-    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), p->ln2_g, p->ln2_b, y, y_bstride, B, W, D, s),
+    const long long tiles64 = ((long long)B * W + 63) / 64 * ((D + 127) / 128);
+    const float *z2 = nullptr;
+    if (dt == TXL_FP32 && F >= 1024 && tiles64 < 512) {
+        const int ks = (int)round_up((F + 1) / 2, 64);
+        GemmProblem f2b = f2;
+        f2.kdim = ks;
+        f2b.kdim = F - ks;
+        f2b.a = (const char *)f2.a + (size_t)ks * es_of(dt);
+        f2b.b0 = (const char *)f2.b0 + (size_t)ks * es_of(dt);
+        f2b.bias = nullptr;
+        f2b.res = nullptr;
+        f2b.c0 = ws + L.z2;
+        z2 = (const float *)(ws + L.z2);
+        TXL_TRY(hip_check(launch_gemm(bf, grouped({f2, f2b}), s), "FFN2 launch"));
+    } else {
+        TXL_TRY(hip_check(launch_gemm(bf, single(f2), s), "FFN2 launch"));
+    }
+    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), z2, p->ln2_g, p->ln2_b, y, y_bstride, B, W,
+                                        D, s),
                       "LayerNorm launch"));
     return TXL_OK;
 }
@@ -763,21 +804,6 @@ GemmProblem batched_problem(int entries, int rows, int cols, int kdim, const voi
     return p;
 }
 
-GemmLaunch grouped(std::initializer_list<GemmProblem> ps) {
-    GemmLaunch g;
-    memset(&g, 0, sizeof(g));
-    int t = 0;
-    for (const GemmProblem &p0 : ps) {
-        GemmProblem &P = g.p[g.count++];
-        P = p0;
-        P.tiles_n = (P.cols + 127) / 128;
-        P.tile_begin = t;
-        P.tile_count = ((P.rows + 127) / 128) * P.tiles_n;
-        t += P.tile_count;
-    }
-    g.total_tiles = t;
-    return g;
-}
 
 }  // namespace
 

@@ -266,8 +266,8 @@ hipError_t launch_bwd_finish(const BwdDims &d, const float *drh, const float *pa
 // ---------------------------------------------------------------------------
 // A planned ring copy (plan_ring_copy) as its own launch of `blocks` workgroups.
 hipError_t launch_ring_copy(const RingCopy &rc, int blocks, hipStream_t s);
-// y[b][t] = LN(x[b][t]) with fp32 input, T output (batch stride y_bstride)
-hipError_t launch_layer_norm(bool is_bf16, const float *x, const void *g, const void *b, void *y,
+// y[b][t] = LN(x[b][t] (+ x2[b][t])) with fp32 input(s), T output (batch stride y_bstride); x2 may be null
+hipError_t launch_layer_norm(bool is_bf16, const float *x, const float *x2, const void *g, const void *b, void *y,
                              long long y_bstride, int B, int W, int D, hipStream_t s);
 hipError_t launch_sinusoid(bool is_bf16, void *R, int R_len, int D, hipStream_t s);
 

@@ -20,14 +20,16 @@ __global__ void __launch_bounds__(256) ring_write_kernel(const RingCopy rc) { ri
 
 // LayerNorm of the NumPy layer on "Implementing Transformer-XL":
 // gamma * (x - mean) / (std + 1e-6) + beta with the population std. One wave
-// per row; statistics in fp32 from an fp32 input row.
+// per row; statistics in fp32 from an fp32 input row, which is x, or x + x2
+// when the producing GEMM split its reduction in two.
 template <typename T>
-__global__ void layer_norm_kernel(const float *x, const T *g, const T *bt, T *y, long long y_bstride,
-                                  int rows, int W, int D) {
+__global__ void layer_norm_kernel(const float *x, const float *x2, const T *g, const T *bt, T *y,
+                                  long long y_bstride, int rows, int W, int D) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const float *xr = x + (long long)row * D;
+    const float *x2r = x2 ? x2 + (long long)row * D : nullptr;
     constexpr int MAXE = 16;                 // D <= 1024
     float v[MAXE];
     float s = 0.f;
@@ -35,6 +37,7 @@ __global__ void layer_norm_kernel(const float *x, const T *g, const T *bt, T *y,
     for (int e = 0; e < MAXE; ++e) {
         const int c = lane + 64 * e;
         v[e] = c < D ? xr[c] : 0.f;
+        if (x2r && c < D) v[e] += x2r[c];    // the second half of a split reduction
         s += v[e];
     }
 #pragma unroll
@@ -109,15 +112,15 @@ hipError_t launch_ring_copy(const RingCopy &rc, int blocks, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_layer_norm(bool is_bf16, const float *x, const void *g, const void *b, void *y,
+hipError_t launch_layer_norm(bool is_bf16, const float *x, const float *x2, const void *g, const void *b, void *y,
                              long long y_bstride, int B, int W, int D, hipStream_t s) {
     const int rows = B * W;
     dim3 grid((rows + 3) / 4), block(256);
     if (is_bf16)
-        hipLaunchKernelGGL(layer_norm_kernel<bf16>, grid, block, 0, s, x, (const bf16 *)g, (const bf16 *)b,
+        hipLaunchKernelGGL(layer_norm_kernel<bf16>, grid, block, 0, s, x, x2, (const bf16 *)g, (const bf16 *)b,
                            (bf16 *)y, y_bstride, rows, W, D);
     else
-        hipLaunchKernelGGL(layer_norm_kernel<float>, grid, block, 0, s, x, (const float *)g,
+        hipLaunchKernelGGL(layer_norm_kernel<float>, grid, block, 0, s, x, x2, (const float *)g,
                            (const float *)b, (float *)y, y_bstride, rows, W, D);
     return hipGetLastError();
 }
