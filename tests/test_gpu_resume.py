@@ -133,19 +133,22 @@ def _attn_once(prob, R, B_run, misaligned=False):
 
 def test_launch_shapes_agree():
     # headline shape: 16 rows (128-row GEMM tiles, one attention part per query
-    # block) against 1 row (64-row tiles, the key range split over 4 parts and
-    # merged) and against 16 rows with a 4-byte-aligned batch stride
+    # block) against 8 rows (128-row tiles, the key range split over 2 parts),
+    # 1 row (64-row tiles, 4 parts merged) and 16 rows with a 4-byte-aligned
+    # batch stride (the register-staged GEMM)
     wl = syn.WORKLOADS["attn_w512_bf16"]
     wl = syn.Workload(**{**wl.__dict__, "S": 2})
     prob = syn.draw_problem(wl)
     say("launch shapes: headline attention, rows 0 and 15")
     R = table(wl.M + wl.W, wl.D, wl.dtype)
     a16 = _attn_once(prob, R, 16)
+    a8 = _attn_once(prob, R, 8)
     a1 = _attn_once(prob, R, 1)
     am = _attn_once(prob, R, 16, misaligned=True)
     ref = orc.rel_attn(prob.x[[0, 15], wl.M:wl.M + wl.W].astype(np.float64),
                        prob.x[[0, 15], :wl.M].astype(np.float64), prob.params[0], R, wl.H)
     errs = {"16_vs_oracle": rel_err(a16[[0, 15]], ref), "1_vs_oracle": rel_err(a1[[0]], ref[[0]]),
+            "8_vs_oracle": rel_err(a8[[0]], ref[[0]]), "8_vs_16": rel_err(a8, a16[:8]),
             "misaligned_vs_oracle": rel_err(am[[0, 15]], ref),
             "1_vs_16": rel_err(a1[0], a16[0]), "misaligned_vs_16": rel_err(am, a16)}
     say(f"  errors {errs}; aligned and 4-byte-aligned rows bit-identical: {np.array_equal(am, a16)}")
