@@ -56,6 +56,13 @@ struct Layout {
     size_t z, z2, h1, f;               // block: fp32 pre-LN sums (z2: second half of a split FFN2), LN1 output,
                                        // FFN hidden
     size_t hb0, hb1;                   // stack: inter-layer activations
+    // block with rows that are not 16-byte aligned: activations at the padded
+    // pitches Dp and Fp (pad columns zero), the input rows copied to that pitch
+    // (hx) and W_o, W1 repacked to it (wo, w1), so that the block's own GEMMs
+    // take the direct-to-LDS kernel
+    bool pad;
+    int Dp, Fp;
+    size_t hx, wo, w1;
     size_t total;
     int Wp, Kp, dp;
 };
@@ -74,6 +81,14 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
         off = (size_t)round_up((long long)(off + bytes), 256);
         return at;
     };
+    L.Dp = D;
+    L.Fp = F;
+    if (op == TXL_OP_LAYER || op == TXL_OP_STACK) {
+        const int epr = 16 / (int)es;                 // elements per 16 bytes
+        L.Dp = (int)round_up(D, epr);
+        L.Fp = (int)round_up(F, epr);
+        L.pad = L.Dp != D || L.Fp != F;
+    }
     const size_t q_bytes = (size_t)B * H * L.Wp * L.dp * es;
     const size_t k_bytes = (size_t)B * H * L.Kp * L.dp * es;
     L.qu = take(q_bytes);
@@ -83,7 +98,7 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
         L.vt = take(k_bytes);
     }
     L.rk = take((size_t)H * rk_table_rows(L.Kp) * L.dp * es);
-    L.o = take((size_t)B * W * D * es);
+    L.o = take((size_t)B * W * L.Dp * es);
     if (op == TXL_OP_ATTN_VARIANT) L.lse = take((size_t)B * H * L.Wp * 4);
     L.nsplit = attn_splits(B, H, W, Kmax);
     if (L.nsplit > 1) {
@@ -91,14 +106,19 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
         L.part_ml = take((size_t)L.nsplit * B * H * L.Wp * 2 * 4);
     }
     if (op == TXL_OP_LAYER || op == TXL_OP_STACK) {
-        L.z = take((size_t)B * W * D * 4);
-        L.z2 = take((size_t)B * W * D * 4);
-        L.h1 = take((size_t)B * W * D * es);
-        L.f = take((size_t)B * W * F * es);
+        L.z = take((size_t)B * W * L.Dp * 4);
+        L.z2 = take((size_t)B * W * L.Dp * 4);
+        L.h1 = take((size_t)B * W * L.Dp * es);
+        L.f = take((size_t)B * W * L.Fp * es);
+        if (L.pad) {
+            L.hx = take((size_t)B * W * L.Dp * es);
+            L.wo = take((size_t)D * L.Dp * es);
+            L.w1 = take((size_t)F * L.Dp * es);
+        }
     }
     if (op == TXL_OP_STACK) {
-        L.hb0 = take((size_t)B * W * D * es);
-        L.hb1 = take((size_t)B * W * D * es);
+        L.hb0 = take((size_t)B * W * L.Dp * es);
+        L.hb1 = take((size_t)B * W * L.Dp * es);
     }
     L.total = off;
     return L;
@@ -244,10 +264,15 @@ struct Variant {
     int clip;
 };
 
+// h rows are h_ld elements apart (0: D), the attention output o is written at
+// row pitch o_ld (0: D); `extra` copies ride along the projection launch.
 txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const void *h, long long h_bstride,
                              const txl_mem *mem, const txl_kv_cache *cache, const txl_layer_params *p,
                              const void *R, char *ws, const Layout &L, hipStream_t s,
-                             const Variant *var = nullptr) {
+                             const Variant *var = nullptr, long long h_ld = 0, long long o_ld = 0,
+                             const PitchCopy *extra = nullptr, int n_extra = 0) {
+    if (h_ld <= 0) h_ld = D;
+    if (o_ld <= 0) o_ld = D;
     const bool bf = dt == TXL_BF16;
     const int dh = D / H, dp = L.dp;
     const int m = cache ? cache->len : mem ? mem->len : 0;
@@ -260,7 +285,7 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     GemmProblem &q = g.p[0];
     q.rows = B * L.Wp; q.cols = H * dp; q.kdim = D;
     q.seg_rows = L.Wp; q.valid_rows = W;
-    q.a_mode = A_ROWS; q.a = h; q.a_ld = D; q.a_bstride = h_bstride;
+    q.a_mode = A_ROWS; q.a = h; q.a_ld = h_ld; q.a_bstride = h_bstride;
     q.b_mode = B_HEADS; q.b0 = p->Wq; q.b_split = q.cols; q.b_ld = D;
     q.dh = dh; q.dhp = dp; q.heads = H;
     q.epi = EPI_QUV; q.c0 = ws + L.qu; q.c1 = ws + L.qv;
@@ -273,8 +298,8 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     } else {
     kv.rows = B * Kp; kv.cols = 2 * H * dp; kv.kdim = D;
     kv.seg_rows = Kp; kv.valid_rows = W;
-    kv.a_mode = A_CONTEXT; kv.a = h; kv.a_ld = D; kv.a_bstride = h_bstride;
-    kv.ring = m > 0 ? mem->data : h; kv.ring_bstride = m > 0 ? (long long)mem->M * D : 0;
+    kv.a_mode = A_CONTEXT; kv.a = h; kv.a_ld = h_ld; kv.a_bstride = h_bstride;
+    kv.ring = m > 0 ? mem->data : h; kv.ring_bstride = m > 0 ? (long long)mem->M * D : 0; kv.ring_ld = D;
     kv.ring_M = m > 0 ? mem->M : 1; kv.ring_head = m > 0 ? mem->head : 0; kv.mem_len = m;
     kv.b_mode = B_HEADS; kv.b0 = p->WkE; kv.b1 = p->Wv; kv.b_split = H * dp; kv.b_ld = D;
     kv.dh = dh; kv.dhp = dp; kv.heads = H;
@@ -300,6 +325,8 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
         t += P.tile_count;
     }
     g.total_tiles = t;
+    for (int i = 0; i < n_extra; ++i) g.pc[i] = extra[i];
+    g.pc_count = n_extra;
     TXL_TRY(hip_check(launch_gemm(bf, g, s), "projection GEMM launch"));
     if (var && var->kind == TXL_POS_SHAW)
         TXL_TRY(hip_check(launch_shaw_rows(bf, ws + L.rk, var->aK, var->clip, K, Kp, dh, dp, rk_frag_off(m), s),
@@ -313,7 +340,7 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     a.lse = var && var->kind == TXL_POS_SHAW ? (float *)(ws + L.lse) : nullptr;
     a.ke = cache ? cache->k : (const void *)(ws + L.ke);
     a.vt = cache ? cache->vt : (const void *)(ws + L.vt);
-    a.o = ws + L.o; a.o_bstride = (long long)W * D;
+    a.o = ws + L.o; a.o_bstride = (long long)W * o_ld; a.o_ld = o_ld;
     a.B = B; a.H = H; a.W = W; a.Wp = L.Wp; a.m = m; a.K = K; a.Kp = Kp; a.dh = dh; a.dp = dp; a.D = D;
     a.C = cache ? cache->C : Kp;
     a.khead = cache ? cache->head : 0;
@@ -375,11 +402,11 @@ GemmProblem rows_problem(int B, int W, int kdim, int cols, const void *a, long l
 // mem = last M rows of [mem; h]: plans the ring copy into rc (blocks workgroups)
 // and advances the ring's host-side state; the copy runs in whichever launch
 // carries rc, which must come after every launch that reads the old rows.
-txl_status plan_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const void *h, long long h_bstride, int W,
-                           RingCopy &rc, int &blocks) {
+txl_status plan_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const void *h, long long h_bstride,
+                           long long h_ld, int W, RingCopy &rc, int &blocks) {
     const int n = W < mem->M ? W : mem->M;
     const int pos0 = (int)(((long long)mem->head + mem->len) % mem->M);
-    blocks = plan_ring_copy(dt == TXL_BF16, rc, mem->data, mem->M, D, pos0, h, h_bstride, W - n, n, B);
+    blocks = plan_ring_copy(dt == TXL_BF16, rc, mem->data, mem->M, D, pos0, h, h_bstride, h_ld, W - n, n, B);
     if (blocks < 0) return fail(TXL_ERR_UNSUPPORTED, "memory update of %d rows of %d elements exceeds 32-bit indexing",
                                 n, D);
     if (mem->len + n <= mem->M) {
@@ -396,38 +423,101 @@ txl_status enqueue_mem_update(txl_dtype dt, int B, int D, txl_mem *mem, const vo
     RingCopy rc;
     int blocks = 0;
     txl_mem next = *mem;
-    TXL_TRY(plan_mem_update(dt, B, D, &next, h, h_bstride, W, rc, blocks));
+    TXL_TRY(plan_mem_update(dt, B, D, &next, h, h_bstride, D, W, rc, blocks));
     TXL_TRY(hip_check(launch_ring_copy(rc, blocks, s), "memory update launch"));
     *mem = next;
     return TXL_OK;
 }
 
-// One layer; with `update` (the layer's own memory, the ring `mem` reads) the
-// memory update mem = last M rows of [mem; h] rides along the output
-// projection's launch, which comes after every read of the old rows.
+// A pitched copy of `rows` rows (seg_rows per batch entry) of `cols` elements:
+// src rows src_ld apart (batch stride src_bs), dst rows dst_ld apart (batch
+// stride dst_bs), dst columns cols .. dst_ld-1 zeroed; src null zeroes only the
+// pad columns. Element counts are even for bf16, so rows are whole words.
+PitchCopy pitch_job(size_t es, const void *src, long long src_ld, long long src_bs, void *dst, long long dst_ld,
+                    long long dst_bs, int rows, int seg_rows, int cols) {
+    PitchCopy pc;
+    memset(&pc, 0, sizeof(pc));
+    auto words = [&](long long elems) { return elems * (long long)es / 4; };
+    pc.src = (const uint32_t *)src;
+    pc.dst = (uint32_t *)dst;
+    pc.src_pitch = words(src_ld);
+    pc.dst_pitch = words(dst_ld);
+    pc.src_bstride = words(src_bs);
+    pc.dst_bstride = words(dst_bs);
+    pc.seg_rows = seg_rows;
+    pc.rows = rows;
+    pc.w0 = src ? 0 : (int)words(cols);
+    pc.w1 = (int)words(dst_ld);
+    pc.copy_w = src ? (int)words(cols) : 0;
+    // wide rows: a workgroup per row (at most 1024); narrow ones: about 16 words per thread
+    const long long work = (long long)rows * (pc.w1 - pc.w0);
+    pc.blocks = pc.w1 - pc.w0 >= 64 ? std::max(1, std::min(rows, 1024))
+                                    : (int)std::max(1LL, std::min(1024LL, (work + 4095) / 4096));
+    return pc;
+}
+
+// One layer. h rows are h_ld elements apart and y rows are written y_ld apart.
+// With `update` (the layer's own memory, the ring `mem` reads) the memory update
+// mem = last M rows of [mem; h] rides along the output projection's launch,
+// which comes after every read of the old rows. With a padded layout (L.pad)
+// the block's activations live at the 16-byte aligned pitches Dp and Fp, h is
+// first copied to that pitch unless it is there already, and W_o and W1 are
+// repacked to it by workgroups riding along the projection launch, which also
+// zero the pad columns of o and h1: the output projection and the first FFN
+// product then reduce over Dp (the pad columns contribute zeros) with every
+// operand 16-byte aligned.
 txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const void *h, long long h_bstride,
-                         const txl_mem *mem, const txl_layer_params *p, const void *R, void *y,
-                         long long y_bstride, char *ws, const Layout &L, hipStream_t s,
+                         long long h_ld, const txl_mem *mem, const txl_layer_params *p, const void *R, void *y,
+                         long long y_bstride, long long y_ld, char *ws, const Layout &L, hipStream_t s,
                          txl_mem *update = nullptr) {
     const bool bf = dt == TXL_BF16;
-    TXL_TRY(enqueue_attention(dt, B, W, D, H, h, h_bstride, mem, nullptr, p, R, ws, L, s));
-    const long long WD = (long long)W * D;
+    const size_t es = es_of(dt);
+    const int Dp = L.Dp, Fp = L.Fp;
+    const long long WDp = (long long)W * Dp, WFp = (long long)W * Fp;
+    const void *Wo = p->Wo, *W1 = p->W1;
+    PitchCopy extra[kMaxPitchCopies];
+    int n_extra = 0;
+    if (L.pad) {
+        if (h_ld != Dp) {
+            // the input rows at the padded pitch, in a launch of their own (the
+            // projection reads them)
+            const PitchCopy px = pitch_job(es, h, h_ld, h_bstride, ws + L.hx, Dp, WDp, B * W, W, D);
+            TXL_TRY(hip_check(launch_pitch_copies(&px, 1, s), "input pitch copy launch"));
+            h = ws + L.hx;
+            h_ld = Dp;
+            h_bstride = WDp;
+        }
+        // W_o and W1 reduce over d_model: repacked when its rows are not aligned.
+        // W2 reduces over F and is used as it is (aligned rows when F is; a
+        // repacked W2 measured no faster than the dword-aligned kernel)
+        if (Dp != D) {
+            extra[n_extra++] = pitch_job(es, p->Wo, D, 0, ws + L.wo, Dp, 0, D, D, D);
+            extra[n_extra++] = pitch_job(es, p->W1, D, 0, ws + L.w1, Dp, 0, F, F, D);
+            Wo = ws + L.wo;
+            W1 = ws + L.w1;
+        }
+        // pad columns of the GEMM inputs the block writes (nothing else writes them)
+        extra[n_extra++] = pitch_job(es, nullptr, 0, 0, ws + L.o, Dp, WDp, B * W, W, D);
+        extra[n_extra++] = pitch_job(es, nullptr, 0, 0, ws + L.h1, Dp, WDp, B * W, W, D);
+    }
+    TXL_TRY(enqueue_attention(dt, B, W, D, H, h, h_bstride, mem, nullptr, p, R, ws, L, s, nullptr, h_ld, Dp, extra,
+                              n_extra));
     // z = h + O Wo^T (fp32)
-    GemmProblem wo = rows_problem(B, W, D, D, ws + L.o, D, WD, p->Wo, ws + L.z, D, WD);
-    wo.res = h; wo.res_ld = D; wo.res_bstride = h_bstride; wo.out_f32 = 1;
+    GemmProblem wo = rows_problem(B, W, Dp, D, ws + L.o, Dp, WDp, Wo, ws + L.z, Dp, WDp);
+    wo.res = h; wo.res_ld = h_ld; wo.res_bstride = h_bstride; wo.out_f32 = 1;
     GemmLaunch gwo = single(wo);
     txl_mem next;
     if (update) {
         next = *update;
-        TXL_TRY(plan_mem_update(dt, B, D, &next, h, h_bstride, W, gwo.rc, gwo.copy_blocks));
+        TXL_TRY(plan_mem_update(dt, B, D, &next, h, h_bstride, h_ld, W, gwo.rc, gwo.copy_blocks));
     }
     TXL_TRY(hip_check(launch_gemm(bf, gwo, s), "output projection launch"));
     if (update) *update = next;
-    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), nullptr, p->ln1_g, p->ln1_b, ws + L.h1, WD, B,
-                                        W, D, s),
+    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), nullptr, Dp, p->ln1_g, p->ln1_b, ws + L.h1, WDp,
+                                        Dp, B, W, D, s),
                       "LayerNorm launch"));
     // f = ReLU(h1 W1^T + b1)
-    GemmProblem f1 = rows_problem(B, W, D, F, ws + L.h1, D, WD, p->W1, ws + L.f, F, (long long)W * F);
+    GemmProblem f1 = rows_problem(B, W, Dp, F, ws + L.h1, Dp, WDp, W1, ws + L.f, Fp, WFp);
     f1.bias = p->b1; f1.relu = 1;
     TXL_TRY(hip_check(launch_gemm(bf, single(f1), s), "FFN1 launch"));
     // z = h1 + f W2^T + b2 (fp32). In fp32 a long reduction over too few tiles
@@ -436,8 +526,8 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
     // writes its partial sums to z2, and LayerNorm adds the two (the 16-layer
     // fp32 stack: 75.2 -> 72.5 ms per schedule; in bf16 the split measured
     // slower, 21.3 -> 21.7 ms, and is not taken).
-    GemmProblem f2 = rows_problem(B, W, F, D, ws + L.f, F, (long long)W * F, p->W2, ws + L.z, D, WD);
-    f2.bias = p->b2; f2.res = ws + L.h1; f2.res_ld = D; f2.res_bstride = WD; f2.out_f32 = 1;
+    GemmProblem f2 = rows_problem(B, W, F, D, ws + L.f, Fp, WFp, p->W2, ws + L.z, Dp, WDp);
+    f2.bias = p->b2; f2.res = ws + L.h1; f2.res_ld = Dp; f2.res_bstride = WDp; f2.out_f32 = 1;
     const long long tiles64 = ((long long)B * W + 63) / 64 * ((D + 127) / 128);
     const float *z2 = nullptr;
     if (dt == TXL_FP32 && F >= 1024 && tiles64 < 512) {
@@ -445,8 +535,8 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
         GemmProblem f2b = f2;
         f2.kdim = ks;
         f2b.kdim = F - ks;
-        f2b.a = (const char *)f2.a + (size_t)ks * es_of(dt);
-        f2b.b0 = (const char *)f2.b0 + (size_t)ks * es_of(dt);
+        f2b.a = (const char *)f2.a + (size_t)ks * es;
+        f2b.b0 = (const char *)f2.b0 + (size_t)ks * es;
         f2b.bias = nullptr;
         f2b.res = nullptr;
         f2b.c0 = ws + L.z2;
@@ -455,8 +545,8 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
     } else {
         TXL_TRY(hip_check(launch_gemm(bf, single(f2), s), "FFN2 launch"));
     }
-    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), z2, p->ln2_g, p->ln2_b, y, y_bstride, B, W,
-                                        D, s),
+    TXL_TRY(hip_check(launch_layer_norm(bf, (const float *)(ws + L.z), z2, Dp, p->ln2_g, p->ln2_b, y, y_bstride, y_ld,
+                                        B, W, D, s),
                       "LayerNorm launch"));
     return TXL_OK;
 }
@@ -573,7 +663,7 @@ txl_status txl_rel_attn_fwd_update(txl_dtype dtype, int B, int W, int D, int H, 
     txl_mem next = *mem;
     GemmLaunch gwo = single(rows_problem(B, W, D, D, w + L.o, D, (long long)W * D, p->Wo, out, D, out_bstride));
     // the copy is planned before any launch so that a refused update launches nothing
-    TXL_TRY(plan_mem_update(dtype, B, D, &next, h, h_bstride, W, gwo.rc, gwo.copy_blocks));
+    TXL_TRY(plan_mem_update(dtype, B, D, &next, h, h_bstride, D, W, gwo.rc, gwo.copy_blocks));
     TXL_TRY(enqueue_attention(dtype, B, W, D, H, h, h_bstride, mem, nullptr, p, R, w, L, s));
     TXL_TRY(hip_check(launch_gemm(dtype == TXL_BF16, gwo, s), "output projection launch"));
     *mem = next;
@@ -660,7 +750,7 @@ txl_status txl_layer_fwd(txl_dtype dtype, int B, int W, int D, int H, int F, con
     const Layout L = plan(TXL_OP_LAYER, dtype, B, W, m + W, D, H, F);
     if (!ws || ws_bytes < L.total) return fail(TXL_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total, ws_bytes);
     if ((uintptr_t)ws % 256) return fail(TXL_ERR_ARG, "workspace must be 256-byte aligned");
-    return enqueue_block(dtype, B, W, D, H, F, h, h_bstride, mem, p, R, y, y_bstride, (char *)ws, L,
+    return enqueue_block(dtype, B, W, D, H, F, h, h_bstride, D, mem, p, R, y, y_bstride, D, (char *)ws, L,
                          (hipStream_t)stream);
 }
 
@@ -691,15 +781,18 @@ txl_status txl_stack_fwd_segments(txl_dtype dtype, int B, int W, int D, int H, i
     const size_t es = es_of(dtype);
     for (int t = 0; t < n_seg; ++t) {
         const char *hin = (const char *)x + (size_t)t * W * D * es;
-        long long hin_bs = seq * D;
+        long long hin_bs = seq * D, hin_ld = D;
         for (int l = 0; l < n_layers; ++l) {
             const bool last = l == n_layers - 1;
+            // inter-layer activations at the layout's row pitch, the output in y's
             char *hout = last ? (char *)y + (size_t)t * W * D * es : w + ((l & 1) ? L.hb1 : L.hb0);
-            const long long hout_bs = last ? seq * D : (long long)W * D;
-            TXL_TRY(enqueue_block(dtype, B, W, D, H, F, hin, hin_bs, &mems[l], &params[l], R, hout, hout_bs, w, L, s,
-                                  &mems[l]));
+            const long long hout_ld = last ? D : L.Dp;
+            const long long hout_bs = last ? seq * D : (long long)W * L.Dp;
+            TXL_TRY(enqueue_block(dtype, B, W, D, H, F, hin, hin_bs, hin_ld, &mems[l], &params[l], R, hout, hout_bs,
+                                  hout_ld, w, L, s, &mems[l]));
             hin = hout;
             hin_bs = hout_bs;
+            hin_ld = hout_ld;
         }
     }
     return TXL_OK;
@@ -724,14 +817,17 @@ txl_status txl_stack_fwd_window(txl_dtype dtype, int B, int W, int D, int H, int
     hipStream_t s = (hipStream_t)stream;
     char *w = (char *)ws;
     const char *hin = (const char *)x;
-    long long hin_bs = x_bstride;
+    long long hin_bs = x_bstride, hin_ld = D;
     for (int l = 0; l < n_layers; ++l) {
         const bool last = l == n_layers - 1;
         char *hout = last ? (char *)y : w + ((l & 1) ? L.hb1 : L.hb0);
-        const long long hout_bs = last ? y_bstride : (long long)W * D;
-        TXL_TRY(enqueue_block(dtype, B, W, D, H, F, hin, hin_bs, nullptr, &params[l], R, hout, hout_bs, w, L, s));
+        const long long hout_ld = last ? D : L.Dp;
+        const long long hout_bs = last ? y_bstride : (long long)W * L.Dp;
+        TXL_TRY(enqueue_block(dtype, B, W, D, H, F, hin, hin_bs, hin_ld, nullptr, &params[l], R, hout, hout_bs, hout_ld,
+                              w, L, s));
         hin = hout;
         hin_bs = hout_bs;
+        hin_ld = hout_ld;
     }
     return TXL_OK;
 }

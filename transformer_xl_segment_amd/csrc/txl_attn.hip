@@ -459,10 +459,10 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     const float inv = 1.f / l_tot;
     // log2 of the softmax denominator in the pre-scaled score units
     if (MODE == 1 && hf == 0) A.lse[(long long)bh * A.Wp + qi] = m_run + log2f(l_tot);
-    T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.D + h * A.dh;
+    T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.o_ld + h * A.dh;
     // each group of four registers holds four consecutive columns: one store
     // per group when the row offsets keep those stores aligned
-    const bool vec4 = A.dh % 4 == 0 && A.D % 4 == 0 && A.o_bstride % 4 == 0 &&
+    const bool vec4 = A.dh % 4 == 0 && A.o_ld % 4 == 0 && A.o_bstride % 4 == 0 &&
                       ((uintptr_t)A.o % (4 * sizeof(T))) == 0;
     if (vec4) {
 #pragma unroll
@@ -539,7 +539,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const AttnArgs A) {
     }
     const float inv = 1.f / L;
     const int b = bh / A.H, h = bh - b * A.H;
-    T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.D + h * A.dh;
+    T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.o_ld + h * A.dh;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int d = 8 * g + i;
@@ -598,6 +598,7 @@ bool rel_attn_supported(int dh) { return dh >= 1 && dh <= 64; }
 hipError_t launch_rel_attn(bool is_bf16, const AttnArgs &args, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
     AttnArgs a = args;
     if (a.nsplit < 1 || !a.part_o || !a.part_ml) a.nsplit = 1;
+    if (a.o_ld <= 0) a.o_ld = a.D;
     return is_bf16 ? launch_t<bf16>(a, s, start, stop) : launch_t<float>(a, s, start, stop);
 }
 

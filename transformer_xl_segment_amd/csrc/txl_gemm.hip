@@ -16,6 +16,8 @@
 // Tiles are numbered so that tiles sharing rows of A are consecutive, and the
 // workgroup index is remapped so that consecutive tiles land on the same XCD
 // (workgroups are dealt round-robin over the 8 XCDs, each with its own L2).
+#include <string.h>
+
 #include <type_traits>
 
 #include "txl_device.hpp"
@@ -56,7 +58,7 @@ __device__ __forceinline__ const char *a_row_ptr(const GemmProblem &P, int row, 
         if (t < P.mem_len) {
             int pr = P.ring_head + t;
             if (pr >= P.ring_M) pr -= P.ring_M;
-            return (const char *)P.ring + ((long long)b * P.ring_bstride + (long long)pr * P.a_ld) * (long long)sizeof(T);
+            return (const char *)P.ring + ((long long)b * P.ring_bstride + (long long)pr * P.ring_ld) * (long long)sizeof(T);
         }
         t -= P.mem_len;
     }
@@ -306,8 +308,8 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
     constexpr int kChA = BM * (kRowBytes / 16) / kThreads;          // 16-byte chunks per thread, A
     constexpr int kChB = kBN * (kRowBytes / 16) / kThreads;         // ... B
     __shared__ GemmSmem<BM> sm;
-    if ((int)blockIdx.x >= g.total_tiles) {                         // a memory-update workgroup
-        ring_copy_block(g.rc, blockIdx.x - g.total_tiles);
+    if ((int)blockIdx.x >= g.total_tiles) {                         // a copy workgroup
+        extra_block(g, blockIdx.x - g.total_tiles);
         return;
     }
     // XCD-aware remap: deal consecutive tiles to the same XCD.
@@ -475,8 +477,8 @@ __global__ void __launch_bounds__(kThreads, BN == 64 ? 4 : 3) gemm_lds_kernel(co
     constexpr int EPC = 16 / (int)sizeof(T);             // elements per chunk
     static_assert(ROWS % 64 == 0, "whole load instructions per wave");
     __shared__ GemmLdsSmem<BM, BN> sm;
-    if ((int)blockIdx.x >= g.total_tiles) {                         // a memory-update workgroup
-        ring_copy_block(g.rc, blockIdx.x - g.total_tiles);
+    if ((int)blockIdx.x >= g.total_tiles) {                         // a copy workgroup
+        extra_block(g, blockIdx.x - g.total_tiles);
         return;
     }
 
@@ -612,7 +614,8 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p) {
     const long long epc = 16 / es;
     if (p.kdim % epc) return false;
     if ((p.a_ld * es) % 16 || (p.a_bstride * es) % 16 || !aligned16(p.a)) return false;
-    if (p.a_mode == A_CONTEXT && (!aligned16(p.ring) || (p.ring_bstride * es) % 16)) return false;
+    if (p.a_mode == A_CONTEXT && (!aligned16(p.ring) || (p.ring_bstride * es) % 16 || (p.ring_ld * es) % 16))
+        return false;
     if ((p.b_ld * es) % 16 || (p.b_bstride * es) % 16 || !aligned16(p.b0) || (p.b1 && !aligned16(p.b1))) return false;
     if (p.epi == EPI_ROWS) {
         // eight-column vector stores of the output (and loads of the residual)
@@ -625,7 +628,7 @@ bool gemm_vec_ok(bool is_bf16, const GemmProblem &p) {
 
 template <int BM>
 void launch_bm(bool is_bf16, bool vec, const GemmLaunch &g, hipStream_t s) {
-    dim3 grid(g.total_tiles + g.copy_blocks), block(kThreads);
+    dim3 grid(g.total_tiles + extra_blocks(g)), block(kThreads);
     if (is_bf16) {
         if (vec) hipLaunchKernelGGL((gemm_lds_kernel<bf16, BM, kBN>), grid, block, 0, s, g);
         else hipLaunchKernelGGL((gemm_kernel<bf16, false, BM>), grid, block, 0, s, g);
@@ -640,9 +643,9 @@ void launch_bm(bool is_bf16, bool vec, const GemmLaunch &g, hipStream_t s) {
 constexpr int kSmallGrid = 512;
 
 hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s) {
-    if (g.total_tiles <= 0 && g.copy_blocks <= 0) return hipSuccess;
-    if (g.total_tiles <= 0) {                     // a memory update alone
-        hipLaunchKernelGGL((gemm_kernel<bf16, false, 64>), dim3(g.copy_blocks), dim3(kThreads), 0, s, g);
+    if (g.total_tiles <= 0 && extra_blocks(g) <= 0) return hipSuccess;
+    if (g.total_tiles <= 0) {                     // copies alone
+        hipLaunchKernelGGL((gemm_kernel<bf16, false, 64>), dim3(extra_blocks(g)), dim3(kThreads), 0, s, g);
         return hipGetLastError();
     }
     bool vec = true, narrow = true;
@@ -663,7 +666,7 @@ hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s) {
             t += P.tile_count;
         }
         gn.total_tiles = t;
-        dim3 grid(gn.total_tiles + gn.copy_blocks), block(kThreads);
+        dim3 grid(gn.total_tiles + extra_blocks(gn)), block(kThreads);
         if (is_bf16) hipLaunchKernelGGL((gemm_lds_kernel<bf16, 128, 64>), grid, block, 0, s, gn);
         else hipLaunchKernelGGL((gemm_lds_kernel<float, 128, 64>), grid, block, 0, s, gn);
         return hipGetLastError();
@@ -683,6 +686,20 @@ hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s) {
         launch_bm<64>(is_bf16, vec, g64, s);
     }
     return hipGetLastError();
+}
+
+}  // namespace txl
+
+namespace txl {
+
+hipError_t launch_pitch_copies(const PitchCopy *pc, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (n > kMaxPitchCopies) return hipErrorInvalidValue;
+    GemmLaunch g;
+    memset(&g, 0, sizeof(g));
+    for (int i = 0; i < n; ++i) g.pc[i] = pc[i];
+    g.pc_count = n;
+    return launch_gemm(true, g, s);
 }
 
 }  // namespace txl

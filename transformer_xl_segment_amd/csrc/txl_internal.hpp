@@ -49,6 +49,7 @@ struct GemmProblem {
     long long a_ld, a_bstride;
     const void *ring;
     long long ring_bstride;      // elements between batch entries of the ring (M*ld)
+    long long ring_ld;           // elements between rows of the ring
     int ring_M, ring_head, mem_len;
     // B operand
     int b_mode;
@@ -79,17 +80,35 @@ struct GemmProblem {
 // Memory update riding along a GEMM launch (segment-recurrence simulator: mem =
 // last M rows of [mem; h]): the workgroups after the launch's tiles copy, for
 // every batch row b, the n source rows src_row0 .. src_row0+n-1 of b into ring
-// slots pos0, pos0+1, ... (mod M). One batch row's copy is two contiguous runs
-// (before and after the wrap), moved in words of 16 bytes (vec) or 4 bytes;
-// word indices within a batch row fit 32 bits. blocks_x workgroups per batch
-// row, each kRingCopyUnroll x 256 words.
+// slots pos0, pos0+1, ... (mod M). With contiguous source rows one batch row's
+// copy is two contiguous runs (before and after the wrap), moved in words of
+// 16 bytes (vec) or 4 bytes, kRingCopyUnroll x 256 words per workgroup; with a
+// source row pitch other than the row length (a padded activation) each
+// workgroup copies kRingCopyRows rows word by word. Word indices within a
+// batch row fit 32 bits. blocks_x workgroups per batch row.
 struct RingCopy {
     char *ring;
     const char *src;
     long long src_bstride_bytes;
     int M, row_words, pos0, src_row0, n, blocks_x, vec;
+    int src_pitch_words;         // words between source rows
 };
 constexpr int kRingCopyUnroll = 4;
+constexpr int kRingCopyRows = 8;
+
+// A strided copy with zero fill riding along a launch the same way: for rows
+// r < rows (batch entry r / seg_rows, row r % seg_rows), dst words [w0, w1) take
+// src word c - w0 while c - w0 < copy_w and zero after it (src null: zeros
+// only). Used to lay rows out at a 16-byte aligned pitch.
+struct PitchCopy {
+    const uint32_t *src;
+    uint32_t *dst;
+    long long src_pitch, dst_pitch;   // words between rows of one batch entry
+    long long src_bstride, dst_bstride;  // words between batch entries
+    int seg_rows;                     // rows per batch entry (row r = (r / seg_rows, r % seg_rows))
+    int rows, w0, w1, copy_w, blocks;
+};
+constexpr int kMaxPitchCopies = 6;
 
 struct GemmLaunch {
     GemmProblem p[3];
@@ -97,16 +116,39 @@ struct GemmLaunch {
     int total_tiles;
     RingCopy rc;
     int copy_blocks;             // workgroups after the tiles that run rc (0: none)
+    PitchCopy pc[kMaxPitchCopies];
+    int pc_count;                // pitched copies run by the workgroups after those
 };
+
+// Workgroups a launch adds after its tiles.
+inline int extra_blocks(const GemmLaunch &g) {
+    int n = g.copy_blocks;
+    for (int i = 0; i < g.pc_count; ++i) n += g.pc[i].blocks;
+    return n;
+}
 
 // Workgroup `blk` (0 <= blk < blocks_x * B) of a ring copy, 256 threads.
 __device__ __forceinline__ void ring_copy_block(const RingCopy &rc, int blk) {
     const int b = blk / rc.blocks_x, bx = blk - b * rc.blocks_x;
+    const char *s0 = rc.src + (long long)b * rc.src_bstride_bytes;
+    char *d0 = rc.ring + (long long)b * rc.M * rc.row_words * (rc.vec ? 16 : 4);
+    if (rc.src_pitch_words != rc.row_words) {
+        // pitched source rows (4-byte words): kRingCopyRows rows per workgroup
+        const uint32_t *s = reinterpret_cast<const uint32_t *>(s0);
+        uint32_t *d = reinterpret_cast<uint32_t *>(d0);
+        const int r1 = min(rc.n, (bx + 1) * kRingCopyRows);
+        for (int r = bx * kRingCopyRows; r < r1; ++r) {
+            int slot = rc.pos0 + r;
+            if (slot >= rc.M) slot -= rc.M;
+            const uint32_t *sr = s + (long long)(rc.src_row0 + r) * rc.src_pitch_words;
+            uint32_t *dr = d + (long long)slot * rc.row_words;
+            for (int c = (int)threadIdx.x; c < rc.row_words; c += 256) dr[c] = sr[c];
+        }
+        return;
+    }
     const int total = rc.n * rc.row_words;                       // words of this batch row
     const int split = min(rc.n, rc.M - rc.pos0) * rc.row_words;  // words before the wrap
     const int base = bx * 256 * kRingCopyUnroll + (int)threadIdx.x;
-    const char *s0 = rc.src + (long long)b * rc.src_bstride_bytes;
-    char *d0 = rc.ring + (long long)b * rc.M * rc.row_words * (rc.vec ? 16 : 4);
     auto run = [&](auto word) {
         typedef decltype(word) Word;
         const Word *s = reinterpret_cast<const Word *>(s0) + (long long)rc.src_row0 * rc.row_words;
@@ -128,11 +170,55 @@ __device__ __forceinline__ void ring_copy_block(const RingCopy &rc, int blk) {
     else run(uint32_t());
 }
 
+__device__ __forceinline__ void pitch_copy_block(const PitchCopy &pc, int blk) {
+    const int width = pc.w1 - pc.w0;
+    if (width >= 64) {
+        // wide rows: a row per step, the threads across its words
+        for (int r = blk; r < pc.rows; r += pc.blocks) {
+            const int b = r / pc.seg_rows, t = r - b * pc.seg_rows;
+            const uint32_t *sr = pc.src ? pc.src + (long long)b * pc.src_bstride + (long long)t * pc.src_pitch : nullptr;
+            uint32_t *dr = pc.dst + (long long)b * pc.dst_bstride + (long long)t * pc.dst_pitch + pc.w0;
+            for (int k = (int)threadIdx.x; k < width; k += 256) dr[k] = (sr && k < pc.copy_w) ? sr[k] : 0u;
+        }
+        return;
+    }
+    // narrow rows (pad columns): one word per thread and step over rows x words
+    const long long total = (long long)pc.rows * width;
+    for (long long idx = (long long)blk * 256 + threadIdx.x; idx < total; idx += (long long)pc.blocks * 256) {
+        const int r = (int)(idx / width);
+        const int k = (int)(idx - (long long)r * width);
+        const int b = r / pc.seg_rows, t = r - b * pc.seg_rows;
+        uint32_t v = 0u;
+        if (pc.src && k < pc.copy_w) v = pc.src[(long long)b * pc.src_bstride + (long long)t * pc.src_pitch + k];
+        pc.dst[(long long)b * pc.dst_bstride + (long long)t * pc.dst_pitch + pc.w0 + k] = v;
+    }
+}
+
+// The work of workgroup `blk` counted from the first one after a launch's tiles.
+__device__ __forceinline__ void extra_block(const GemmLaunch &g, int blk) {
+    if (blk < g.copy_blocks) {
+        ring_copy_block(g.rc, blk);
+        return;
+    }
+    blk -= g.copy_blocks;
+#pragma unroll
+    for (int i = 0; i < kMaxPitchCopies; ++i) {
+        if (i < g.pc_count) {
+            if (blk < g.pc[i].blocks) {
+                pitch_copy_block(g.pc[i], blk);
+                return;
+            }
+            blk -= g.pc[i].blocks;
+        }
+    }
+}
+
 // Plans the copy "ring rows (pos0 + t) % M of every batch entry <- src rows
-// src_row0 + t, t < n" into rc; returns the number of workgroups (B * blocks_x,
-// 0 for nothing to copy) or -1 if the sizes exceed the 32-bit word indexing.
+// src_row0 + t, t < n" (source rows src_ld elements apart) into rc; returns the
+// number of workgroups (B * blocks_x, 0 for nothing to copy) or -1 if the sizes
+// exceed the 32-bit word indexing.
 int plan_ring_copy(bool is_bf16, RingCopy &rc, void *ring, int M, int D, int pos0, const void *src,
-                   long long src_bstride, int src_row0, int n, int B);
+                   long long src_bstride, long long src_ld, int src_row0, int n, int B);
 
 // Returns a hipError_t from the launch.
 hipError_t launch_gemm(bool is_bf16, const GemmLaunch &g, hipStream_t s);
@@ -161,6 +247,7 @@ struct AttnArgs {
     const void *qu, *qv, *ke, *vt, *rk;
     void *o;
     long long o_bstride;
+    long long o_ld;              // elements between rows of o (0: D)
     int B, H, W, Wp, m, K, Kp, dh, dp, D;
     int C, khead;
     long long rk_hstride;
@@ -266,9 +353,13 @@ hipError_t launch_bwd_finish(const BwdDims &d, const float *drh, const float *pa
 // ---------------------------------------------------------------------------
 // A planned ring copy (plan_ring_copy) as its own launch of `blocks` workgroups.
 hipError_t launch_ring_copy(const RingCopy &rc, int blocks, hipStream_t s);
-// y[b][t] = LN(x[b][t] (+ x2[b][t])) with fp32 input(s), T output (batch stride y_bstride); x2 may be null
-hipError_t launch_layer_norm(bool is_bf16, const float *x, const float *x2, const void *g, const void *b, void *y,
-                             long long y_bstride, int B, int W, int D, hipStream_t s);
+// Pitched copies (at most kMaxPitchCopies) as a launch of their own.
+hipError_t launch_pitch_copies(const PitchCopy *pc, int n, hipStream_t s);
+// y[b][t] = LN(x[b][t] (+ x2[b][t])) with fp32 input(s) (rows x_ld apart, row b*W + t), T output (batch
+// stride y_bstride, rows y_ld apart); x2 may be null
+hipError_t launch_layer_norm(bool is_bf16, const float *x, const float *x2, long long x_ld, const void *g,
+                             const void *b, void *y, long long y_bstride, long long y_ld, int B, int W, int D,
+                             hipStream_t s);
 hipError_t launch_sinusoid(bool is_bf16, void *R, int R_len, int D, hipStream_t s);
 
 }  // namespace txl

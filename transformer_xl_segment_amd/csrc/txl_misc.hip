@@ -23,13 +23,13 @@ __global__ void __launch_bounds__(256) ring_write_kernel(const RingCopy rc) { ri
 // per row; statistics in fp32 from an fp32 input row, which is x, or x + x2
 // when the producing GEMM split its reduction in two.
 template <typename T>
-__global__ void layer_norm_kernel(const float *x, const float *x2, const T *g, const T *bt, T *y,
-                                  long long y_bstride, int rows, int W, int D) {
+__global__ void layer_norm_kernel(const float *x, const float *x2, long long x_ld, const T *g, const T *bt, T *y,
+                                  long long y_bstride, long long y_ld, int rows, int W, int D) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
-    const float *xr = x + (long long)row * D;
-    const float *x2r = x2 ? x2 + (long long)row * D : nullptr;
+    const float *xr = x + (long long)row * x_ld;
+    const float *x2r = x2 ? x2 + (long long)row * x_ld : nullptr;
     constexpr int MAXE = 16;                 // D <= 1024
     float v[MAXE];
     float s = 0.f;
@@ -54,7 +54,7 @@ __global__ void layer_norm_kernel(const float *x, const float *x2, const T *g, c
     for (int off = 32; off >= 1; off >>= 1) q += __shfl_xor(q, off);
     const float inv = 1.f / (sqrtf(q / (float)D) + 1e-6f);
     const int b = row / W, t = row - b * W;
-    T *yr = y + (long long)b * y_bstride + (long long)t * D;
+    T *yr = y + (long long)b * y_bstride + (long long)t * y_ld;
 #pragma unroll
     for (int e = 0; e < MAXE; ++e) {
         const int c = lane + 64 * e;
@@ -81,17 +81,19 @@ __global__ void sinusoid_kernel(T *R, int R_len, int D) {
 }  // namespace
 
 int plan_ring_copy(bool is_bf16, RingCopy &rc, void *ring, int M, int D, int pos0, const void *src,
-                   long long src_bstride, int src_row0, int n, int B) {
+                   long long src_bstride, long long src_ld, int src_row0, int n, int B) {
     if (n <= 0 || B <= 0) return 0;
     const long long es = is_bf16 ? 2 : 4;
     const long long row_bytes = D * es;
-    const bool vec = (row_bytes % 16 == 0) && (((uintptr_t)ring | (uintptr_t)src) % 16 == 0) &&
+    const bool pitched = src_ld != D;
+    const bool vec = !pitched && (row_bytes % 16 == 0) && (((uintptr_t)ring | (uintptr_t)src) % 16 == 0) &&
                      ((src_bstride * es) % 16 == 0);
     const long long per_block = 256LL * kRingCopyUnroll;
     const long long row_words = row_bytes / (vec ? 16 : 4);
     const long long words = (long long)n * row_words;            // per batch row
     if (words > 0x7fffffffLL - per_block || (long long)M * row_words > 0x7fffffffLL) return -1;
-    const long long bx = (words + per_block - 1) / per_block;
+    if (pitched && (src_ld * es) % 4) return -1;
+    const long long bx = pitched ? (n + kRingCopyRows - 1) / kRingCopyRows : (words + per_block - 1) / per_block;
     if (bx * B > 0x7fffffffLL) return -1;
     rc.ring = (char *)ring;
     rc.src = (const char *)src;
@@ -103,6 +105,7 @@ int plan_ring_copy(bool is_bf16, RingCopy &rc, void *ring, int M, int D, int pos
     rc.n = n;
     rc.blocks_x = (int)bx;
     rc.vec = vec;
+    rc.src_pitch_words = pitched ? (int)(src_ld * es / 4) : (int)row_words;
     return (int)(bx * B);
 }
 
@@ -112,16 +115,17 @@ hipError_t launch_ring_copy(const RingCopy &rc, int blocks, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_layer_norm(bool is_bf16, const float *x, const float *x2, const void *g, const void *b, void *y,
-                             long long y_bstride, int B, int W, int D, hipStream_t s) {
+hipError_t launch_layer_norm(bool is_bf16, const float *x, const float *x2, long long x_ld, const void *g,
+                             const void *b, void *y, long long y_bstride, long long y_ld, int B, int W, int D,
+                             hipStream_t s) {
     const int rows = B * W;
     dim3 grid((rows + 3) / 4), block(256);
     if (is_bf16)
-        hipLaunchKernelGGL(layer_norm_kernel<bf16>, grid, block, 0, s, x, x2, (const bf16 *)g, (const bf16 *)b,
-                           (bf16 *)y, y_bstride, rows, W, D);
+        hipLaunchKernelGGL(layer_norm_kernel<bf16>, grid, block, 0, s, x, x2, x_ld, (const bf16 *)g, (const bf16 *)b,
+                           (bf16 *)y, y_bstride, y_ld, rows, W, D);
     else
-        hipLaunchKernelGGL(layer_norm_kernel<float>, grid, block, 0, s, x, x2, (const float *)g,
-                           (const float *)b, (float *)y, y_bstride, rows, W, D);
+        hipLaunchKernelGGL(layer_norm_kernel<float>, grid, block, 0, s, x, x2, x_ld, (const float *)g,
+                           (const float *)b, (float *)y, y_bstride, y_ld, rows, W, D);
     return hipGetLastError();
 }
 

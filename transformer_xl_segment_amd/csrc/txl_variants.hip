@@ -168,7 +168,7 @@ __global__ void __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) shaw_values_ker
         }
     }
     if (!q_ok) return;
-    T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * A.D + h * dh;
+    T *orow = (T *)A.o + (long long)b * A.o_bstride + (long long)qi * (A.o_ld > 0 ? A.o_ld : A.D) + h * dh;
 #pragma unroll
     for (int o = 0; o < NO; ++o)
 #pragma unroll
