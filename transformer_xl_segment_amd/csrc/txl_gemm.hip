@@ -455,6 +455,7 @@ struct GemmLdsSmem {
 };
 static_assert(sizeof(GemmLdsSmem<64, 128>) >= 64 * 132 * 4, "C staging must fit in the operand buffers");
 static_assert(sizeof(GemmLdsSmem<128, 64>) >= 64 * 132 * 4, "C staging must fit in the operand buffers");
+static_assert(sizeof(GemmLdsSmem<128, 128>) >= 128 * 136 * 2, "bf16 staging must fit in the operand buffers");
 
 // Source of lanes whose chunk lies past kdim or in a row without data.
 __device__ __align__(16) unsigned int g_zero_chunk[4];
@@ -528,12 +529,6 @@ __global__ void __launch_bounds__(kThreads, BN == 64 ? 4 : 3) gemm_lds_kernel(co
         }
     };
 
-    f32x16 acc[MI][NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = zero16();
-
     const int fr = lane & 31, fh = lane >> 5;
     const int sw = (fr >> 2) & 3;                        // this lane's row swizzle
     auto frag = [&](Frag<T> &f, const char *bufp, int row, int e0) {
@@ -546,63 +541,139 @@ __global__ void __launch_bounds__(kThreads, BN == 64 ? 4 : 3) gemm_lds_kernel(co
             f.hi = *reinterpret_cast<const f32x4 *>(r + (((e0 / EPC + 1) ^ sw) << 4));
         }
     };
-    auto mma_tile = [&](const char *bufp) {
+
+    // bf16 key / value tiles wholly on one side of the split write their output
+    // through a bf16 staging tile in one round; the value tiles compute C blocks
+    // (operands swapped: lane = column, registers = four consecutive rows) so
+    // that the staging holds the transposed output row by row
+    const bool kvtile = sizeof(T) == 2 && BM == 128 && BN == 128 && P.epi == EPI_KV &&
+                        (n0 + BN <= P.b_split || n0 >= P.b_split);
+    const bool vtile = kvtile && n0 >= P.b_split;
+
+    auto run = [&](auto swap) {
+        constexpr bool SWAP = decltype(swap)::value;
+        f32x16 acc[MI][NJ];
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            Frag<T> fa[MI], fb[NJ];
-            const int e0 = ks * 16 + fh * 8;
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int i = 0; i < MI; ++i) frag(fa[i], bufp, wm * (BM / 2) + i * 32 + fr, e0);
+            for (int j = 0; j < NJ; ++j) acc[i][j] = zero16();
+        auto mma_tile = [&](const char *bufp) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) frag(fb[j], bufp, BM + wn * (BN / 2) + j * 32 + fr, e0);
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                Frag<T> fa[MI], fb[NJ];
+                const int e0 = ks * 16 + fh * 8;
 #pragma unroll
-            for (int i = 0; i < MI; ++i)
+                for (int i = 0; i < MI; ++i) frag(fa[i], bufp, wm * (BM / 2) + i * 32 + fr, e0);
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) mma16(acc[i][j], fb[j], fa[i]);   // C^T block: lane = row of C
+                for (int j = 0; j < NJ; ++j) frag(fb[j], bufp, BM + wn * (BN / 2) + j * 32 + fr, e0);
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        if constexpr (SWAP) mma16(acc[i][j], fa[i], fb[j]);   // C block: lane = column of C
+                        else mma16(acc[i][j], fb[j], fa[i]);                  // C^T block: lane = row of C
+                    }
+            }
+        };
+
+        // Each wave completes all of its loads in flight before the barrier of a
+        // k-tile (the compiler cannot tell the three buffers apart and would wait
+        // for them before the fragment reads anyway): k-tile kt+2 is requested
+        // right after the barrier of k-tile kt and complete at the barrier of
+        // k-tile kt+1, one k-tile of products later.
+        // a causal band of zeros in A: this tile's rows are zero before k-tile kt0
+        int kt0 = 0;
+        if (P.kz_on) kt0 = min(max(0, m0 - bidx * P.seg_rows - P.kz_lag) / BK, nk - 1);   // >= 1 k-tile runs
+        issue(kt0, 0);
+        if (kt0 + 1 < nk) issue(kt0 + 1, 1);
+        int b = 0;                                           // buffer of k-tile kt
+        for (int kt = kt0; kt < nk; ++kt) {
+            // every wave's chunks of k-tile kt are in LDS, and every wave is done
+            // reading the buffer of k-tile kt-1, which k-tile kt+2 now fills
+            wait_loads();
+            __syncthreads();
+            if (kt + 2 < nk) issue(kt + 2, b == 0 ? 2 : b - 1);
+            mma_tile(sm.buf[b]);
+            b = b == 2 ? 0 : b + 1;
         }
-    };
+        __syncthreads();                                     // all reads done before C staging
 
-    // Each wave completes all of its loads in flight before the barrier of a
-    // k-tile (the compiler cannot tell the three buffers apart and would wait
-    // for them before the fragment reads anyway): k-tile kt+2 is requested
-    // right after the barrier of k-tile kt and complete at the barrier of
-    // k-tile kt+1, one k-tile of products later.
-    // a causal band of zeros in A: this tile's rows are zero before k-tile kt0
-    int kt0 = 0;
-    if (P.kz_on) kt0 = min(max(0, m0 - bidx * P.seg_rows - P.kz_lag) / BK, nk - 1);   // >= 1 k-tile runs
-    issue(kt0, 0);
-    if (kt0 + 1 < nk) issue(kt0 + 1, 1);
-    int b = 0;                                           // buffer of k-tile kt
-    for (int kt = kt0; kt < nk; ++kt) {
-        // every wave's chunks of k-tile kt are in LDS, and every wave is done
-        // reading the buffer of k-tile kt-1, which k-tile kt+2 now fills
-        wait_loads();
-        __syncthreads();
-        if (kt + 2 < nk) issue(kt + 2, b == 0 ? 2 : b - 1);
-        mma_tile(sm.buf[b]);
-        b = b == 2 ? 0 : b + 1;
-    }
-    __syncthreads();                                     // all reads done before C staging
-
-    // C staged 64 rows at a time (the waves whose rows fall in that half)
-    float *cs = reinterpret_cast<float *>(&sm);
-#pragma unroll
-    for (int half = 0; half < BM / 64; ++half) {
-        if ((wm * (BM / 2)) / 64 == half) {
+        if (SWAP || kvtile) {
+            // bf16 staging, 136 elements (272 bytes) per row: rows of the tile for
+            // key tiles, columns of the tile for value tiles
+            constexpr int SP = 136;
+            bf16 *st = reinterpret_cast<bf16 *>(&sm);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<f32x4 *>(&cs[(wm * (BM / 2) + i * 32 + fr - 64 * half) * kCPitch + wn * (BN / 2) +
-                                                       j * 32 + crow(4 * q, lane)]) =
-                            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    for (int q = 0; q < 4; ++q) {
+                        const bf16x4 v4 = {(bf16)acc[i][j][4 * q], (bf16)acc[i][j][4 * q + 1],
+                                           (bf16)acc[i][j][4 * q + 2], (bf16)acc[i][j][4 * q + 3]};
+                        // C^T: lane row wm*64 + 32i + fr, columns wn*64 + 32j + crow(4q);
+                        // C: lane column wn*64 + 32j + fr, rows wm*64 + 32i + crow(4q)
+                        const int lr = SWAP ? wn * (BN / 2) + 32 * j + fr : wm * (BM / 2) + 32 * i + fr;
+                        const int lc = SWAP ? wm * (BM / 2) + 32 * i + crow(4 * q, lane)
+                                            : wn * (BN / 2) + 32 * j + crow(4 * q, lane);
+                        *reinterpret_cast<bf16x4 *>(__builtin_assume_aligned(st + lr * SP + lc, 8)) = v4;
+                    }
+            __syncthreads();
+            // 16-byte chunks: 128 staging rows x 16 chunks of 8 elements
+#pragma unroll 2
+            for (int ch = tid; ch < 128 * 16; ch += kThreads) {
+                const int sr = ch >> 4, cc = ch & 15;
+                const bf16x8 v8 = *reinterpret_cast<const bf16x8 *>(
+                    __builtin_assume_aligned(st + sr * SP + 8 * cc, 16));
+                if constexpr (SWAP) {
+                    // staging row = value column n, chunk = 8 consecutive rows (key slots)
+                    const int n = n0 + sr, row = m0 + 8 * cc;
+                    if (n < P.cols && row < P.rows) {
+                        const int bb = fdiv(row, P.seg_rows, inv_seg);
+                        const int t = row - bb * P.seg_rows;
+                        const int nn = n - P.b_split;
+                        const int hh = nn / P.dhp, c = nn - hh * P.dhp;
+                        *reinterpret_cast<bf16x8 *>((bf16 *)P.c1 + (((long long)bb * P.heads + hh) * P.dhp + c) *
+                                                                       P.kv_slots + kv_slot(P, t)) = v8;
+                    }
+                } else {
+                    // staging row = tile row, chunk = 8 consecutive key columns of one head
+                    const int row = m0 + sr, n = n0 + 8 * cc;
+                    if (n < P.cols && row < P.rows) {
+                        const int bb = fdiv(row, P.seg_rows, inv_seg);
+                        const int t = row - bb * P.seg_rows;
+                        const int hh = n / P.dhp, c = n - hh * P.dhp;
+                        *reinterpret_cast<bf16x8 *>((bf16 *)P.c0 + (((long long)bb * P.heads + hh) * P.kv_slots +
+                                                                    kv_slot(P, t)) * P.dhp + c) = v8;
+                    }
+                }
+            }
+            return;
         }
-        __syncthreads();
-        epilogue<T, true, 64, BN>(P, cs, m0 + 64 * half, n0, tid, inv_seg);
-        if (half + 1 < BM / 64) __syncthreads();
-    }
+
+        // C staged 64 rows at a time (the waves whose rows fall in that half)
+        float *cs = reinterpret_cast<float *>(&sm);
+#pragma unroll
+        for (int half = 0; half < BM / 64; ++half) {
+            if ((wm * (BM / 2)) / 64 == half) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<f32x4 *>(&cs[(wm * (BM / 2) + i * 32 + fr - 64 * half) * kCPitch +
+                                                           wn * (BN / 2) + j * 32 + crow(4 * q, lane)]) =
+                                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                      acc[i][j][4 * q + 3]};
+            }
+            __syncthreads();
+            epilogue<T, true, 64, BN>(P, cs, m0 + 64 * half, n0, tid, inv_seg);
+            if (half + 1 < BM / 64) __syncthreads();
+        }
+    };
+    if (vtile) run(std::true_type());
+    else run(std::false_type());
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
