@@ -69,6 +69,9 @@ ATTN_CASES = [
     ("dh64_split_long_mem", 1, 64, 1, 20, 600, 3),
     ("dh64_split_empty_parts", 1, 64, 1, 1024, 16, 2),
     ("dh41_split", 2, 82, 2, 200, 900, 2),
+    # bf16 runs 150 queries as two three-wave blocks (96 + 54) and stores only
+    # the 48 value rows of d_head 41 padded to 48; the ring wraps in segment 2
+    ("dh41_three_wave_blocks", 2, 82, 2, 150, 150, 3),
 ]
 
 

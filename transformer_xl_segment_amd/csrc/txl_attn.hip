@@ -7,8 +7,10 @@
 // projected operands arrive head-major; (q + u) and (q + v) are pre-scaled by
 // log2(e)/sqrt(dh) so the softmax runs on exp2.
 //
-// Work split. A 256-thread workgroup owns 128 consecutive queries of one
-// (b, h); each wave owns 32 of them and walks the visible keys in blocks of 64.
+// Work split. A workgroup of NW waves (four, or three when that does not add
+// query blocks, e.g. 150 queries: two blocks of 96 rather than of 128) owns
+// 32 NW consecutive queries of one (b, h); each wave owns 32 of them and walks
+// the visible keys in blocks of 64.
 // All products use the 32x32 MFMA block with the scores held TRANSPOSED
 // (S^T = K Q^T): lane a%32 of a wave holds the column of query a, and the keys
 // sit in its registers, so row max and row sum over keys are register
@@ -61,12 +63,10 @@ namespace txl {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kQB = 128;          // queries per workgroup (32 per wave)
 constexpr int kKB = 64;           // keys per block
 constexpr int kMaxSplit = 8;      // most key parts per query block
 
-template <typename T, int DP, bool DIST>
+template <typename T, int DP, bool DIST, int NW>
 struct AttnSmem {
     static constexpr int NO = (DP + 31) / 32;                  // 32-row blocks of O^T
     // bf16: key and value rows of 128 bytes whose 16-byte chunks are
@@ -76,9 +76,12 @@ struct AttnSmem {
     static constexpr bool SWZ = sizeof(T) == 2;
     static constexpr int kPitchK = SWZ ? 128 : DP * (int)sizeof(T) + 16;   // bytes per key row
     static constexpr int kPitchV = SWZ ? 128 : kKB * (int)sizeof(T) + 16;  // bytes per value row (V^T)
-    float g[DIST ? kWaves : 1][DIST ? 32 * kGPitch : 4];
+    // V^T rows past DP: stored as zero rows (fp32) or not stored, their
+    // fragments then taken as zero (bf16)
+    static constexpr int kRowsV = SWZ ? DP : NO * 32;
+    float g[DIST ? NW : 1][DIST ? 32 * kGPitch : 4];
     alignas(16) char k[kKB * kPitchK];
-    alignas(16) char v[NO * 32 * kPitchV];
+    alignas(16) char v[kRowsV * kPitchV];
 };
 
 // bf16 key tiles hold their rows permuted inside each group of 16: row r
@@ -105,17 +108,23 @@ __device__ __forceinline__ float psum(const Frag<float> &f, float acc) {
 }
 
 // bf16: two workgroups per CU when their LDS fits in the CU's 160 KB (two
-// waves per SIMD hide each other's latency). fp32 operands double the fragment
-// registers, so fp32 runs one workgroup per CU with the full register file.
-template <typename T, int DP, bool DIST>
-constexpr int attn_wgs_per_cu() { return sizeof(T) == 2 && 2 * sizeof(AttnSmem<T, DP, DIST>) <= 160 * 1024 ? 2 : 1; }
+// waves per SIMD hide each other's latency; a third would leave too few
+// registers). fp32 operands double the fragment registers, so fp32 runs one
+// workgroup per CU with the full register file.
+template <typename T, int DP, bool DIST, int NW>
+constexpr int attn_wgs_per_cu() { return sizeof(T) == 2 && 2 * sizeof(AttnSmem<T, DP, DIST, NW>) <= 160 * 1024 ? 2 : 1; }
+// the same as waves per SIMD, the unit of the launch bound
+template <typename T, int DP, bool DIST, int NW>
+constexpr int attn_waves_per_simd() { return (attn_wgs_per_cu<T, DP, DIST, NW>() * NW + 3) / 4; }
 
 // MODE 0: the full score; 1: also writes the log-sum-exp of every query (for
 // a correction applied afterwards); 2: no distance term (content attention).
-template <typename T, int DP, int MODE>
-__global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) rel_attn_kernel(const AttnArgs A) {
+template <typename T, int DP, int MODE, int NW>
+__global__ void __launch_bounds__(64 * NW, (attn_waves_per_simd<T, DP, MODE != 2, NW>())) rel_attn_kernel(const AttnArgs A) {
     constexpr bool DIST = MODE != 2;
-    typedef AttnSmem<T, DP, DIST> SM;
+    constexpr int NT = 64 * NW;                        // threads
+    constexpr int kQB = 32 * NW;                       // queries per workgroup
+    typedef AttnSmem<T, DP, DIST, NW> SM;
     constexpr int NS = DP / 16;
     constexpr int NO = SM::NO;
     __shared__ SM sm;
@@ -164,7 +173,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     const int dlow = -94 + ((roff - (ATTN_RPAD - 94)) & 31);
 
     // zero the V^T rows past DP once (they pad the last 32-row block of O^T)
-    for (int idx = tid; idx < (NO * 32 - DP) * (SM::kPitchV / 4); idx += 256)
+    for (int idx = tid; idx < (SM::kRowsV - DP) * (SM::kPitchV / 4); idx += NT)
         reinterpret_cast<uint32_t *>(sm.v + DP * SM::kPitchV)[idx] = 0u;
 
     Frag<T> fqu[NS], fqv[NS];
@@ -206,7 +215,7 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     auto key_slot = [&](int j) { const int s = A.khead + j; return s >= A.C ? s - A.C : s; };
     constexpr int KCH = kKB * DP * (int)sizeof(T) / 16;    // 16-byte chunks per K tile
     constexpr int VCH = DP * kKB * (int)sizeof(T) / 16;    // ... per V^T tile
-    constexpr int KPT = (KCH + 255) / 256, VPT = (VCH + 255) / 256;
+    constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT;
     constexpr int KCPR = DP * (int)sizeof(T) / 16;         // chunks per key row
     constexpr int VCPR = kKB * (int)sizeof(T) / 16;        // chunks per V^T row
     constexpr bool SWZ = SM::SWZ;
@@ -215,16 +224,16 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
     do {                                                                                           \
         const int j0_ = (kb_) * kKB;                                                               \
         _Pragma("unroll") for (int c = 0; c < KPT; ++c) {                                          \
-            const int idx = tid + 256 * c;                                                         \
-            if (KCH % 256 == 0 || idx < KCH) {                                                     \
+            const int idx = tid + NT * c;                                                          \
+            if (KCH % NT == 0 || idx < KCH) {                                                      \
                 const int r_ = idx / KCPR, q_ = idx - r_ * KCPR;                                   \
                 const int s_ = key_slot(j0_ + (SWZ ? perm_key(r_) : r_));                          \
                 rkt[c] = *reinterpret_cast<const u32x4 *>((const char *)(ke + (long long)s_ * DP) + q_ * 16); \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int c = 0; c < VPT; ++c) {                                          \
-            const int idx = tid + 256 * c;                                                         \
-            if (VCH % 256 == 0 || idx < VCH) {                                                     \
+            const int idx = tid + NT * c;                                                          \
+            if (VCH % NT == 0 || idx < VCH) {                                                      \
                 const int r_ = idx / VCPR, q_ = idx - r_ * VCPR;                                   \
                 const int s_ = key_slot(j0_ + q_ * (16 / (int)sizeof(T)));                         \
                 rvt[c] = *reinterpret_cast<const u32x4 *>(vt + (long long)r_ * A.C + s_);           \
@@ -234,15 +243,15 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 #define TXL_KV_SSTORE()                                                                            \
     do {                                                                                           \
         _Pragma("unroll") for (int c = 0; c < KPT; ++c) {                                          \
-            const int idx = tid + 256 * c;                                                         \
-            if (KCH % 256 == 0 || idx < KCH) {                                                     \
+            const int idx = tid + NT * c;                                                          \
+            if (KCH % NT == 0 || idx < KCH) {                                                      \
                 const int r_ = idx / KCPR, q_ = idx - r_ * KCPR;                                   \
                 *reinterpret_cast<u32x4 *>(sm.k + r_ * SM::kPitchK + ((SWZ ? q_ ^ (r_ & 7) : q_) << 4)) = rkt[c]; \
             }                                                                                      \
         }                                                                                          \
         _Pragma("unroll") for (int c = 0; c < VPT; ++c) {                                          \
-            const int idx = tid + 256 * c;                                                         \
-            if (VCH % 256 == 0 || idx < VCH) {                                                     \
+            const int idx = tid + NT * c;                                                          \
+            if (VCH % NT == 0 || idx < VCH) {                                                      \
                 const int r_ = idx / VCPR, q_ = idx - r_ * VCPR;                                   \
                 *reinterpret_cast<u32x4 *>(sm.v + r_ * SM::kPitchV + ((SWZ ? q_ ^ (r_ & 7) : q_) << 4)) = rvt[c]; \
             }                                                                                      \
@@ -417,10 +426,15 @@ __global__ void __launch_bounds__(256, (attn_wgs_per_cu<T, DP, MODE != 2>())) re
 #pragma unroll
             for (int o = 0; o < NO; ++o) {
                 Frag<T> fv;
-                if constexpr (SWZ)      // keys 16 p + 8 hf .. + 7: one swizzled chunk
+                if constexpr (SWZ) {    // keys 16 p + 8 hf .. + 7: one swizzled chunk
+                    // rows past DP are not stored: read a stored row, use zeros
+                    const int vr = 32 * o + fr;
+                    const bool in = DP % 32 == 0 || o + 1 < NO || vr < DP;
+                    const int rr = in ? vr : DP - 1;
                     fv.v = *reinterpret_cast<const bf16x8 *>(__builtin_assume_aligned(
-                        sm.v + (32 * o + fr) * SM::kPitchV + (((2 * p + hf) ^ (fr & 7)) << 4), 16));
-                else
+                        sm.v + rr * SM::kPitchV + (((2 * p + hf) ^ (rr & 7)) << 4), 16));
+                    if (!in) fv.v = bf16x8{};
+                } else
                     load_vt(fv, sm.v + (32 * o + fr) * SM::kPitchV, 16 * p + 4 * hf);
                 mma16(oacc[o], fv, fp4[p]);
             }
@@ -551,18 +565,37 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const AttnArgs A) {
 // start/stop (may be null) are stamped by the kernels' own dispatches, so they
 // bracket exactly this launch (attention, and the merge of a key split) on its
 // stream.
+// Three waves (96 queries) per bf16 workgroup when that takes no more query
+// blocks than four would: fewer idle waves in the last block and the active
+// queries spread more evenly over the blocks (150 queries: 96 + 54 instead of
+// 128 + 22). The number of query blocks, and so the key split, is the same
+// either way.
+int attn_waves(bool is_bf16, int W) { return is_bf16 && (W + 95) / 96 <= (W + 127) / 128 ? 3 : 4; }
+
+template <typename T, int DP, int NW>
+void launch_modes(const AttnArgs &a, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop1) {
+    dim3 block(64 * NW);
+    if (!a.dist)
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 2, NW>), grid, block, 0, s, start, stop1, 0, a);
+    else if (a.lse)
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 1, NW>), grid, block, 0, s, start, stop1, 0, a);
+    else
+        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 0, NW>), grid, block, 0, s, start, stop1, 0, a);
+}
+
 template <typename T, int DP>
 hipError_t launch_dp(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-    const int nqb = (a.W + kQB - 1) / kQB;
+    const int nw = attn_waves(sizeof(T) == 2, a.W);
+    const int nqb = (a.W + 32 * nw - 1) / (32 * nw);
     dim3 grid(a.B * a.H * nqb * a.nsplit), block(256);
     const bool merge = a.nsplit > 1;
     hipEvent_t stop1 = merge ? nullptr : stop;
-    if (!a.dist)
-        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 2>), grid, block, 0, s, start, stop1, 0, a);
-    else if (a.lse)
-        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 1>), grid, block, 0, s, start, stop1, 0, a);
-    else
-        hipExtLaunchKernelGGL((rel_attn_kernel<T, DP, 0>), grid, block, 0, s, start, stop1, 0, a);
+    if constexpr (sizeof(T) == 2) {
+        if (nw == 3) launch_modes<T, DP, 3>(a, grid, s, start, stop1);
+        else launch_modes<T, DP, 4>(a, grid, s, start, stop1);
+    } else {
+        launch_modes<T, DP, 4>(a, grid, s, start, stop1);
+    }
     if (merge) {
         const long long threads = (long long)a.B * a.H * a.W * (DP / 8);
         dim3 mgrid((unsigned)((threads + 255) / 256));
@@ -587,7 +620,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent
 int attn_dp(int dh) { return (dh + 15) / 16 * 16; }
 
 int attn_splits(int B, int H, int W, int K) {
-    const long long wgs = (long long)B * H * ((W + kQB - 1) / kQB);
+    const long long wgs = (long long)B * H * ((W + 127) / 128);     // query blocks (of 128 or of 96)
     if (wgs >= 512) return 1;                     // two workgroups per CU already
     const int nkb = (K + kKB - 1) / kKB;          // key blocks of the last query block
     const int want = (int)((512 + wgs - 1) / wgs);
