@@ -73,7 +73,9 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
     const size_t es = es_of(dt);
     const int dh = D / H;
     L.dp = attn_dp(dh);
-    L.Wp = (int)round_up(W, ATTN_QBLOCK);
+    // query rows per (b, h) of the projected q: whole waves of 32 (a
+    // workgroup's last wave past W reads clamped rows and writes nothing)
+    L.Wp = (int)round_up(W, 32);
     L.Kp = (int)round_up(Kmax, ATTN_KBLOCK);
     size_t off = 0;
     auto take = [&](size_t bytes) {
