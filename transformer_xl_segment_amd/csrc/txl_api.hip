@@ -58,11 +58,11 @@ struct Layout {
     size_t hb0, hb1;                   // stack: inter-layer activations
     // block with rows that are not 16-byte aligned: activations at the padded
     // pitches Dp and Fp (pad columns zero), the input rows copied to that pitch
-    // (hx) and W_o, W1 repacked to it (wo, w1), so that the block's own GEMMs
-    // take the direct-to-LDS kernel
+    // (hx) and W_o, W1 repacked to Dp (wo, w1) and W2 to Fp (w2), so that the
+    // block's own GEMMs take the direct-to-LDS kernel
     bool pad;
     int Dp, Fp;
-    size_t hx, wo, w1;
+    size_t hx, wo, w1, w2;
     size_t total;
     int Wp, Kp, dp;
 };
@@ -116,6 +116,7 @@ Layout plan(txl_op op, txl_dtype dt, int B, int W, int Kmax, int D, int H, int F
             L.hx = take((size_t)B * W * L.Dp * es);
             L.wo = take((size_t)D * L.Dp * es);
             L.w1 = take((size_t)F * L.Dp * es);
+            L.w2 = take((size_t)D * L.Fp * es);
         }
     }
     if (op == TXL_OP_STACK) {
@@ -463,11 +464,11 @@ PitchCopy pitch_job(size_t es, const void *src, long long src_ld, long long src_
 // mem = last M rows of [mem; h] rides along the output projection's launch,
 // which comes after every read of the old rows. With a padded layout (L.pad)
 // the block's activations live at the 16-byte aligned pitches Dp and Fp, h is
-// first copied to that pitch unless it is there already, and W_o and W1 are
-// repacked to it by workgroups riding along the projection launch, which also
-// zero the pad columns of o and h1: the output projection and the first FFN
-// product then reduce over Dp (the pad columns contribute zeros) with every
-// operand 16-byte aligned.
+// first copied to that pitch unless it is there already, and W_o, W1 (to Dp)
+// and W2 (to Fp) are repacked by workgroups riding along the projection
+// launch, which also zero the pad columns of o, h1 and f: the output
+// projection and the FFN products then reduce over Dp or Fp (the pad columns
+// contribute zeros) with every operand 16-byte aligned.
 txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const void *h, long long h_bstride,
                          long long h_ld, const txl_mem *mem, const txl_layer_params *p, const void *R, void *y,
                          long long y_bstride, long long y_ld, char *ws, const Layout &L, hipStream_t s,
@@ -476,7 +477,8 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
     const size_t es = es_of(dt);
     const int Dp = L.Dp, Fp = L.Fp;
     const long long WDp = (long long)W * Dp, WFp = (long long)W * Fp;
-    const void *Wo = p->Wo, *W1 = p->W1;
+    const void *Wo = p->Wo, *W1 = p->W1, *W2 = p->W2;
+    static_assert(kMaxPitchCopies >= 6, "the block's repacks and pad clears ride along one launch");
     PitchCopy extra[kMaxPitchCopies];
     int n_extra = 0;
     if (L.pad) {
@@ -489,18 +491,22 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
             h_ld = Dp;
             h_bstride = WDp;
         }
-        // W_o and W1 reduce over d_model: repacked when its rows are not aligned.
-        // W2 reduces over F and is used as it is (aligned rows when F is; a
-        // repacked W2 measured no faster than the dword-aligned kernel)
+        // W_o and W1 reduce over d_model, W2 over F: repacked when their rows
+        // are not aligned
         if (Dp != D) {
             extra[n_extra++] = pitch_job(es, p->Wo, D, 0, ws + L.wo, Dp, 0, D, D, D);
             extra[n_extra++] = pitch_job(es, p->W1, D, 0, ws + L.w1, Dp, 0, F, F, D);
             Wo = ws + L.wo;
             W1 = ws + L.w1;
         }
+        if (Fp != F) {
+            extra[n_extra++] = pitch_job(es, p->W2, F, 0, ws + L.w2, Fp, 0, D, D, F);
+            W2 = ws + L.w2;
+        }
         // pad columns of the GEMM inputs the block writes (nothing else writes them)
         extra[n_extra++] = pitch_job(es, nullptr, 0, 0, ws + L.o, Dp, WDp, B * W, W, D);
         extra[n_extra++] = pitch_job(es, nullptr, 0, 0, ws + L.h1, Dp, WDp, B * W, W, D);
+        if (Fp != F) extra[n_extra++] = pitch_job(es, nullptr, 0, 0, ws + L.f, Fp, WFp, B * W, W, F);
     }
     TXL_TRY(enqueue_attention(dt, B, W, D, H, h, h_bstride, mem, nullptr, p, R, ws, L, s, nullptr, h_ld, Dp, extra,
                               n_extra));
@@ -522,21 +528,24 @@ txl_status enqueue_block(txl_dtype dt, int B, int W, int D, int H, int F, const 
     GemmProblem f1 = rows_problem(B, W, Dp, F, ws + L.h1, Dp, WDp, W1, ws + L.f, Fp, WFp);
     f1.bias = p->b1; f1.relu = 1;
     TXL_TRY(hip_check(launch_gemm(bf, single(f1), s), "FFN1 launch"));
-    // z = h1 + f W2^T + b2 (fp32). In fp32 a long reduction over too few tiles
-    // to give every CU two (64-row tiles) is split in two at a k-tile boundary:
-    // the first half carries the bias and the residual into z, the second half
-    // writes its partial sums to z2, and LayerNorm adds the two (the 16-layer
-    // fp32 stack: 75.2 -> 72.5 ms per schedule; in bf16 the split measured
-    // slower, 21.3 -> 21.7 ms, and is not taken).
-    GemmProblem f2 = rows_problem(B, W, F, D, ws + L.f, Fp, WFp, p->W2, ws + L.z, Dp, WDp);
+    // z = h1 + f W2^T + b2 (fp32), reduced over Fp when W2 was repacked (the pad
+    // columns of f and of the repacked W2 are zero). A long reduction over too
+    // few tiles to give every CU two (64-row tiles) is split in two at a k-tile
+    // boundary when it runs on the direct-to-LDS kernel: the first half carries
+    // the bias and the residual into z, the second half writes its partial sums
+    // to z2, and LayerNorm adds the two (16-layer stacks: fp32 75.2 -> 72.5 ms
+    // per schedule; bf16 with W2 repacked 20.1 -> 19.2 ms, where the split over
+    // the caller's dword-aligned W2 on the register-staged kernel was slower).
+    const int Fk = W2 == p->W2 ? F : Fp;
+    GemmProblem f2 = rows_problem(B, W, Fk, D, ws + L.f, Fp, WFp, W2, ws + L.z, Dp, WDp);
     f2.bias = p->b2; f2.res = ws + L.h1; f2.res_ld = Dp; f2.res_bstride = WDp; f2.out_f32 = 1;
     const long long tiles64 = ((long long)B * W + 63) / 64 * ((D + 127) / 128);
     const float *z2 = nullptr;
-    if (dt == TXL_FP32 && F >= 1024 && tiles64 < 512) {
-        const int ks = (int)round_up((F + 1) / 2, 64);
+    if ((dt == TXL_FP32 || Fk % 8 == 0) && F >= 1024 && tiles64 < 512) {
+        const int ks = (int)round_up((Fk + 1) / 2, 64);
         GemmProblem f2b = f2;
         f2.kdim = ks;
-        f2b.kdim = F - ks;
+        f2b.kdim = Fk - ks;
         f2b.a = (const char *)f2.a + (size_t)ks * es;
         f2b.b0 = (const char *)f2.b0 + (size_t)ks * es;
         f2b.bias = nullptr;
