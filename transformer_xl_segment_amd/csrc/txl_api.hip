@@ -282,10 +282,12 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     const int K = m + W;
     const int Kp = (int)round_up(K, ATTN_KBLOCK);
 
-    GemmLaunch g;
-    memset(&g, 0, sizeof(g));
+    GemmProblem q, kv, r;
+    memset(&q, 0, sizeof(q));
+    memset(&kv, 0, sizeof(kv));
+    memset(&r, 0, sizeof(r));
     // Q: (h Wq^T + u, + v) * log2(e)/sqrt(dh), head-major
-    GemmProblem &q = g.p[0];
+
     q.rows = B * L.Wp; q.cols = H * dp; q.kdim = D;
     q.seg_rows = L.Wp; q.valid_rows = W;
     q.a_mode = A_ROWS; q.a = h; q.a_ld = h_ld; q.a_bstride = h_bstride;
@@ -295,7 +297,6 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     q.u = var ? nullptr : p->u; q.v = var ? nullptr : p->v;        // the variants have no u, v
     q.qscale = (float)(1.4426950408889634 / sqrt((double)dh));
     // K_E and V: of the context [mem; h], or of the segment rows into the cache
-    GemmProblem &kv = g.p[1];
     if (cache) {
         kv = kv_cache_problem(B, W, D, H, dp, h, h_bstride, p, cache);
     } else {
@@ -310,7 +311,6 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     kv.kv_slots = Kp; kv.kv_base = 0;
     }
     // r = R[0:K] WkR^T, shared by the batch
-    GemmProblem &r = g.p[2];
     r.rows = Kp + 2 * ATTN_RPAD; r.cols = H * dp; r.kdim = D;
     r.seg_rows = Kp + 2 * ATTN_RPAD; r.valid_rows = K; r.a_first = ATTN_RPAD;
     r.a_mode = A_ROWS; r.a = R; r.a_ld = D; r.a_bstride = 0;
@@ -318,7 +318,23 @@ txl_status enqueue_attention(txl_dtype dt, int B, int W, int D, int H, const voi
     r.dh = dh; r.dhp = dp; r.heads = H;
     r.epi = EPI_RFRAG; r.c0 = ws + L.rk;
     r.frag_off = rk_frag_off(m); r.frag_hstride = (long long)rk_table_rows(Kp) * dp;
-    g.count = var ? 2 : 3;                                           // the variants need no R W_kR^T
+    // Q and r first: their tiles end with the slower epilogues (two outputs;
+    // the fragment-major table), so they are dealt out ahead of the key/value
+    // tiles and all start in the launch's first round, which then leaves only
+    // key/value tiles for the partly filled second round
+    GemmLaunch g;
+    memset(&g, 0, sizeof(g));
+    g.p[0] = q;
+    if (var) {                                                       // the variants need no R W_kR^T
+        g.p[1] = kv;
+        g.count = 2;
+        g.lead = 1;
+    } else {
+        g.p[1] = r;
+        g.p[2] = kv;
+        g.count = 3;
+        g.lead = 2;
+    }
     int t = 0;
     for (int i = 0; i < g.count; ++i) {
         GemmProblem &P = g.p[i];

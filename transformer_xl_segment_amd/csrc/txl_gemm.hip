@@ -313,10 +313,7 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_kernel(const GemmLaunch g) {
         return;
     }
     // XCD-aware remap: deal consecutive tiles to the same XCD.
-    const int total = g.total_tiles;
-    const int gid = blockIdx.x;
-    const int full = total - (total & 7);
-    const int tile = gid < full ? (gid & 7) * (full >> 3) + (gid >> 3) : gid;
+    const int tile = deal_tile(blockIdx.x, g.total_tiles, lead_tiles(g));
     // select the problem with uniform branches (a dynamic index into the
     // kernel-argument struct would copy it to private memory)
     GemmProblem P;
@@ -483,10 +480,7 @@ __global__ void __launch_bounds__(kThreads, BN == 64 ? 4 : 3) gemm_lds_kernel(co
         return;
     }
 
-    const int total = g.total_tiles;
-    const int gid = blockIdx.x;
-    const int full = total - (total & 7);
-    const int tile = gid < full ? (gid & 7) * (full >> 3) + (gid >> 3) : gid;
+    const int tile = deal_tile(blockIdx.x, g.total_tiles, lead_tiles(g));
     GemmProblem P;
     if (g.count > 2 && tile >= g.p[2].tile_begin) P = g.p[2];
     else if (g.count > 1 && tile >= g.p[1].tile_begin) P = g.p[1];

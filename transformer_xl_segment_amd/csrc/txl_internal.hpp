@@ -114,11 +114,29 @@ struct GemmLaunch {
     GemmProblem p[3];
     int count;
     int total_tiles;
+    int lead;                    // 1 or 2: the tiles of p[0 .. lead-1] are dealt out before the others
     RingCopy rc;
     int copy_blocks;             // workgroups after the tiles that run rc (0: none)
     PitchCopy pc[kMaxPitchCopies];
     int pc_count;                // pitched copies run by the workgroups after those
 };
+
+// Tile of workgroup gid. Workgroups are dispatched in order, round-robin over
+// the 8 XCDs (gid % 8), so each XCD is dealt a contiguous run of tiles
+// (consecutive tiles share A rows in its L2). With `first` > 0 the first
+// first & ~7 tiles are dealt that way before the rest: they all start in the
+// first round of a launch with more tiles than slots.
+__device__ __forceinline__ int deal_tile(int gid, int total, int first) {
+    const int p8 = first & ~7;
+    const int base = gid < p8 ? 0 : p8;
+    const int n = gid < p8 ? p8 : total - p8;
+    const int g = gid - base;
+    const int full = n - (n & 7);
+    return base + (g < full ? (g & 7) * (full >> 3) + (g >> 3) : g);
+}
+__device__ __forceinline__ int lead_tiles(const GemmLaunch &g) {
+    return g.lead == 1 && g.count > 1 ? g.p[1].tile_begin : g.lead == 2 && g.count > 2 ? g.p[2].tile_begin : 0;
+}
 
 // Workgroups a launch adds after its tiles.
 inline int extra_blocks(const GemmLaunch &g) {
