@@ -468,10 +468,10 @@ PitchCopy pitch_job(size_t es, const void *src, long long src_ld, long long src_
     pc.w0 = src ? 0 : (int)words(cols);
     pc.w1 = (int)words(dst_ld);
     pc.copy_w = src ? (int)words(cols) : 0;
-    // wide rows: a workgroup per row (at most 1024); narrow ones: about 16 words per thread
-    const long long work = (long long)rows * (pc.w1 - pc.w0);
-    pc.blocks = pc.w1 - pc.w0 >= 64 ? std::max(1, std::min(rows, 1024))
-                                    : (int)std::max(1LL, std::min(1024LL, (work + 4095) / 4096));
+    // whole rows per workgroup, about kPitchWords words each
+    const int width = std::max(1, pc.w1 - pc.w0);
+    pc.rb = std::max(1, kPitchWords / width);
+    pc.blocks = std::max(1, (rows + pc.rb - 1) / pc.rb);
     return pc;
 }
 

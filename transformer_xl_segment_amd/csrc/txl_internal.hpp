@@ -107,7 +107,9 @@ struct PitchCopy {
     long long src_bstride, dst_bstride;  // words between batch entries
     int seg_rows;                     // rows per batch entry (row r = (r / seg_rows, r % seg_rows))
     int rows, w0, w1, copy_w, blocks;
+    int rb;                           // rows per workgroup (about kPitchWords words)
 };
+constexpr int kPitchWords = 2048;     // words a pitched-copy workgroup moves (8 per thread)
 constexpr int kMaxPitchCopies = 6;
 
 struct GemmLaunch {
@@ -188,27 +190,47 @@ __device__ __forceinline__ void ring_copy_block(const RingCopy &rc, int blk) {
     else run(uint32_t());
 }
 
+// floor(x / d) for 0 <= x < 2^22 (a float reciprocal and one fix-up)
+__device__ __forceinline__ int small_div(int x, int d, float inv) {
+    int q = (int)((float)x * inv);
+    const int r = x - q * d;
+    if (r < 0) q -= 1;
+    else if (r >= d) q += 1;
+    return q;
+}
+
+// Workgroup `blk` of a pitched copy: rows blk rb .. +rb, flat over those rows'
+// words (columns w0 .. w1 of the destination), eight words per thread with
+// all eight loads in flight before the stores.
 __device__ __forceinline__ void pitch_copy_block(const PitchCopy &pc, int blk) {
     const int width = pc.w1 - pc.w0;
-    if (width >= 64) {
-        // wide rows: a row per step, the threads across its words
-        for (int r = blk; r < pc.rows; r += pc.blocks) {
-            const int b = r / pc.seg_rows, t = r - b * pc.seg_rows;
-            const uint32_t *sr = pc.src ? pc.src + (long long)b * pc.src_bstride + (long long)t * pc.src_pitch : nullptr;
-            uint32_t *dr = pc.dst + (long long)b * pc.dst_bstride + (long long)t * pc.dst_pitch + pc.w0;
-            for (int k = (int)threadIdx.x; k < width; k += 256) dr[k] = (sr && k < pc.copy_w) ? sr[k] : 0u;
+    const int r0 = blk * pc.rb;
+    const int nr = min(pc.rb, pc.rows - r0);
+    if (nr <= 0 || width <= 0) return;
+    const int total = nr * width;                     // < 2^22: rb width is about kPitchWords
+    const float inv_w = 1.f / (float)width, inv_s = 1.f / (float)pc.seg_rows;
+    constexpr int U = kPitchWords / 256;
+    for (int base = (int)threadIdx.x; base < total; base += 256 * U) {
+        uint32_t v[U];
+        long long at[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = base + 256 * u;
+            v[u] = 0u;
+            at[u] = -1;
+            if (idx < total) {
+                const int rl = small_div(idx, width, inv_w);
+                const int k = idx - rl * width;
+                const int r = r0 + rl;
+                const int b = small_div(r, pc.seg_rows, inv_s), t = r - b * pc.seg_rows;
+                if (pc.src && pc.w0 + k < pc.copy_w)
+                    v[u] = pc.src[(long long)b * pc.src_bstride + (long long)t * pc.src_pitch + pc.w0 + k];
+                at[u] = (long long)b * pc.dst_bstride + (long long)t * pc.dst_pitch + pc.w0 + k;
+            }
         }
-        return;
-    }
-    // narrow rows (pad columns): one word per thread and step over rows x words
-    const long long total = (long long)pc.rows * width;
-    for (long long idx = (long long)blk * 256 + threadIdx.x; idx < total; idx += (long long)pc.blocks * 256) {
-        const int r = (int)(idx / width);
-        const int k = (int)(idx - (long long)r * width);
-        const int b = r / pc.seg_rows, t = r - b * pc.seg_rows;
-        uint32_t v = 0u;
-        if (pc.src && k < pc.copy_w) v = pc.src[(long long)b * pc.src_bstride + (long long)t * pc.src_pitch + k];
-        pc.dst[(long long)b * pc.dst_bstride + (long long)t * pc.dst_pitch + pc.w0 + k] = v;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (at[u] >= 0) pc.dst[at[u]] = v[u];
     }
 }
 
