@@ -9,6 +9,8 @@
 // parts; "Transformer-XL, explained.", the u and v legend entries: one vector
 // per model, shared by every query). dq, dk and dval are written in their row
 // layouts by the fused kernel and the GEMM epilogue.
+#include <cstring>
+
 #include "txl_device.hpp"
 #include "txl_internal.hpp"
 
@@ -23,13 +25,28 @@ namespace {
 // zero for t >= nrows or c >= dh. A workgroup owns 64 rows of one entry: loads and head-major
 // stores along c, transposed stores along t through an LDS tile. VEC (16-byte aligned rows,
 // dh % 8 == 0): a thread moves eight consecutive elements per access.
+// One operand to pack (rows of src, its row counts, biases, scale, outputs).
+struct PackJob {
+    const void *src;
+    long long src_bs;
+    int nrows, nrows_p;
+    const void *bias0, *bias1;
+    float hm_scale;
+    void *hm0, *hm1, *tr0, *tr1;
+    int block_begin;             // first workgroup of this job in the launch; it has nrows_p / 64 x B H
+};
+// The four operands of a backward call in one launch.
+struct PackLaunch {
+    PackJob j[4];
+    int count, D, H, dh, dp;
+};
+
 template <typename T, bool VEC>
-__global__ void __launch_bounds__(256) pack_kernel(const T *src, long long src_bs, int nrows, int nrows_p, int D,
-                                                   int H, int dh, int dp, const T *bias0, const T *bias1,
-                                                   float hm_scale, T *hm0, T *hm1, T *tr0, T *tr1) {
-    __shared__ float tile[64][65];
-    const int g = blockIdx.y, b = g / H, h = g - b * H;
-    const int t0 = blockIdx.x * 64;
+__device__ __forceinline__ void pack_tile(float (&tile)[64][65], const T *src, long long src_bs, int nrows,
+                                          int nrows_p, int D, int H, int dh, int dp, const T *bias0, const T *bias1,
+                                          float hm_scale, T *hm0, T *hm1, T *tr0, T *tr1, int bx, int g) {
+    const int b = g / H, h = g - b * H;
+    const int t0 = bx * 64;
     const int tid = threadIdx.x;
     const bool two = hm1 || tr1;
     const T *s = src + (long long)b * src_bs + h * dh;
@@ -136,6 +153,23 @@ __global__ void __launch_bounds__(256) pack_kernel(const T *src, long long src_b
     }
 }
 
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256) pack_kernel(const PackLaunch L) {
+    __shared__ float tile[64][65];
+    // the job of this workgroup, by uniform branches (a dynamic index into the
+    // kernel-argument struct would copy it to private memory)
+    const int blk = blockIdx.x;
+    PackJob J;
+    if (L.count > 3 && blk >= L.j[3].block_begin) J = L.j[3];
+    else if (L.count > 2 && blk >= L.j[2].block_begin) J = L.j[2];
+    else if (L.count > 1 && blk >= L.j[1].block_begin) J = L.j[1];
+    else J = L.j[0];
+    const int local = blk - J.block_begin, bxn = J.nrows_p / 64;
+    const int g = local / bxn, bx = local - g * bxn;
+    pack_tile<T, VEC>(tile, (const T *)J.src, J.src_bs, J.nrows, J.nrows_p, L.D, L.H, L.dh, L.dp, (const T *)J.bias0,
+                      (const T *)J.bias1, J.hm_scale, (T *)J.hm0, (T *)J.hm1, (T *)J.tr0, (T *)J.tr1, bx, g);
+}
+
 // Distance-key table of every head in the rk_elem layout (row offset off):
 // table row ATTN_RPAD + d holds r[d][h*dh + c] for 0 <= d < K, c < dh; zeros elsewhere.
 template <typename T>
@@ -207,30 +241,34 @@ int grid_for(long long n) {
 }
 
 template <typename T>
-void pack_rows(const BwdDims &d, const void *src, long long src_bs, int nrows, int nrows_p, const void *bias0,
-               const void *bias1, float hm_scale, void *hm0, void *hm1, void *tr0, void *tr1, hipStream_t s) {
-    const dim3 grid(nrows_p / 64, d.B * d.H), block(256);
-    const bool vec = d.dh % 8 == 0 && (d.D * sizeof(T)) % 16 == 0 && (src_bs * sizeof(T)) % 16 == 0 &&
-                     (uintptr_t)src % 16 == 0 && (!bias0 || (uintptr_t)bias0 % 16 == 0) &&
-                     (!bias1 || (uintptr_t)bias1 % 16 == 0);
-    if (vec)
-        hipLaunchKernelGGL((pack_kernel<T, true>), grid, block, 0, s, (const T *)src, src_bs, nrows, nrows_p, d.D, d.H,
-                           d.dh, d.dp, (const T *)bias0, (const T *)bias1, hm_scale, (T *)hm0, (T *)hm1, (T *)tr0,
-                           (T *)tr1);
-    else
-        hipLaunchKernelGGL((pack_kernel<T, false>), grid, block, 0, s, (const T *)src, src_bs, nrows, nrows_p, d.D,
-                           d.H, d.dh, d.dp, (const T *)bias0, (const T *)bias1, hm_scale, (T *)hm0, (T *)hm1,
-                           (T *)tr0, (T *)tr1);
-}
-
-template <typename T>
 void pack(const BwdDims &d, const BwdPack &o, const void *q, const void *k, const void *val, const void *r,
           const void *u, const void *v, const void *dO, float qscale, hipStream_t s) {
     const long long qbs = (long long)d.W * d.D, kbs = (long long)d.K * d.D;
-    pack_rows<T>(d, q, qbs, d.W, d.Wp, u, v, qscale, o.qu, o.qv, o.qut, o.qvt, s);
-    pack_rows<T>(d, dO, qbs, d.W, d.Wp, nullptr, nullptr, 1.f, o.dOh, nullptr, o.dOt, nullptr, s);
-    pack_rows<T>(d, k, kbs, d.K, d.Kp, nullptr, nullptr, 1.f, o.ke, nullptr, o.ket, nullptr, s);
-    pack_rows<T>(d, val, kbs, d.K, d.Kp, nullptr, nullptr, 1.f, o.vk, nullptr, o.vt, nullptr, s);
+    PackLaunch L;
+    memset(&L, 0, sizeof(L));
+    L.D = d.D; L.H = d.H; L.dh = d.dh; L.dp = d.dp;
+    auto job = [&](const void *src, long long src_bs, int nrows, int nrows_p, const void *bias0, const void *bias1,
+                   float scale, void *hm0, void *hm1, void *tr0, void *tr1) {
+        PackJob &J = L.j[L.count++];
+        J.src = src; J.src_bs = src_bs; J.nrows = nrows; J.nrows_p = nrows_p;
+        J.bias0 = bias0; J.bias1 = bias1; J.hm_scale = scale;
+        J.hm0 = hm0; J.hm1 = hm1; J.tr0 = tr0; J.tr1 = tr1;
+    };
+    job(q, qbs, d.W, d.Wp, u, v, qscale, o.qu, o.qv, o.qut, o.qvt);
+    job(dO, qbs, d.W, d.Wp, nullptr, nullptr, 1.f, o.dOh, nullptr, o.dOt, nullptr);
+    job(k, kbs, d.K, d.Kp, nullptr, nullptr, 1.f, o.ke, nullptr, o.ket, nullptr);
+    job(val, kbs, d.K, d.Kp, nullptr, nullptr, 1.f, o.vk, nullptr, o.vt, nullptr);
+    int blocks = 0;
+    bool vec = d.dh % 8 == 0 && (d.D * sizeof(T)) % 16 == 0;
+    for (int i = 0; i < L.count; ++i) {
+        PackJob &J = L.j[i];
+        J.block_begin = blocks;
+        blocks += (J.nrows_p / 64) * d.B * d.H;
+        vec = vec && (J.src_bs * sizeof(T)) % 16 == 0 && (uintptr_t)J.src % 16 == 0 &&
+              (!J.bias0 || (uintptr_t)J.bias0 % 16 == 0) && (!J.bias1 || (uintptr_t)J.bias1 % 16 == 0);
+    }
+    if (vec) hipLaunchKernelGGL((pack_kernel<T, true>), dim3(blocks), dim3(256), 0, s, L);
+    else hipLaunchKernelGGL((pack_kernel<T, false>), dim3(blocks), dim3(256), 0, s, L);
     const long long nrk = (long long)d.H * rk_table_rows(d.Kp) * d.dp;
     hipLaunchKernelGGL(rk_table_kernel<T>, dim3(grid_for(nrk)), dim3(256), 0, s, (const T *)r, d.K, d.D, d.H, d.dh,
                        d.dp, d.Kp, rk_frag_off(d.m), (T *)o.rk);
