@@ -161,6 +161,28 @@ def longmem_warm(tb, torch, syn, dev, steps):
             "attn_compulsory_gbs": by / avg / 1e9, "attn_frac_hbm_peak": by / avg / 1e9 / HBM_PEAK_GBS}
 
 
+def longmem_schedule(tb, torch, syn, dev, reps):
+    """The long-memory workload as scheduled: its S segments from an empty
+    memory, so the memory grows W rows per segment (m = 0, W, .., (S-1) W)."""
+    bf = torch.bfloat16
+    wl = syn.WORKLOADS["longmem_m1600_bf16"]
+    B, D, H, W, M = wl.B, wl.D, wl.H, wl.W, wl.M
+    prob = syn.draw_problem(wl)
+    params = tb.LayerParams.from_numpy(prob.params[0], bf, dev)
+    R = tb.sinusoid_table(M + W, D, bf, dev)
+    x = torch.from_numpy(prob.x).to(dev).to(bf)
+    segs = [x[:, k * W:(k + 1) * W] for k in range(wl.S)]
+    out = torch.empty(B, W, D, dtype=bf, device=dev)
+    ws = torch.empty(tb.workspace_bytes(tb.OP_REL_ATTN, bf, B, W, M, D, H), dtype=torch.uint8, device=dev)
+    r = time_schedule(tb, torch, segs, params, R, B, M, D, H, out, ws, reps)
+    dh = D // H
+    fl = sum(attn_flops(B, H, dh, W, m) + proj_flops(B, W, m, D) for m in r["memory_lengths"])
+    r.update({"workload": wl.name, "B": B, "W": W, "M": M, "D": D, "H": H,
+              "step": "txl_rel_attn_fwd_update per segment",
+              "tflops_algorithmic": fl / (r["ms_per_schedule"] * 1e-3) / 1e12})
+    return r
+
+
 def time_mem_update(tb, torch, segs, B, M, D, dev, calls):
     """txl_mem_update alone on the headline shape (W = M rows of D moved per
     batch row: read from the segment, written into the ring), HIP events on the
@@ -606,6 +628,7 @@ def main():
     rec["rel_attn_fwd_only"] = time_fwd_only(tb, torch, segs, ring, params, R, H, out, ws, args.steps)
     rec["schedule"] = time_schedule(tb, torch, segs, params, R, B, M, D, H, out, ws, max(3, args.steps // 8))
     rec["longmem_warm"] = longmem_warm(tb, torch, syn, dev, max(10, args.steps // 4))
+    rec["longmem_schedule"] = longmem_schedule(tb, torch, syn, dev, max(3, args.steps // 8))
     rec["mem_update"] = time_mem_update(tb, torch, segs, B, M, D, dev, max(20, args.steps // 2))
     rec["stack16"] = time_stack16(tb, torch, syn, dev, 2)
     rec["stack16_fp32"] = time_stack16(tb, torch, syn, dev, 2, "stack16_fp32")
