@@ -72,6 +72,10 @@ ATTN_CASES = [
     # bf16 runs 150 queries as two three-wave blocks (96 + 54) and stores only
     # the 48 value rows of d_head 41 padded to 48; the ring wraps in segment 2
     ("dh41_three_wave_blocks", 2, 82, 2, 150, 150, 3),
+    # bf16: 320 (b, h) of 150 queries take two rounds as three-wave blocks
+    # (640 on 512 slots) but one as two-wave blocks (960 on 1024), so the
+    # launch runs 64-query blocks of 64 + 64 + 22 queries, four per CU
+    ("dh16_two_wave_grid", 16, 320, 20, 150, 150, 2),
 ]
 
 
@@ -85,6 +89,31 @@ def test_rel_attn_small(dtype, case):
     # bf16 at 5x (score std ~1.3): its q/k rounding moves a score by ~|s| 2^-8,
     # so much sharper rows leave the 2e-2 regime the workloads are held to
     prob = syn.draw_problem(wl, weight_scale=0.3 if dtype == "fp32" else 0.1)
+    errs = run_attn_segments(prob, table(M + W, D, dtype))
+    say(f"  errors {errs}")
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_rel_attn_far_negative_first_scores(dtype):
+    # rows near all-ones with q = 5 h and k = -5 h: every score is about
+    # -25 dh / sqrt(dh) = -100, i.e. -144 in the kernel's log2 units, so each
+    # query's first re-base moves its running maximum far below zero (where
+    # 2^-shift overflows); the output must still be the plain softmax average
+    say(f"far negative first scores {dtype}")
+    B, H, D, W, M, S = 2, 2, 32, 40, 24, 2
+    rng = np.random.default_rng(7)
+    eye = np.eye(D, dtype=np.float32)
+    prm = {"Wq": 5.0 * eye, "WkE": -5.0 * eye, "WkR": np.zeros((D, D), np.float32),
+           "Wv": 0.3 * rng.standard_normal((D, D)).astype(np.float32),
+           "Wo": 0.3 * rng.standard_normal((D, D)).astype(np.float32),
+           "u": np.zeros(D, np.float32), "v": np.zeros(D, np.float32)}
+    x = (1.0 + 0.05 * rng.standard_normal((B, S * W, D))).astype(np.float32)
+    if dtype == "bf16":
+        prm = {k: syn.round_to_bf16(v) for k, v in prm.items()}
+        x = syn.round_to_bf16(x)
+    wl = syn.Workload("far_negative", dtype, B=B, D=D, H=H, W=W, M=M, S=S, op="attn", seed_w=0, seed_x=0)
+    prob = syn.Problem(wl, [prm], x)
     errs = run_attn_segments(prob, table(M + W, D, dtype))
     say(f"  errors {errs}")
     assert max(errs.values()) <= TOL[dtype], errs

@@ -8,9 +8,10 @@
 // log2(e)/sqrt(dh) so the softmax runs on exp2.
 //
 // Work split. A workgroup of NW waves (four, or three when that does not add
-// query blocks, e.g. 150 queries: two blocks of 96 rather than of 128) owns
-// 32 NW consecutive queries of one (b, h); each wave owns 32 of them and walks
-// the visible keys in blocks of 64.
+// query blocks, e.g. 150 queries: two blocks of 96 rather than of 128; or two
+// when that takes fewer rounds of the chip) owns 32 NW consecutive queries of
+// one (b, h); each wave owns 32 of them and walks the visible keys in blocks of
+// 64.
 // All products use the 32x32 MFMA block with the scores held TRANSPOSED
 // (S^T = K Q^T): lane a%32 of a wave holds the column of query a, and the keys
 // sit in its registers, so row max and row sum over keys are register
@@ -107,12 +108,18 @@ __device__ __forceinline__ float psum(const Frag<float> &f, float acc) {
     return acc + ((f.lo[0] + f.lo[1]) + (f.lo[2] + f.lo[3])) + ((f.hi[0] + f.hi[1]) + (f.hi[2] + f.hi[3]));
 }
 
-// bf16: two workgroups per CU when their LDS fits in the CU's 160 KB (two
-// waves per SIMD hide each other's latency; a third would leave too few
-// registers). fp32 operands double the fragment registers, so fp32 runs one
-// workgroup per CU with the full register file.
+// bf16: as many workgroups per CU as its 160 KB of LDS holds, up to two waves
+// per SIMD (two waves hide each other's latency; a third would leave too few
+// registers): two four- or three-wave workgroups, up to four two-wave ones.
+// fp32 operands double the fragment registers, so fp32 runs one workgroup per
+// CU with the full register file.
 template <typename T, int DP, bool DIST, int NW>
-constexpr int attn_wgs_per_cu() { return sizeof(T) == 2 && 2 * sizeof(AttnSmem<T, DP, DIST, NW>) <= 160 * 1024 ? 2 : 1; }
+constexpr int attn_wgs_per_cu() {
+    if (sizeof(T) != 2) return 1;
+    const int by_lds = (int)((160 * 1024) / sizeof(AttnSmem<T, DP, DIST, NW>));
+    const int by_regs = 8 / NW;                  // at most two waves per SIMD
+    return by_lds < 1 ? 1 : by_lds < by_regs ? by_lds : by_regs;
+}
 // the same as waves per SIMD, the unit of the launch bound
 template <typename T, int DP, bool DIST, int NW>
 constexpr int attn_waves_per_simd() { return (attn_wgs_per_cu<T, DP, DIST, NW>() * NW + 3) / 4; }
@@ -373,11 +380,15 @@ __global__ void __launch_bounds__(64 * NW, (attn_waves_per_simd<T, DP, MODE != 2
         mx = half_max(mx);
         // lazy re-base: to the first block's maximum, then whenever a block
         // maximum exceeds the base by more than 8
-        const bool rebase = mx > 8.f || (!started && mx > -INFINITY);
+        const bool first = !started && mx > -INFINITY;
+        const bool rebase = mx > 8.f || first;
         started = started || mx > -INFINITY;
         if (__any(rebase)) {
             const float shift = rebase ? mx : 0.f;
-            const float alpha = __builtin_amdgcn_exp2f(-shift);
+            // before its first visible key a query's output and sum are exactly
+            // zero and stay so: the first re-base scales nothing (its shift, the
+            // first maximum, may be far below zero, where exp2(-shift) overflows)
+            const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-shift);
 #pragma unroll
             for (int o = 0; o < NO; ++o)
 #pragma unroll
@@ -572,6 +583,41 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(const AttnArgs A) {
 // either way.
 int attn_waves(bool is_bf16, int W) { return is_bf16 && (W + 95) / 96 <= (W + 127) / 128 ? 3 : 4; }
 
+// Compute units of the current device (queried once per device).
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// bf16: two-wave workgroups (64 queries) when they take fewer rounds of the
+// chip than the three- or four-wave choice above. A grid just past one round
+// of those (the 16-layer workload's 320 (b, h) x 2 blocks of 96 queries on 512
+// slots) fits one round as 960 blocks of 64 queries, four per CU.
+template <typename T, int DP>
+int pick_waves(const AttnArgs &a) {
+    const int nw = attn_waves(sizeof(T) == 2, a.W);
+    if constexpr (sizeof(T) != 2) return nw;
+    else {
+        const long long bh = (long long)a.B * a.H * a.nsplit;
+        const long long cus = device_cus();
+        auto rounds = [&](int w, int per_cu) {
+            const long long wgs = bh * ((a.W + 32 * w - 1) / (32 * w));
+            return (wgs + per_cu * cus - 1) / (per_cu * cus);
+        };
+        const int per_nw = a.dist ? (nw == 3 ? attn_wgs_per_cu<T, DP, true, 3>() : attn_wgs_per_cu<T, DP, true, 4>())
+                                  : (nw == 3 ? attn_wgs_per_cu<T, DP, false, 3>() : attn_wgs_per_cu<T, DP, false, 4>());
+        const int per_2 = a.dist ? attn_wgs_per_cu<T, DP, true, 2>() : attn_wgs_per_cu<T, DP, false, 2>();
+        return rounds(2, per_2) < rounds(nw, per_nw) ? 2 : nw;
+    }
+}
+
 template <typename T, int DP, int NW>
 void launch_modes(const AttnArgs &a, dim3 grid, hipStream_t s, hipEvent_t start, hipEvent_t stop1) {
     dim3 block(64 * NW);
@@ -585,13 +631,14 @@ void launch_modes(const AttnArgs &a, dim3 grid, hipStream_t s, hipEvent_t start,
 
 template <typename T, int DP>
 hipError_t launch_dp(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEvent_t stop) {
-    const int nw = attn_waves(sizeof(T) == 2, a.W);
+    const int nw = pick_waves<T, DP>(a);
     const int nqb = (a.W + 32 * nw - 1) / (32 * nw);
     dim3 grid(a.B * a.H * nqb * a.nsplit), block(256);
     const bool merge = a.nsplit > 1;
     hipEvent_t stop1 = merge ? nullptr : stop;
     if constexpr (sizeof(T) == 2) {
-        if (nw == 3) launch_modes<T, DP, 3>(a, grid, s, start, stop1);
+        if (nw == 2) launch_modes<T, DP, 2>(a, grid, s, start, stop1);
+        else if (nw == 3) launch_modes<T, DP, 3>(a, grid, s, start, stop1);
         else launch_modes<T, DP, 4>(a, grid, s, start, stop1);
     } else {
         launch_modes<T, DP, 4>(a, grid, s, start, stop1);
