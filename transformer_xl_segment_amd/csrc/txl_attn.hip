@@ -108,16 +108,16 @@ __device__ __forceinline__ float psum(const Frag<float> &f, float acc) {
     return acc + ((f.lo[0] + f.lo[1]) + (f.lo[2] + f.lo[3])) + ((f.hi[0] + f.hi[1]) + (f.hi[2] + f.hi[3]));
 }
 
-// bf16: as many workgroups per CU as its 160 KB of LDS holds, up to two waves
-// per SIMD (two waves hide each other's latency; a third would leave too few
-// registers): two four- or three-wave workgroups, up to four two-wave ones.
-// fp32 operands double the fragment registers, so fp32 runs one workgroup per
-// CU with the full register file.
+// As many workgroups per CU as its 160 KB of LDS holds, up to two waves per
+// SIMD in bf16 (two waves hide each other's latency; a third would leave too
+// few registers): two four- or three-wave workgroups, up to four two-wave ones.
+// fp32 operands double the fragment registers, so fp32 runs one wave per SIMD
+// with the full register file: one four-wave workgroup per CU, or two
+// two-wave ones.
 template <typename T, int DP, bool DIST, int NW>
 constexpr int attn_wgs_per_cu() {
-    if (sizeof(T) != 2) return 1;
     const int by_lds = (int)((160 * 1024) / sizeof(AttnSmem<T, DP, DIST, NW>));
-    const int by_regs = 8 / NW;                  // at most two waves per SIMD
+    const int by_regs = (sizeof(T) == 2 ? 8 : 4) / NW;   // two waves per SIMD (bf16), one (fp32)
     return by_lds < 1 ? 1 : by_lds < by_regs ? by_lds : by_regs;
 }
 // the same as waves per SIMD, the unit of the launch bound
@@ -596,26 +596,24 @@ int device_cus() {
     return cus[dev];
 }
 
-// bf16: two-wave workgroups (64 queries) when they take fewer rounds of the
-// chip than the three- or four-wave choice above. A grid just past one round
-// of those (the 16-layer workload's 320 (b, h) x 2 blocks of 96 queries on 512
-// slots) fits one round as 960 blocks of 64 queries, four per CU.
+// Two-wave workgroups (64 queries) when they take fewer rounds of the chip
+// than the three- or four-wave choice above. The 16-layer workload's 320 (b, h)
+// of 150 queries: in bf16 640 three-wave blocks on 512 slots, or 960 two-wave
+// blocks on 1024 (one round); in fp32 640 four-wave blocks on 256 slots, or
+// 960 two-wave blocks on 512 (two rounds instead of three).
 template <typename T, int DP>
 int pick_waves(const AttnArgs &a) {
     const int nw = attn_waves(sizeof(T) == 2, a.W);
-    if constexpr (sizeof(T) != 2) return nw;
-    else {
-        const long long bh = (long long)a.B * a.H * a.nsplit;
-        const long long cus = device_cus();
-        auto rounds = [&](int w, int per_cu) {
-            const long long wgs = bh * ((a.W + 32 * w - 1) / (32 * w));
-            return (wgs + per_cu * cus - 1) / (per_cu * cus);
-        };
-        const int per_nw = a.dist ? (nw == 3 ? attn_wgs_per_cu<T, DP, true, 3>() : attn_wgs_per_cu<T, DP, true, 4>())
-                                  : (nw == 3 ? attn_wgs_per_cu<T, DP, false, 3>() : attn_wgs_per_cu<T, DP, false, 4>());
-        const int per_2 = a.dist ? attn_wgs_per_cu<T, DP, true, 2>() : attn_wgs_per_cu<T, DP, false, 2>();
-        return rounds(2, per_2) < rounds(nw, per_nw) ? 2 : nw;
-    }
+    const long long bh = (long long)a.B * a.H * a.nsplit;
+    const long long cus = device_cus();
+    auto rounds = [&](int w, int per_cu) {
+        const long long wgs = bh * ((a.W + 32 * w - 1) / (32 * w));
+        return (wgs + per_cu * cus - 1) / (per_cu * cus);
+    };
+    const int per_nw = a.dist ? (nw == 3 ? attn_wgs_per_cu<T, DP, true, 3>() : attn_wgs_per_cu<T, DP, true, 4>())
+                              : (nw == 3 ? attn_wgs_per_cu<T, DP, false, 3>() : attn_wgs_per_cu<T, DP, false, 4>());
+    const int per_2 = a.dist ? attn_wgs_per_cu<T, DP, true, 2>() : attn_wgs_per_cu<T, DP, false, 2>();
+    return rounds(2, per_2) < rounds(nw, per_nw) ? 2 : nw;
 }
 
 template <typename T, int DP, int NW>
@@ -641,7 +639,8 @@ hipError_t launch_dp(const AttnArgs &a, hipStream_t s, hipEvent_t start, hipEven
         else if (nw == 3) launch_modes<T, DP, 3>(a, grid, s, start, stop1);
         else launch_modes<T, DP, 4>(a, grid, s, start, stop1);
     } else {
-        launch_modes<T, DP, 4>(a, grid, s, start, stop1);
+        if (nw == 2) launch_modes<T, DP, 2>(a, grid, s, start, stop1);
+        else launch_modes<T, DP, 4>(a, grid, s, start, stop1);
     }
     if (merge) {
         const long long threads = (long long)a.B * a.H * a.W * (DP / 8);
