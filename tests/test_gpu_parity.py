@@ -76,6 +76,10 @@ ATTN_CASES = [
     # (640 on 512 slots) but one as two-wave blocks (960 on 1024), so the
     # launch runs 64-query blocks of 64 + 64 + 22 queries, four per CU
     ("dh16_two_wave_grid", 16, 320, 20, 150, 150, 2),
+    # fp32 (one four-wave workgroup per CU): 160 (b, h) of 150 queries take two
+    # rounds as 320 four-wave blocks, one as 480 two-wave blocks two per CU
+    ("dh32_two_wave_grid", 8, 640, 20, 150, 150, 2),
+    ("dh64_two_wave_grid", 8, 1280, 20, 150, 150, 2),
 ]
 
 
